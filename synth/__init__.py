@@ -1,0 +1,246 @@
+"""Seeded synthetic decode workloads for paged MLA decode.
+
+This module only draws inputs: sequence lengths, a page permutation, query and
+latent-cache values, and top-k index lists.  It holds no attention arithmetic.
+Both the CPU oracle and the GPU library consume exactly the arrays built here.
+
+Recipe (all draws from ``numpy.random.Generator(PCG64(seed))``, in this order):
+
+1. ``cache_seqlens`` (fixed list, or uniform integers in ``[lo, hi]``).
+2. Page permutation: the pool holds ``ceil(1.1 * N)`` pages (``N`` = pages the
+   sequences need; exactly ``N`` when ``slack`` is 0).  Sequence ``b`` gets the
+   next ``ceil(L_b / page_size)`` entries of one random permutation of the pool.
+   Unused block-table slots are -1.
+3. Q: ``[B, s_q, h_q, 576]`` standard normal float32, rounded to bf16 (RNE).
+4. Top-k indices (sparse workloads only): per (b, i), ``topk`` distinct
+   positions drawn uniformly without replacement from ``[0, L_b)``.
+5. KV: one standard normal float32 row of 576 values per *referenced* token,
+   in ascending (b, t) order, rounded to bf16.  Dense workloads reference
+   every ``t < L_b``; sparse workloads reference the union of their indices.
+   Every other byte of the pool (page tails, slack pages, unreferenced rows)
+   is 0xFF: NaN in bf16, e4m3fn and fp32, so any read of it shows up.
+
+Latent rows in the 656-byte FP8 layout: the first 512 (NoPE) values of the
+bf16 row are encoded per 1x128 tile with scale = amax / 448 (float32) and
+codes = float8_e4m3fn(x / scale) (torch's cast, clamped to +-448; an all-zero
+tile gets scale 0 and zero codes); bytes [512, 528) hold the four float32
+scales, bytes [528, 656) the 64 RoPE values as bf16.  This is input encoding
+only; decoding is done separately by each consumer.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+D_QK = 576
+D_V = 512
+D_NOPE = 512
+D_ROPE = 64
+ROW_BYTES_BF16 = D_QK * 2  # 1152
+ROW_BYTES_FP8 = D_NOPE + 4 * 4 + D_ROPE * 2  # 656
+KV_BF16 = 0
+KV_FP8_656 = 1
+
+
+@dataclasses.dataclass
+class Workload:
+    """One decode batch: every array is host (numpy) memory."""
+
+    name: str
+    batch: int
+    s_q: int
+    h_q: int
+    page_size: int
+    kv_format: int
+    topk: int
+    is_causal: int
+    softmax_scale: float  # float32 value
+    q: np.ndarray  # uint16 [B, s_q, h_q, 576] bf16 bit patterns
+    kv: np.ndarray  # uint8 [num_pages, page_size, row_bytes]
+    block_table: np.ndarray  # int32 [B, max_pages_per_seq]
+    cache_seqlens: np.ndarray  # int32 [B]
+    indices: Optional[np.ndarray]  # int32 [B, s_q, topk] or None
+
+    @property
+    def num_pages(self) -> int:
+        return int(self.kv.shape[0])
+
+    @property
+    def max_pages_per_seq(self) -> int:
+        return int(self.block_table.shape[1])
+
+    @property
+    def row_bytes(self) -> int:
+        return int(self.kv.shape[2])
+
+    def flops(self) -> int:
+        """2*h_q*s_q*s_k*(d_qk+d_v) summed over the batch (s_k = L_b, or topk)."""
+        if self.topk > 0:
+            sk = self.batch * self.topk
+        else:
+            sk = int(self.cache_seqlens.astype(np.int64).sum())
+        return 2 * self.h_q * self.s_q * sk * (D_QK + D_V)
+
+    def algorithmic_bytes(self) -> int:
+        """Bytes the method must move once: visible KV rows once per fetching
+        query set, Q, out (bf16), lse (fp32), block-table and index reads."""
+        L = self.cache_seqlens.astype(np.int64)
+        if self.topk > 0:
+            kv_rows = self.batch * self.s_q * self.topk
+            table = 4 * kv_rows
+            idx = 4 * kv_rows
+        else:
+            kv_rows = int(L.sum())
+            table = 4 * int(((L + self.page_size - 1) // self.page_size).sum())
+            idx = 0
+        rows = self.batch * self.s_q * self.h_q
+        return (kv_rows * self.row_bytes + rows * D_QK * 2 + rows * D_V * 2
+                + rows * 4 + table + idx + 4 * self.batch)
+
+
+def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns via torch's round-to-nearest-even cast."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def encode_fp8_rows(rows_bf16: np.ndarray) -> np.ndarray:
+    """bf16 bit rows [n, 576] -> 656-byte rows [n, 656] (input encoding)."""
+    import torch
+
+    n = rows_bf16.shape[0]
+    x = bf16_bits_to_f32(rows_bf16)
+    nope = x[:, :D_NOPE].reshape(n, 4, 128)
+    amax = np.abs(nope).max(axis=2).astype(np.float32)  # [n, 4]
+    scale = (amax / np.float32(448.0)).astype(np.float32)
+    safe = np.where(scale == 0, np.float32(1.0), scale)
+    y = np.clip(nope / safe[:, :, None], -448.0, 448.0).astype(np.float32)
+    y = np.where(scale[:, :, None] == 0, np.float32(0.0), y)
+    codes = torch.from_numpy(y.reshape(n, D_NOPE)).to(torch.float8_e4m3fn)
+    codes = codes.view(torch.uint8).numpy()
+    out = np.empty((n, ROW_BYTES_FP8), dtype=np.uint8)
+    out[:, :D_NOPE] = codes
+    out[:, D_NOPE:D_NOPE + 16] = scale.view(np.uint8).reshape(n, 16)
+    out[:, D_NOPE + 16:] = rows_bf16[:, D_NOPE:].copy().view(np.uint8).reshape(n, 128)
+    return out
+
+
+@dataclasses.dataclass(frozen=True)
+class Uniform:
+    """Sequence lengths drawn uniformly from the closed range [lo, hi]."""
+
+    lo: int
+    hi: int
+
+
+def _ceil_div(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def make_workload(name: str, *, batch: int, h_q: int, s_q: int, seqlens,
+                  seed: int, kv_format: int = KV_BF16, topk: int = 0,
+                  is_causal: int = 0, page_size: int = 64, slack: float = 0.1,
+                  softmax_scale: Optional[float] = None,
+                  max_pages_per_seq: Optional[int] = None,
+                  kv_chunk_rows: int = 1 << 18) -> Workload:
+    """Build one seeded workload following the recipe in the module docstring.
+
+    ``seqlens`` is either a sequence of ints (one per batch entry) or a
+    :class:`Uniform` for uniform integers in a closed range.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if isinstance(seqlens, Uniform):
+        L = rng.integers(seqlens.lo, seqlens.hi, size=batch, endpoint=True).astype(np.int32)
+    else:
+        L = np.asarray(list(seqlens), dtype=np.int32)
+        assert L.shape == (batch,)
+    n_pages = [_ceil_div(int(l), page_size) for l in L]
+    need = int(sum(n_pages))
+    pool = max(1, need if slack == 0 else int(math.ceil((1.0 + slack) * need)))
+    perm = rng.permutation(pool).astype(np.int32)
+    width = max_pages_per_seq if max_pages_per_seq is not None else max(1, max(n_pages) if n_pages else 1)
+    table = np.full((batch, width), -1, dtype=np.int32)
+    off = 0
+    for b in range(batch):
+        table[b, :n_pages[b]] = perm[off:off + n_pages[b]]
+        off += n_pages[b]
+
+    q32 = rng.standard_normal((batch, s_q, h_q, D_QK), dtype=np.float32)
+    q = bf16_bits_from_f32(q32)
+    del q32
+
+    indices = None
+    if topk > 0:
+        indices = np.empty((batch, s_q, topk), dtype=np.int32)
+        for b in range(batch):
+            for i in range(s_q):
+                assert topk <= L[b], "topk distinct positions need topk <= L_b"
+                indices[b, i] = rng.choice(int(L[b]), size=topk, replace=False).astype(np.int32)
+
+    row_bytes = ROW_BYTES_BF16 if kv_format == KV_BF16 else ROW_BYTES_FP8
+    kv = np.full((pool, page_size, row_bytes), 0xFF, dtype=np.uint8)
+    # referenced tokens in ascending (b, t) order
+    refs_b: List[np.ndarray] = []
+    refs_t: List[np.ndarray] = []
+    for b in range(batch):
+        if topk > 0:
+            t = np.unique(indices[b].reshape(-1))
+        else:
+            t = np.arange(int(L[b]), dtype=np.int64)
+        refs_b.append(np.full(t.shape, b, dtype=np.int64))
+        refs_t.append(t.astype(np.int64))
+    rb = np.concatenate(refs_b) if refs_b else np.zeros(0, np.int64)
+    rt = np.concatenate(refs_t) if refs_t else np.zeros(0, np.int64)
+    pages = table[rb, rt // page_size].astype(np.int64)
+    slots = rt % page_size
+    flat = kv.reshape(pool * page_size, row_bytes)
+    dest = pages * page_size + slots
+    for s in range(0, rb.shape[0], kv_chunk_rows):
+        e = min(rb.shape[0], s + kv_chunk_rows)
+        x = rng.standard_normal((e - s, D_QK), dtype=np.float32)
+        bits = bf16_bits_from_f32(x)
+        if kv_format == KV_BF16:
+            flat[dest[s:e]] = bits.view(np.uint8).reshape(e - s, row_bytes)
+        else:
+            flat[dest[s:e]] = encode_fp8_rows(bits)
+    scale = np.float32(1.0 / math.sqrt(D_QK)) if softmax_scale is None else np.float32(softmax_scale)
+    return Workload(name=name, batch=batch, s_q=s_q, h_q=h_q, page_size=page_size,
+                    kv_format=kv_format, topk=topk, is_causal=is_causal,
+                    softmax_scale=float(scale), q=q, kv=kv, block_table=table,
+                    cache_seqlens=L, indices=indices)
+
+
+# The five decode configurations, by number.  ``batch`` may be overridden to
+# build a smaller batch of the same shape for parity runs.
+CONFIGS = {
+    1: dict(name="c1_tiny_bf16", batch=2, h_q=16, s_q=1, seqlens=[100, 257],
+            kv_format=KV_BF16, slack=0.0),
+    2: dict(name="c2_dense_bf16_b64_sq1", batch=64, h_q=128, s_q=1, seqlens=Uniform(1024, 8192),
+            kv_format=KV_BF16, max_pages_per_seq=128),
+    3: dict(name="c3_dense_bf16_b128_sq2_causal", batch=128, h_q=128, s_q=2, seqlens=4096,
+            kv_format=KV_BF16, is_causal=1),
+    4: dict(name="c4_dense_fp8_b128_sq2", batch=128, h_q=128, s_q=2, seqlens=Uniform(8192, 32768),
+            kv_format=KV_FP8_656, max_pages_per_seq=512),
+    5: dict(name="c5_sparse_fp8_b128_sq2_topk2048", batch=128, h_q=128, s_q=2, seqlens=65536,
+            kv_format=KV_FP8_656, topk=2048),
+}
+
+
+def config_workload(n: int, batch: Optional[int] = None, seed: Optional[int] = None) -> Workload:
+    """Workload of configuration ``n`` (seed 1000 + n unless given)."""
+    c = dict(CONFIGS[n])
+    b = batch if batch is not None else c["batch"]
+    c["batch"] = b
+    if isinstance(c["seqlens"], int):
+        c["seqlens"] = [c["seqlens"]] * b
+    return make_workload(seed=1000 + n if seed is None else seed, **c)
