@@ -1,0 +1,176 @@
+"""Benchmark of paged MLA decode on one MI355X.
+
+A step is one pass of the whole path over one synthetic decode batch:
+split-KV metadata, the decode kernel and the combine kernel, enqueued through
+the C ABI on one stream.  Inputs are resident in HBM before timing starts.
+Successive steps read different copies of the latent cache (as successive
+layers do), so the 256 MB last-level cache cannot serve a repeated batch.
+
+Prints one JSON line: whole-job TFLOPS (value), HBM GB/s, the decode
+kernel's roofline fraction measured with HIP events on its stream, and the
+CPU oracle timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
+RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)
+
+DEFAULT_CONFIG = 3  # dense bf16, h_q=128, s_q=2 causal: the workload the target is stated on
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=DEFAULT_CONFIG, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--num-parts", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-units", type=int, default=None)
+    return ap.parse_args()
+
+
+def traffic_record(config_name: str):
+    """HBM traffic of the decode kernel from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"decode_{config_name}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = open(os.path.join(ROOT, "paged_kv_head_amd", "csrc", "decode.hip"), "rb").read()
+    if rec.get("decode_source_sha256") != hashlib.sha256(src).hexdigest():
+        return None
+    return rec
+
+
+def cpu_baseline(w, sample_units):
+    import oracle
+
+    threads = oracle.num_threads()
+    U = w.batch * w.s_q
+    n = sample_units if sample_units is not None else max(1, 2 * threads)
+    n = min(n, U)
+    rng = np.random.default_rng(0)
+    pick = np.sort(rng.choice(U, size=n, replace=False))
+    mask = np.zeros(U, dtype=np.uint8)
+    mask[pick] = 1
+    _, _, secs = oracle.timed_mla_decode(w, unit_mask=mask)
+    # FLOPs of the sampled query tokens (each attends over its own key count)
+    if w.topk > 0:
+        sk = np.full(U, w.topk, dtype=np.int64)
+    else:
+        sk = np.repeat(w.cache_seqlens.astype(np.int64), w.s_q)
+    flops = float(2 * w.h_q * sk[pick].sum() * (576 + 512))
+    return {"value": flops / secs / 1e12, "unit": "TFLOPS", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of {U} query tokens (all {w.h_q} heads each) of {w.name}, "
+                      f"{secs:.2f} s on the host"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); "
+              "the path shards by batch or by query head with no exchange, so N GPUs "
+              "would run N independent copies of the one-GPU step.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_kv_head_amd as mla
+    import synth
+    from tests.harness import problem, to_device
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    w = synth.config_workload(args.config)
+    print(f"[bench] workload {w.name}: generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    p = problem(w)
+    q, kv, bt, sl, idx = to_device(w, dev)
+    pool_bytes = kv.numel()
+    copies = max(2, math.ceil(1.0e9 / pool_bytes))
+    kvs = [kv] + [kv.clone() for _ in range(copies - 1)]
+    plan = mla.DecodePlan(p, dev, args.num_parts)
+    out = torch.empty((w.batch, w.s_q, w.h_q, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.batch, w.s_q, w.h_q), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        plan.metadata(sl)
+        if ev is not None:
+            ev[0].record(stream)
+        mla.mla_decode_paged(p, q, kvs[i % copies], bt, sl, idx, plan.sched, plan.num_parts,
+                             plan.num_splits, plan.workspace, out, lse)
+        if ev is not None:
+            ev[1].record(stream)
+        mla.mla_decode_combine(p, plan.num_parts, plan.num_splits, plan.workspace, out, lse)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    ms_per_step = wall * 1e3 / args.steps
+
+    flops = w.flops()
+    alg_bytes = w.algorithmic_bytes()
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    gbps = alg_bytes / (ms_per_step * 1e-3) / 1e9
+    intensity = flops / alg_bytes
+    if intensity >= RIDGE:
+        roof = {"bound": "mfma", "achieved": flops / (dec_ms * 1e-3) / 1e12,
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": alg_bytes / (dec_ms * 1e-3) / 1e9,
+                "peak": PEAK_HBM_GBPS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    tr = traffic_record(w.name)
+    roof["traffic"] = None if tr is None else tr["hbm_bytes_per_launch"]
+    roof["kernel"] = "decode_kernel"
+    roof["kernel_ms"] = dec_ms
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, args.cpu_sample_units)
+
+    line = {
+        "metric": "paged MLA decode TFLOPS + HBM GB/s (h_q=128, d_qk=576, d_v=512), % of roofline",
+        "value": tflops, "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "hbm_gbps": gbps, "arithmetic_intensity": intensity,
+        "config": {"workload": w.name, "batch": w.batch, "s_q": w.s_q, "h_q": w.h_q,
+                   "kv_format": "bf16" if w.kv_format == 0 else "fp8_656", "topk": w.topk,
+                   "is_causal": w.is_causal, "sum_seqlen": int(w.cache_seqlens.astype(np.int64).sum()),
+                   "num_parts": plan.num_parts, "kv_copies": copies,
+                   "flops_per_step": flops, "algorithmic_bytes_per_step": alg_bytes},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,290 @@
+"""Paged MLA decode for AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding over ``libmla_decode.so`` (C ABI in
+``include/mla_decode.h``).  Function names match the C entry points; the
+wrappers only marshal arguments (torch tensors -> device pointers, the
+current HIP stream) and turn nonzero statuses into exceptions.  Every step of
+the computation runs in the library's HIP kernels; there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = [
+    "MLA_KV_BF16", "MLA_KV_FP8_656", "MLA_FLAG_NATURAL_BASE", "MlaError", "Problem",
+    "library_path", "mla_decode_num_units", "mla_decode_num_parts", "mla_decode_metadata_size",
+    "mla_decode_workspace_bytes", "mla_decode_get_metadata", "mla_decode_paged",
+    "mla_decode_paged_fp8", "mla_decode_sparse_fp8", "mla_decode_combine", "mla_last_error",
+    "mla_decode_with_kvcache",
+]
+
+MLA_KV_BF16 = 0
+MLA_KV_FP8_656 = 1
+MLA_FLAG_NATURAL_BASE = 1
+
+MLA_OK = 0
+MLA_ERR_INVALID_ARGUMENT = 1
+MLA_ERR_UNSUPPORTED = 2
+MLA_ERR_WORKSPACE_TOO_SMALL = 3
+MLA_ERR_HIP = 4
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libmla_decode.so")
+
+
+class MlaError(RuntimeError):
+    """A nonzero status from the library; ``status`` holds the code."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[mla status {status}] {message}")
+        self.status = status
+
+
+class Problem(ctypes.Structure):
+    """Mirror of ``mla_problem``."""
+
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("s_q", ctypes.c_int32), ("h_q", ctypes.c_int32),
+        ("h_kv", ctypes.c_int32), ("d_qk", ctypes.c_int32), ("d_v", ctypes.c_int32),
+        ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32), ("topk", ctypes.c_int32),
+        ("kv_format", ctypes.c_int32), ("is_causal", ctypes.c_int32), ("flags", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+    ]
+
+    @classmethod
+    def make(cls, *, batch, s_q, h_q, num_pages, max_pages_per_seq, softmax_scale, topk=0,
+             kv_format=MLA_KV_BF16, is_causal=0, flags=0, h_kv=1, d_qk=576, d_v=512,
+             page_size=64) -> "Problem":
+        return cls(batch, s_q, h_q, h_kv, d_qk, d_v, page_size, num_pages, max_pages_per_seq,
+                   topk, kv_format, is_causal, flags, float(softmax_scale))
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"libmla_decode.so is not built ({_LIB_PATH}); run paged_kv_head_amd/build.py")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    PP = ctypes.POINTER(Problem)
+    I32 = ctypes.c_int32
+    SZ = ctypes.c_size_t
+    lib.mla_decode_num_units.argtypes = [PP]
+    lib.mla_decode_num_units.restype = I32
+    lib.mla_decode_num_parts.argtypes = [PP, ctypes.c_int, ctypes.POINTER(I32)]
+    lib.mla_decode_metadata_size.argtypes = [PP, I32, ctypes.POINTER(SZ), ctypes.POINTER(SZ)]
+    lib.mla_decode_workspace_bytes.argtypes = [PP, I32, ctypes.POINTER(SZ)]
+    lib.mla_decode_get_metadata.argtypes = [PP, P, I32, P, P, P]
+    lib.mla_decode_paged.argtypes = [PP, P, P, P, P, P, P, I32, P, P, SZ, P, P, P]
+    lib.mla_decode_paged_fp8.argtypes = [PP, P, P, P, P, P, I32, P, P, SZ, P, P, P]
+    lib.mla_decode_sparse_fp8.argtypes = [PP, P, P, P, P, P, P, I32, P, P, SZ, P, P, P]
+    lib.mla_decode_combine.argtypes = [PP, I32, P, P, SZ, P, P, P]
+    for fn in ("mla_decode_num_parts", "mla_decode_metadata_size", "mla_decode_workspace_bytes",
+               "mla_decode_get_metadata", "mla_decode_paged", "mla_decode_paged_fp8",
+               "mla_decode_sparse_fp8", "mla_decode_combine"):
+        getattr(lib, fn).restype = ctypes.c_int
+    lib.mla_last_error.argtypes = []
+    lib.mla_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def mla_last_error() -> str:
+    return _load().mla_last_error().decode()
+
+
+def _check(status: int) -> None:
+    """Invalid arguments raise ValueError (the message names the argument);
+    every other failure raises MlaError."""
+    if status == MLA_OK:
+        return
+    msg = mla_last_error()
+    if status == MLA_ERR_INVALID_ARGUMENT:
+        raise ValueError(msg)
+    raise MlaError(status, msg)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if t.numel() > 0 and not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr()) if t.data_ptr() else None
+
+
+def _expect(name, t, dtype, numel, at_least=False):
+    if t is None:
+        raise ValueError(f"{name}: missing tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    n = t.numel() * t.element_size() if dtype is None else t.numel()
+    if (n < numel) if at_least else (n != numel):
+        raise ValueError(f"{name}: {n} {'bytes' if dtype is None else 'elements'}, expected "
+                         f"{'at least ' if at_least else ''}{numel}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a device tensor")
+
+
+def _check_decode_tensors(p: Problem, q, kv_pool, block_table, cache_seqlens, indices, out, lse):
+    """Buffer sizes are not visible to the C ABI; check them here so that no
+    kernel can be handed a buffer smaller than the problem says."""
+    rows = p.batch * p.s_q * p.h_q
+    _expect("q", q, torch.bfloat16, rows * 576)
+    row_bytes = 1152 if p.kv_format == MLA_KV_BF16 else 656
+    _expect("kv_pool", kv_pool, None, p.num_pages * p.page_size * row_bytes)
+    _expect("block_table", block_table, torch.int32, p.batch * p.max_pages_per_seq)
+    _expect("cache_seqlens", cache_seqlens, torch.int32, p.batch)
+    if p.topk > 0:
+        _expect("indices", indices, torch.int32, p.batch * p.s_q * p.topk)
+    _expect("out", out, torch.bfloat16, rows * 512)
+    _expect("lse", lse, torch.float32, rows)
+
+
+def _check_meta_tensors(p: Problem, num_parts, sched, num_splits):
+    n_sched, n_splits = mla_decode_metadata_size(p, num_parts)
+    _expect("sched", sched, torch.int32, n_sched, at_least=True)
+    _expect("num_splits", num_splits, torch.int32, n_splits, at_least=True)
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def mla_decode_num_units(p: Problem) -> int:
+    return int(_load().mla_decode_num_units(ctypes.byref(p)))
+
+
+def mla_decode_num_parts(p: Problem, device: int = 0) -> int:
+    n = ctypes.c_int32(0)
+    _check(_load().mla_decode_num_parts(ctypes.byref(p), int(device), ctypes.byref(n)))
+    return int(n.value)
+
+
+def mla_decode_metadata_size(p: Problem, num_parts: int) -> Tuple[int, int]:
+    a, b = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check(_load().mla_decode_metadata_size(ctypes.byref(p), int(num_parts), ctypes.byref(a), ctypes.byref(b)))
+    return int(a.value), int(b.value)
+
+
+def mla_decode_workspace_bytes(p: Problem, num_parts: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_load().mla_decode_workspace_bytes(ctypes.byref(p), int(num_parts), ctypes.byref(n)))
+    return int(n.value)
+
+
+def mla_decode_get_metadata(p: Problem, cache_seqlens, num_parts, sched, num_splits, stream=None):
+    _expect("cache_seqlens", cache_seqlens, torch.int32, p.batch)
+    _check_meta_tensors(p, num_parts, sched, num_splits)
+    _check(_load().mla_decode_get_metadata(ctypes.byref(p), _ptr(cache_seqlens), int(num_parts),
+                                           _ptr(sched), _ptr(num_splits), _stream(stream)))
+
+
+def mla_decode_paged(p: Problem, q, kv_pool, block_table, cache_seqlens, indices, sched, num_parts,
+                     num_splits, workspace, out, lse, stream=None):
+    _check_decode_tensors(p, q, kv_pool, block_table, cache_seqlens, indices, out, lse)
+    _check_meta_tensors(p, num_parts, sched, num_splits)
+    _check(_load().mla_decode_paged(
+        ctypes.byref(p), _ptr(q), _ptr(kv_pool), _ptr(block_table), _ptr(cache_seqlens),
+        _ptr(indices), _ptr(sched), int(num_parts), _ptr(num_splits), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def mla_decode_paged_fp8(p: Problem, q, kv_pool, block_table, cache_seqlens, sched, num_parts,
+                         num_splits, workspace, out, lse, stream=None):
+    _check_decode_tensors(p, q, kv_pool, block_table, cache_seqlens, None, out, lse)
+    _check_meta_tensors(p, num_parts, sched, num_splits)
+    _check(_load().mla_decode_paged_fp8(
+        ctypes.byref(p), _ptr(q), _ptr(kv_pool), _ptr(block_table), _ptr(cache_seqlens),
+        _ptr(sched), int(num_parts), _ptr(num_splits), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def mla_decode_sparse_fp8(p: Problem, q, kv_pool, block_table, cache_seqlens, indices, sched,
+                          num_parts, num_splits, workspace, out, lse, stream=None):
+    _check_decode_tensors(p, q, kv_pool, block_table, cache_seqlens, indices, out, lse)
+    _check_meta_tensors(p, num_parts, sched, num_splits)
+    _check(_load().mla_decode_sparse_fp8(
+        ctypes.byref(p), _ptr(q), _ptr(kv_pool), _ptr(block_table), _ptr(cache_seqlens),
+        _ptr(indices), _ptr(sched), int(num_parts), _ptr(num_splits), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def mla_decode_combine(p: Problem, num_parts, num_splits, workspace, out, lse, stream=None):
+    rows = p.batch * p.s_q * p.h_q
+    _expect("out", out, torch.bfloat16, rows * 512)
+    _expect("lse", lse, torch.float32, rows)
+    _expect("num_splits", num_splits, torch.int32, mla_decode_metadata_size(p, num_parts)[1], at_least=True)
+    _check(_load().mla_decode_combine(
+        ctypes.byref(p), int(num_parts), _ptr(num_splits), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(stream)))
+
+
+class DecodePlan:
+    """Device buffers for one problem shape: metadata and workspace.
+
+    Allocated once (torch caching allocator) and reused across layers and
+    steps; ``run`` enqueues metadata, decode and combine on the stream.
+    """
+
+    def __init__(self, p: Problem, device="cuda", num_parts: Optional[int] = None):
+        self.p = p
+        dev = torch.device(device)
+        self.num_parts = num_parts if num_parts is not None else mla_decode_num_parts(p, dev.index or 0)
+        n_sched, n_splits = mla_decode_metadata_size(p, self.num_parts)
+        self.sched = torch.empty(n_sched, dtype=torch.int32, device=dev)
+        self.num_splits = torch.empty(n_splits, dtype=torch.int32, device=dev)
+        ws = mla_decode_workspace_bytes(p, self.num_parts)
+        self.workspace = torch.empty(max(16, ws), dtype=torch.uint8, device=dev)
+
+    def metadata(self, cache_seqlens, stream=None):
+        mla_decode_get_metadata(self.p, cache_seqlens, self.num_parts, self.sched, self.num_splits, stream)
+
+    def decode(self, q, kv_pool, block_table, cache_seqlens, indices, out, lse, stream=None):
+        mla_decode_paged(self.p, q, kv_pool, block_table, cache_seqlens, indices, self.sched,
+                         self.num_parts, self.num_splits, self.workspace, out, lse, stream)
+        mla_decode_combine(self.p, self.num_parts, self.num_splits, self.workspace, out, lse, stream)
+
+
+def mla_decode_with_kvcache(q, kv_pool, block_table, cache_seqlens, softmax_scale, *,
+                            is_causal=False, kv_format=MLA_KV_BF16, indices=None,
+                            natural_base=False, num_parts=None, out=None, lse=None):
+    """One-call decode: metadata, decode and combine on the current stream.
+
+    q bf16 [B, s_q, h_q, 576]; kv_pool uint8/bf16 [num_pages, 64, row]
+    (row = 576 bf16, or 656 bytes for MLA_KV_FP8_656); block_table int32
+    [B, max_pages]; cache_seqlens int32 [B]; indices int32 [B, s_q, topk] or
+    None.  Returns (out bf16 [B, s_q, h_q, 512], lse float32 [B, s_q, h_q]).
+    """
+    B, s_q, h_q, _ = q.shape
+    topk = 0 if indices is None else int(indices.shape[-1])
+    p = Problem.make(batch=B, s_q=s_q, h_q=h_q, num_pages=int(kv_pool.shape[0]),
+                     max_pages_per_seq=int(block_table.shape[1]), softmax_scale=softmax_scale,
+                     topk=topk, kv_format=kv_format, is_causal=int(bool(is_causal)),
+                     flags=MLA_FLAG_NATURAL_BASE if natural_base else 0)
+    plan = DecodePlan(p, q.device, num_parts)
+    if out is None:
+        out = torch.empty((B, s_q, h_q, 512), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, s_q, h_q), dtype=torch.float32, device=q.device)
+    plan.metadata(cache_seqlens)
+    plan.decode(q, kv_pool, block_table, cache_seqlens, indices, out, lse)
+    return out, lse

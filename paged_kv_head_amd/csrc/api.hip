@@ -1,0 +1,285 @@
+// C ABI of libmla_decode.so: host-side validation and kernel launches.
+// Every check runs before any HIP call; a failed check returns a status and
+// records a message naming the argument (the wrappers in the MAX kernels
+// guide, "max.nn.kernels 内核封装模块全解析", section 输入校验, reject bad
+// tensors by argument name before the kernel runs; scalars such as the
+// softmax scale travel as host float32 values, same section).
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <vector>
+
+#include "../../include/mla_decode.h"
+#include "internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+mla_status fail(mla_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+mla_status ok() {
+  g_err[0] = '\0';
+  return MLA_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Validates the problem and fills the kernel-side shape.
+mla_status check_problem(const mla_problem* p, mla::Shape* s) {
+  if (!p) return fail(MLA_ERR_INVALID_ARGUMENT, "p: NULL problem");
+  if (p->batch < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "batch: must be >= 0 (got %d)", p->batch);
+  if (p->s_q < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "s_q: must be >= 1 (got %d)", p->s_q);
+  if (p->h_q < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "h_q: must be >= 1 (got %d)", p->h_q);
+  if (p->h_kv != 1) return fail(MLA_ERR_UNSUPPORTED, "h_kv: only 1 latent KV head is supported (got %d)", p->h_kv);
+  if (p->d_qk != mla::kDqk) return fail(MLA_ERR_UNSUPPORTED, "d_qk: must be 576 (got %d)", p->d_qk);
+  if (p->d_v != mla::kDv) return fail(MLA_ERR_UNSUPPORTED, "d_v: must be 512 (got %d)", p->d_v);
+  if (p->page_size != mla::kPage) return fail(MLA_ERR_UNSUPPORTED, "page_size: must be 64 (got %d)", p->page_size);
+  if (p->num_pages < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "num_pages: must be >= 1 (got %d)", p->num_pages);
+  if (p->max_pages_per_seq < 1)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "max_pages_per_seq: must be >= 1 (got %d)", p->max_pages_per_seq);
+  if (p->topk < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "topk: must be >= 0 (got %d)", p->topk);
+  if (p->kv_format != MLA_KV_BF16 && p->kv_format != MLA_KV_FP8_656)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "kv_format: unknown value %d", p->kv_format);
+  if (p->is_causal != 0 && p->is_causal != 1)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "is_causal: must be 0 or 1 (got %d)", p->is_causal);
+  if (p->is_causal && p->topk > 0)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "is_causal: sparse decode (topk > 0) takes visibility from indices; is_causal must be 0");
+  if (p->flags & ~MLA_FLAG_NATURAL_BASE)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "flags: unknown bits 0x%x", (unsigned)(p->flags & ~MLA_FLAG_NATURAL_BASE));
+  if (!isfinite(p->softmax_scale))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "softmax_scale: must be finite");
+  const int64_t units = p->topk > 0 ? (int64_t)p->batch * p->s_q : p->batch;
+  const int64_t rows = p->topk > 0 ? p->h_q : (int64_t)p->s_q * p->h_q;
+  if (units > mla::kMaxUnits)
+    return fail(MLA_ERR_UNSUPPORTED, "batch: %lld work units exceed the scheduler limit %d",
+                (long long)units, mla::kMaxUnits);
+  if (rows * 512 > INT32_MAX / 8)
+    return fail(MLA_ERR_UNSUPPORTED, "h_q: %lld query rows per unit is too many", (long long)rows);
+  const int64_t blocks_per_unit =
+      p->topk > 0 ? (p->topk + mla::kPage - 1) / mla::kPage : p->max_pages_per_seq;
+  if (units * (blocks_per_unit + mla::kSplitPenalty) + mla::kMaxParts >= INT32_MAX)
+    return fail(MLA_ERR_UNSUPPORTED, "max_pages_per_seq/topk: total work exceeds the scheduler's int32 range");
+  const int64_t table = (int64_t)p->batch * p->max_pages_per_seq;
+  if (table >= INT32_MAX)
+    return fail(MLA_ERR_UNSUPPORTED, "block_table: more than 2^31 entries");
+  s->batch = p->batch;
+  s->s_q = p->s_q;
+  s->h_q = p->h_q;
+  s->topk = p->topk;
+  s->kv_format = p->kv_format;
+  s->is_causal = p->is_causal;
+  s->natural = (p->flags & MLA_FLAG_NATURAL_BASE) ? 1 : 0;
+  s->num_pages = p->num_pages;
+  s->max_pages = p->max_pages_per_seq;
+  s->units = (int32_t)units;
+  s->rows = (int32_t)rows;
+  s->groups = (int32_t)((rows + mla::kRowsPerGroup - 1) / mla::kRowsPerGroup);
+  s->scale_log2 = s->natural ? (float)((double)p->softmax_scale * 1.4426950408889634) : p->softmax_scale;
+  return MLA_OK;
+}
+
+mla_status check_parts(int32_t num_parts) {
+  if (num_parts < 1 || num_parts > mla::kMaxParts)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "num_parts: must be in [1, %d] (got %d)", mla::kMaxParts, num_parts);
+  return MLA_OK;
+}
+
+std::mutex g_cu_mutex;
+std::vector<int> g_cu_count;  // per device, 0 = unknown
+
+mla_status cu_count(int device, int* cus) {
+  std::lock_guard<std::mutex> lock(g_cu_mutex);
+  if (device < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "device: must be >= 0 (got %d)", device);
+  if ((size_t)device < g_cu_count.size() && g_cu_count[device] > 0) {
+    *cus = g_cu_count[device];
+    return MLA_OK;
+  }
+  int v = 0;
+  hipError_t e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, device);
+  if (e != hipSuccess)
+    return fail(MLA_ERR_HIP, "hipDeviceGetAttribute(device=%d): %s", device, hipGetErrorString(e));
+  if ((size_t)device >= g_cu_count.size()) g_cu_count.resize(device + 1, 0);
+  g_cu_count[device] = v;
+  *cus = v;
+  return MLA_OK;
+}
+
+mla_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+#define MLA_CHECK(expr)              \
+  do {                               \
+    mla_status st_ = (expr);         \
+    if (st_ != MLA_OK) return st_;   \
+  } while (0)
+
+mla_status check_ptr(const void* ptr, const char* name, size_t align) {
+  if (!ptr) return fail(MLA_ERR_INVALID_ARGUMENT, "%s: NULL pointer", name);
+  if (!aligned(ptr, align)) return fail(MLA_ERR_INVALID_ARGUMENT, "%s: must be %zu-byte aligned", name, align);
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t mla_decode_num_units(const mla_problem* p) {
+  if (!p) return -1;
+  return p->topk > 0 ? p->batch * p->s_q : p->batch;
+}
+
+mla_status mla_decode_num_parts(const mla_problem* p, int device, int32_t* num_parts) {
+  mla::Shape s;
+  MLA_CHECK(check_problem(p, &s));
+  if (!num_parts) return fail(MLA_ERR_INVALID_ARGUMENT, "num_parts: NULL pointer");
+  int cus = 0;
+  MLA_CHECK(cu_count(device, &cus));
+  int parts = cus / s.groups;
+  if (parts < 1) parts = 1;
+  *num_parts = parts;
+  return ok();
+}
+
+mla_status mla_decode_metadata_size(const mla_problem* p, int32_t num_parts, size_t* sched_ints,
+                                    size_t* num_splits_ints) {
+  mla::Shape s;
+  MLA_CHECK(check_problem(p, &s));
+  MLA_CHECK(check_parts(num_parts));
+  if (!sched_ints || !num_splits_ints)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "sched_ints/num_splits_ints: NULL pointer");
+  *sched_ints = (size_t)num_parts * 8;
+  *num_splits_ints = (size_t)s.units + 1;
+  return ok();
+}
+
+mla_status mla_decode_workspace_bytes(const mla_problem* p, int32_t num_parts, size_t* bytes) {
+  mla::Shape s;
+  MLA_CHECK(check_problem(p, &s));
+  MLA_CHECK(check_parts(num_parts));
+  if (!bytes) return fail(MLA_ERR_INVALID_ARGUMENT, "bytes: NULL pointer");
+  *bytes = mla::ws_total_bytes(num_parts, s.units, s.rows, s.groups);
+  return ok();
+}
+
+mla_status mla_decode_get_metadata(const mla_problem* p, const int32_t* cache_seqlens,
+                                   int32_t num_parts, int32_t* sched, int32_t* num_splits,
+                                   void* stream) {
+  mla::Shape s;
+  MLA_CHECK(check_problem(p, &s));
+  MLA_CHECK(check_parts(num_parts));
+  MLA_CHECK(check_ptr(cache_seqlens, "cache_seqlens", 4));
+  MLA_CHECK(check_ptr(sched, "sched", 4));
+  MLA_CHECK(check_ptr(num_splits, "num_splits", 4));
+  return hip_status(mla::launch_metadata(s, cache_seqlens, num_parts, sched, num_splits,
+                                         (hipStream_t)stream),
+                    "metadata kernel launch");
+}
+
+mla_status mla_decode_paged(const mla_problem* p, const void* q, const void* kv_pool,
+                            const int32_t* block_table, const int32_t* cache_seqlens,
+                            const int32_t* indices, const int32_t* sched, int32_t num_parts,
+                            const int32_t* num_splits, void* workspace, size_t workspace_bytes,
+                            void* out, float* lse, void* stream) {
+  mla::Shape s;
+  MLA_CHECK(check_problem(p, &s));
+  MLA_CHECK(check_parts(num_parts));
+  MLA_CHECK(check_ptr(q, "q", 16));
+  MLA_CHECK(check_ptr(kv_pool, "kv_pool", 16));
+  MLA_CHECK(check_ptr(block_table, "block_table", 4));
+  MLA_CHECK(check_ptr(cache_seqlens, "cache_seqlens", 4));
+  if (p->topk > 0) {
+    MLA_CHECK(check_ptr(indices, "indices", 4));
+  } else if (indices) {
+    return fail(MLA_ERR_INVALID_ARGUMENT, "indices: must be NULL when topk == 0");
+  }
+  MLA_CHECK(check_ptr(sched, "sched", 4));
+  MLA_CHECK(check_ptr(num_splits, "num_splits", 4));
+  MLA_CHECK(check_ptr(workspace, "workspace", 16));
+  MLA_CHECK(check_ptr(out, "out", 16));
+  MLA_CHECK(check_ptr(lse, "lse", 4));
+  const size_t need = mla::ws_total_bytes(num_parts, s.units, s.rows, s.groups);
+  if (workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes: %zu given, %zu needed", workspace_bytes, need);
+  if (s.units == 0) return ok();
+  mla::DecodeArgs a;
+  a.s = s;
+  a.q = (const uint16_t*)q;
+  a.kv = (const uint8_t*)kv_pool;
+  a.block_table = block_table;
+  a.seqlens = cache_seqlens;
+  a.indices = indices;
+  a.sched = sched;
+  a.num_splits = num_splits;
+  a.num_parts = num_parts;
+  const size_t slots = mla::ws_slots(num_parts, s.units);
+  a.ws_lse = (float*)workspace;
+  a.ws_o = (float*)((char*)workspace + mla::ws_lse_bytes(slots, s.rows));
+  a.ws_flush = (float*)((char*)workspace + mla::ws_lse_bytes(slots, s.rows) + mla::ws_o_bytes(slots, s.rows));
+  a.out = (uint16_t*)out;
+  a.lse = lse;
+  return hip_status(mla::launch_decode(a, (hipStream_t)stream), "decode kernel launch");
+}
+
+mla_status mla_decode_paged_fp8(const mla_problem* p, const void* q, const void* kv_pool,
+                                const int32_t* block_table, const int32_t* cache_seqlens,
+                                const int32_t* sched, int32_t num_parts,
+                                const int32_t* num_splits, void* workspace,
+                                size_t workspace_bytes, void* out, float* lse, void* stream) {
+  if (!p) return fail(MLA_ERR_INVALID_ARGUMENT, "p: NULL problem");
+  if (p->kv_format != MLA_KV_FP8_656)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "kv_format: mla_decode_paged_fp8 needs MLA_KV_FP8_656");
+  if (p->topk != 0) return fail(MLA_ERR_INVALID_ARGUMENT, "topk: mla_decode_paged_fp8 is dense (topk must be 0)");
+  return mla_decode_paged(p, q, kv_pool, block_table, cache_seqlens, nullptr, sched, num_parts,
+                          num_splits, workspace, workspace_bytes, out, lse, stream);
+}
+
+mla_status mla_decode_sparse_fp8(const mla_problem* p, const void* q, const void* kv_pool,
+                                 const int32_t* block_table, const int32_t* cache_seqlens,
+                                 const int32_t* indices, const int32_t* sched,
+                                 int32_t num_parts, const int32_t* num_splits, void* workspace,
+                                 size_t workspace_bytes, void* out, float* lse, void* stream) {
+  if (!p) return fail(MLA_ERR_INVALID_ARGUMENT, "p: NULL problem");
+  if (p->kv_format != MLA_KV_FP8_656)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "kv_format: mla_decode_sparse_fp8 needs MLA_KV_FP8_656");
+  if (p->topk <= 0) return fail(MLA_ERR_INVALID_ARGUMENT, "topk: mla_decode_sparse_fp8 needs topk > 0");
+  return mla_decode_paged(p, q, kv_pool, block_table, cache_seqlens, indices, sched, num_parts,
+                          num_splits, workspace, workspace_bytes, out, lse, stream);
+}
+
+mla_status mla_decode_combine(const mla_problem* p, int32_t num_parts, const int32_t* num_splits,
+                              const void* workspace, size_t workspace_bytes, void* out,
+                              float* lse, void* stream) {
+  mla::Shape s;
+  MLA_CHECK(check_problem(p, &s));
+  MLA_CHECK(check_parts(num_parts));
+  MLA_CHECK(check_ptr(num_splits, "num_splits", 4));
+  MLA_CHECK(check_ptr(workspace, "workspace", 16));
+  MLA_CHECK(check_ptr(out, "out", 16));
+  MLA_CHECK(check_ptr(lse, "lse", 4));
+  const size_t need = mla::ws_total_bytes(num_parts, s.units, s.rows, s.groups);
+  if (workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes: %zu given, %zu needed", workspace_bytes, need);
+  if (s.units == 0) return ok();
+  const size_t slots = mla::ws_slots(num_parts, s.units);
+  const float* ws_lse = (const float*)workspace;
+  const float* ws_o = (const float*)((const char*)workspace + mla::ws_lse_bytes(slots, s.rows));
+  return hip_status(mla::launch_combine(s, num_splits, ws_lse, ws_o, (uint16_t*)out, lse,
+                                        (hipStream_t)stream),
+                    "combine kernel launch");
+}
+
+const char* mla_last_error(void) { return g_err; }
+
+}  // extern "C"

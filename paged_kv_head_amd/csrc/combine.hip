@@ -1,0 +1,81 @@
+// Combine: merges the split partial results of one query row.  Each split s
+// holds its normalised output O_s and lse_s (log2 units); with
+// M = max_s lse_s the merged row is
+//   lse = M + log2(sum_s 2^(lse_s - M)),   out = sum_s 2^(lse_s - lse) * O_s,
+// the online-softmax merge of results over disjoint key ranges ("Modular
+// Platform 设计文档全景导读", sections 六 and 七).  The FlashMLA page
+// ("为什么 FlashMLA 的解码内核能跑到 660 TFLOPS", section 设计 5) runs this
+// as a second kernel after the split decode.
+//
+// One wave per query row; each lane owns 8 of the 512 output columns.
+// Units with no segment (empty visible range) get out = 0 and lse = -inf.
+#include "internal.h"
+
+namespace mla {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+constexpr int kRowsPerBlock = 4;
+
+__device__ inline uint16_t bf16_bits(float x) {
+  __bf16 h = (__bf16)x;
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+__global__ void __launch_bounds__(64 * kRowsPerBlock)
+combine_kernel(Shape s, const int32_t* __restrict__ num_splits, const float* __restrict__ ws_lse,
+               const float* __restrict__ ws_o, uint16_t* __restrict__ out,
+               float* __restrict__ lse) {
+  const int u = blockIdx.y;
+  const int r = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= s.rows) return;
+  const int first = num_splits[u];
+  const int n = num_splits[u + 1] - first;
+  if (n == 1) return;  // written by the decode kernel
+  const int64_t row = (int64_t)u * s.rows + r;
+  float acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
+  float M = -INFINITY;
+  for (int sp = 0; sp < n; ++sp) M = fmaxf(M, ws_lse[(int64_t)(first + sp) * s.rows + r]);
+  float lse2 = -INFINITY;
+  if (M != -INFINITY) {
+    float tot = 0.0f;
+    for (int sp = 0; sp < n; ++sp) {
+      const int64_t wrow = (int64_t)(first + sp) * s.rows + r;
+      const float w = __builtin_amdgcn_exp2f(ws_lse[wrow] - M);
+      tot += w;
+      const f32x4* src = reinterpret_cast<const f32x4*>(ws_o + wrow * kDv + lane * 8);
+      const f32x4 a0 = src[0], a1 = src[1];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        acc[c] += w * a0[c];
+        acc[4 + c] += w * a1[c];
+      }
+    }
+    const float inv = 1.0f / tot;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] *= inv;
+    lse2 = M + log2f(tot);
+  }
+  uint4 packed;
+  packed.x = (uint32_t)bf16_bits(acc[0]) | ((uint32_t)bf16_bits(acc[1]) << 16);
+  packed.y = (uint32_t)bf16_bits(acc[2]) | ((uint32_t)bf16_bits(acc[3]) << 16);
+  packed.z = (uint32_t)bf16_bits(acc[4]) | ((uint32_t)bf16_bits(acc[5]) << 16);
+  packed.w = (uint32_t)bf16_bits(acc[6]) | ((uint32_t)bf16_bits(acc[7]) << 16);
+  *reinterpret_cast<uint4*>(out + row * kDv + lane * 8) = packed;
+  if (lane == 0) lse[row] = s.natural ? lse2 * 0.69314718055994531f : lse2;
+}
+
+}  // namespace
+
+hipError_t launch_combine(const Shape& s, const int32_t* num_splits, const float* ws_lse,
+                          const float* ws_o, uint16_t* out, float* lse, hipStream_t stream) {
+  dim3 grid((s.rows + kRowsPerBlock - 1) / kRowsPerBlock, s.units);
+  hipLaunchKernelGGL(combine_kernel, grid, dim3(64 * kRowsPerBlock), 0, stream, s, num_splits,
+                     ws_lse, ws_o, out, lse);
+  return hipGetLastError();
+}
+
+}  // namespace mla

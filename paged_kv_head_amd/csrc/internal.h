@@ -1,0 +1,69 @@
+// Internal declarations shared by the translation units of libmla_decode.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+constexpr int kDqk = 576;
+constexpr int kDv = 512;
+constexpr int kPage = 64;          // tokens per page == keys per tile
+constexpr int kRowsPerGroup = 128; // query rows one workgroup owns
+constexpr int kSplitPenalty = 2;   // scheduler cost of one segment, in blocks
+constexpr int kMaxUnits = 16384;   // metadata kernel keeps per-unit arrays in LDS
+constexpr int kMaxParts = 65536;
+
+struct Shape {
+  int32_t batch, s_q, h_q, topk, kv_format, is_causal, natural;
+  int32_t num_pages, max_pages;
+  int32_t units;  // U
+  int32_t rows;   // query rows per unit (R)
+  int32_t groups; // ceil(R / 128)
+  float scale_log2;  // exponent multiplier: softmax_scale, times log2(e) for base e
+};
+
+struct DecodeArgs {
+  Shape s;
+  const uint16_t* q;
+  const uint8_t* kv;
+  const int32_t* block_table;
+  const int32_t* seqlens;
+  const int32_t* indices;
+  const int32_t* sched;
+  const int32_t* num_splits;
+  int32_t num_parts;
+  float* ws_lse;  // [slots * R]
+  float* ws_o;    // [slots * R * 512]
+  float* ws_flush;  // [num_parts * groups * 256 threads * 258]
+  uint16_t* out;
+  float* lse;
+};
+
+// Workspace layout: split lse block, split output block (both for
+// num_parts + U slots of R rows), then one flush record per decode thread
+// (num_parts * groups workgroups of 256 threads, 258 floats each).
+constexpr int kFlushFloats = 258;
+inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+inline size_t ws_slots(int32_t num_parts, int32_t units) { return (size_t)num_parts + (size_t)units; }
+inline size_t ws_lse_bytes(size_t slots, int32_t rows) {
+  return align256(slots * (size_t)rows * sizeof(float));
+}
+inline size_t ws_o_bytes(size_t slots, int32_t rows) {
+  return align256(slots * (size_t)rows * kDv * sizeof(float));
+}
+inline size_t ws_flush_bytes(int32_t num_parts, int32_t groups) {
+  return (size_t)num_parts * (size_t)groups * 256 * kFlushFloats * sizeof(float);
+}
+inline size_t ws_total_bytes(int32_t num_parts, int32_t units, int32_t rows, int32_t groups) {
+  size_t slots = ws_slots(num_parts, units);
+  return ws_lse_bytes(slots, rows) + ws_o_bytes(slots, rows) + ws_flush_bytes(num_parts, groups);
+}
+
+hipError_t launch_metadata(const Shape& s, const int32_t* seqlens, int32_t num_parts,
+                           int32_t* sched, int32_t* num_splits, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_combine(const Shape& s, const int32_t* num_splits, const float* ws_lse,
+                          const float* ws_o, uint16_t* out, float* lse, hipStream_t stream);
+
+}  // namespace mla

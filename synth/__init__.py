@@ -15,7 +15,9 @@ Recipe (all draws from ``numpy.random.Generator(PCG64(seed))``, in this order):
 4. Top-k indices (sparse workloads only): per (b, i), ``topk`` distinct
    positions drawn uniformly without replacement from ``[0, L_b)``.
 5. KV: one standard normal float32 row of 576 values per *referenced* token,
-   in ascending (b, t) order, rounded to bf16.  Dense workloads reference
+   in ascending (b, t) order, rounded to bf16.  Rows are drawn in chunks of
+   ``kv_chunk_rows`` tokens; chunk c uses its own stream
+   ``PCG64(SeedSequence([seed, 1, c]))`` so chunks can be filled in parallel.  Dense workloads reference
    every ``t < L_b``; sparse workloads reference the union of their indices.
    Every other byte of the pool (page tails, slack pages, unreferenced rows)
    is 0xFF: NaN in bf16, e4m3fn and fp32, so any read of it shows up.
@@ -30,8 +32,10 @@ only; decoding is done separately by each consumer.
 
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 import math
+import os
 from typing import List, Optional, Sequence
 
 import numpy as np
@@ -152,7 +156,7 @@ def make_workload(name: str, *, batch: int, h_q: int, s_q: int, seqlens,
                   is_causal: int = 0, page_size: int = 64, slack: float = 0.1,
                   softmax_scale: Optional[float] = None,
                   max_pages_per_seq: Optional[int] = None,
-                  kv_chunk_rows: int = 1 << 18) -> Workload:
+                  kv_chunk_rows: int = 1 << 15) -> Workload:
     """Build one seeded workload following the recipe in the module docstring.
 
     ``seqlens`` is either a sequence of ints (one per batch entry) or a
@@ -202,17 +206,31 @@ def make_workload(name: str, *, batch: int, h_q: int, s_q: int, seqlens,
     rb = np.concatenate(refs_b) if refs_b else np.zeros(0, np.int64)
     rt = np.concatenate(refs_t) if refs_t else np.zeros(0, np.int64)
     pages = table[rb, rt // page_size].astype(np.int64)
-    slots = rt % page_size
+    dest = pages * page_size + rt % page_size
     flat = kv.reshape(pool * page_size, row_bytes)
-    dest = pages * page_size + slots
-    for s in range(0, rb.shape[0], kv_chunk_rows):
-        e = min(rb.shape[0], s + kv_chunk_rows)
-        x = rng.standard_normal((e - s, D_QK), dtype=np.float32)
+    # KV rows come in fixed chunks of kv_chunk_rows referenced tokens; chunk c
+    # draws from its own stream PCG64(SeedSequence([seed, 1, c])), so the
+    # values do not depend on how many threads fill the chunks.
+    n_chunks = -(-rb.shape[0] // kv_chunk_rows)
+
+    def fill(c):
+        s0 = c * kv_chunk_rows
+        e0 = min(rb.shape[0], s0 + kv_chunk_rows)
+        crng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 1, c])))
+        x = crng.standard_normal((e0 - s0, D_QK), dtype=np.float32)
         bits = bf16_bits_from_f32(x)
         if kv_format == KV_BF16:
-            flat[dest[s:e]] = bits.view(np.uint8).reshape(e - s, row_bytes)
+            flat[dest[s0:e0]] = bits.view(np.uint8).reshape(e0 - s0, row_bytes)
         else:
-            flat[dest[s:e]] = encode_fp8_rows(bits)
+            flat[dest[s0:e0]] = encode_fp8_rows(bits)
+
+    workers = max(1, min(16, os.cpu_count() or 1))
+    if n_chunks <= 1 or workers == 1:
+        for c in range(n_chunks):
+            fill(c)
+    else:
+        with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+            list(ex.map(fill, range(n_chunks)))
     scale = np.float32(1.0 / math.sqrt(D_QK)) if softmax_scale is None else np.float32(softmax_scale)
     return Workload(name=name, batch=batch, s_q=s_q, h_q=h_q, page_size=page_size,
                     kv_format=kv_format, topk=topk, is_causal=is_causal,

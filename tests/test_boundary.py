@@ -1,0 +1,161 @@
+"""C-ABI library checks that need no GPU: it loads, exports every symbol the
+header declares, and rejects malformed arguments on the host (no device is
+touched: the checks run before any HIP call)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import torch
+
+import paged_kv_head_amd as mla
+
+# These calls pass fake device addresses and rely on the host-side checks
+# rejecting them before any launch: run them only where no GPU exists.
+pytestmark = pytest.mark.skipif(torch.cuda.is_available(),
+                                reason="host-only checks with fake device addresses")
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "mla_decode.h")
+FAKE = 0x10000  # an aligned non-null address; never dereferenced by these calls
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ("mla_decode_get_metadata", "mla_decode_paged", "mla_decode_combine",
+                 "mla_decode_paged_fp8", "mla_decode_sparse_fp8", "mla_last_error"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(mla.library_path())
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def good(**kw):
+    d = dict(batch=2, s_q=1, h_q=16, num_pages=7, max_pages_per_seq=5, softmax_scale=1 / 24)
+    d.update(kw)
+    return mla.Problem.make(**d)
+
+
+def call_paged(p, **ptrs):
+    lib = mla._load()
+    a = dict(q=FAKE, kv=FAKE, bt=FAKE, sl=FAKE, idx=None, sched=FAKE, parts=4, splits=FAKE,
+             ws=FAKE, ws_bytes=1 << 40, out=FAKE, lse=FAKE)
+    a.update(ptrs)
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.mla_decode_paged(ctypes.byref(p), v(a["q"]), v(a["kv"]), v(a["bt"]), v(a["sl"]),
+                                v(a["idx"]), v(a["sched"]), a["parts"], v(a["splits"]), v(a["ws"]),
+                                a["ws_bytes"], v(a["out"]), v(a["lse"]), None)
+
+
+@pytest.mark.parametrize("field,value,status,needle", [
+    ("h_kv", 2, mla.MLA_ERR_UNSUPPORTED, "h_kv"),
+    ("d_qk", 512, mla.MLA_ERR_UNSUPPORTED, "d_qk"),
+    ("d_v", 576, mla.MLA_ERR_UNSUPPORTED, "d_v"),
+    ("page_size", 16, mla.MLA_ERR_UNSUPPORTED, "page_size"),
+    ("s_q", 0, mla.MLA_ERR_INVALID_ARGUMENT, "s_q"),
+    ("h_q", 0, mla.MLA_ERR_INVALID_ARGUMENT, "h_q"),
+    ("batch", -1, mla.MLA_ERR_INVALID_ARGUMENT, "batch"),
+    ("num_pages", 0, mla.MLA_ERR_INVALID_ARGUMENT, "num_pages"),
+    ("max_pages_per_seq", 0, mla.MLA_ERR_INVALID_ARGUMENT, "max_pages_per_seq"),
+    ("kv_format", 7, mla.MLA_ERR_INVALID_ARGUMENT, "kv_format"),
+    ("is_causal", 2, mla.MLA_ERR_INVALID_ARGUMENT, "is_causal"),
+    ("flags", 8, mla.MLA_ERR_INVALID_ARGUMENT, "flags"),
+    ("softmax_scale", float("nan"), mla.MLA_ERR_INVALID_ARGUMENT, "softmax_scale"),
+    ("softmax_scale", float("inf"), mla.MLA_ERR_INVALID_ARGUMENT, "softmax_scale"),
+    ("topk", -3, mla.MLA_ERR_INVALID_ARGUMENT, "topk"),
+])
+def test_problem_fields_rejected(field, value, status, needle):
+    p = good(**{field: value}) if field in ("softmax_scale",) else good()
+    if field != "softmax_scale":
+        setattr(p, field, value)
+    assert call_paged(p) == status
+    assert needle in mla.mla_last_error()
+
+
+def test_sparse_causal_rejected():
+    p = good(topk=8, is_causal=1)
+    assert call_paged(p, idx=FAKE) == mla.MLA_ERR_INVALID_ARGUMENT
+    assert "is_causal" in mla.mla_last_error()
+
+
+@pytest.mark.parametrize("name", ["q", "kv", "bt", "sl", "sched", "splits", "ws", "out", "lse"])
+def test_null_pointer_named(name):
+    assert call_paged(good(), **{name: None}) == mla.MLA_ERR_INVALID_ARGUMENT
+    err = mla.mla_last_error()
+    assert "NULL" in err
+
+
+@pytest.mark.parametrize("name,label", [("q", "q"), ("kv", "kv_pool"), ("out", "out"), ("ws", "workspace")])
+def test_misaligned_pointer_named(name, label):
+    assert call_paged(good(), **{name: FAKE + 4}) == mla.MLA_ERR_INVALID_ARGUMENT
+    assert mla.mla_last_error().startswith(label)
+
+
+def test_indices_must_match_topk():
+    assert call_paged(good(), idx=FAKE) == mla.MLA_ERR_INVALID_ARGUMENT
+    assert "indices" in mla.mla_last_error()
+    assert call_paged(good(topk=4), idx=None) == mla.MLA_ERR_INVALID_ARGUMENT
+    assert "indices" in mla.mla_last_error()
+
+
+def test_workspace_too_small():
+    p = good()
+    need = mla.mla_decode_workspace_bytes(p, 4)
+    assert call_paged(p, ws_bytes=need - 1) == mla.MLA_ERR_WORKSPACE_TOO_SMALL
+    assert "workspace_bytes" in mla.mla_last_error()
+
+
+@pytest.mark.parametrize("parts", [0, -1, 65537])
+def test_num_parts_range(parts):
+    assert call_paged(good(), parts=parts) == mla.MLA_ERR_INVALID_ARGUMENT
+    assert "num_parts" in mla.mla_last_error()
+
+
+def test_named_entry_points_check_format():
+    lib = mla._load()
+    p = good()  # bf16, dense
+    v = ctypes.c_void_p(FAKE)
+    st = lib.mla_decode_paged_fp8(ctypes.byref(p), v, v, v, v, v, 4, v, v, 1 << 40, v, v, None)
+    assert st == mla.MLA_ERR_INVALID_ARGUMENT and "kv_format" in mla.mla_last_error()
+    p = good(kv_format=mla.MLA_KV_FP8_656)
+    st = lib.mla_decode_sparse_fp8(ctypes.byref(p), v, v, v, v, v, v, 4, v, v, 1 << 40, v, v, None)
+    assert st == mla.MLA_ERR_INVALID_ARGUMENT and "topk" in mla.mla_last_error()
+
+
+def test_sizes_and_units():
+    p = good(batch=3, s_q=2, h_q=128)
+    assert mla.mla_decode_num_units(p) == 3
+    assert mla.mla_decode_metadata_size(p, 10) == (80, 4)
+    p.topk = 64
+    assert mla.mla_decode_num_units(p) == 6
+    assert mla.mla_decode_metadata_size(p, 10) == (80, 7)
+    assert mla.mla_decode_workspace_bytes(p, 10) > 0
+
+
+def test_python_wrapper_raises_value_error():
+    p = good(h_kv=3)
+    with pytest.raises(mla.MlaError):
+        mla.mla_decode_workspace_bytes(p, 4)
+    p = good(s_q=0)
+    with pytest.raises(ValueError, match="s_q"):
+        mla.mla_decode_workspace_bytes(p, 4)
+
+
+def test_combine_checks():
+    lib = mla._load()
+    p = good()
+    v = ctypes.c_void_p(FAKE)
+    assert lib.mla_decode_combine(ctypes.byref(p), 4, None, v, 1 << 40, v, v, None) == mla.MLA_ERR_INVALID_ARGUMENT
+    assert "num_splits" in mla.mla_last_error()
+    assert lib.mla_decode_combine(ctypes.byref(p), 4, v, v, 16, v, v, None) == mla.MLA_ERR_WORKSPACE_TOO_SMALL

@@ -1,0 +1,224 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the
+same seeded inputs, at sizes the oracle finishes in seconds (several tiles,
+ragged tails), plus bit-exact layout probes and invariances."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_head_amd as mla
+import synth
+from oracle.schedule import blocks_per_unit, schedule
+from tests.harness import assert_close, run, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def reduced(n, batch, seed=None):
+    return synth.config_workload(n, batch=batch, seed=seed)
+
+
+# ------------------------------------------------------------ configs ---
+
+@pytest.mark.parametrize("n,batch", [(1, None), (2, 4), (3, 3), (4, 2), (5, 2)])
+def test_config_parity(n, batch):
+    w = synth.config_workload(n, batch=batch)
+    print(f"config {n} batch {w.batch} seqlens {w.cache_seqlens.tolist()}", flush=True)
+    out, lse = run(w)
+    ref_out, ref_lse = oracle.mla_decode(w)
+    assert_close(out, lse, ref_out, ref_lse, what=f"config {n}")
+
+
+@pytest.mark.parametrize("n", [1, 3, 5])
+def test_natural_base(n):
+    w = synth.config_workload(n, batch=2)
+    out, lse = run(w, natural=True)
+    ref_out, ref_lse = oracle.mla_decode(w, natural=True)
+    # lse tolerance is stated in log2 units; natural-log lse is ln2 times it
+    assert_close(out, lse / math.log(2), ref_out, ref_lse / math.log(2), what="natural")
+
+
+@pytest.mark.parametrize("parts", [1, 2, 3, 7, 64, 300, 1000])
+def test_forced_split_counts(parts):
+    w = synth.make_workload("t", batch=3, h_q=128, s_q=2, seqlens=[700, 129, 1], seed=31, is_causal=1)
+    out, lse = run(w, num_parts=parts)
+    ref_out, ref_lse = oracle.mla_decode(w)
+    assert_close(out, lse, ref_out, ref_lse, what=f"num_parts={parts}")
+
+
+@pytest.mark.parametrize("h_q,s_q,causal", [(16, 1, 0), (20, 3, 1), (64, 2, 1), (100, 1, 0),
+                                            (128, 1, 0), (192, 1, 0), (256, 2, 1)])
+def test_head_shapes(h_q, s_q, causal):
+    w = synth.make_workload("t", batch=2, h_q=h_q, s_q=s_q, seqlens=[65, 300], seed=32, is_causal=causal)
+    out, lse = run(w)
+    ref_out, ref_lse = oracle.mla_decode(w)
+    assert_close(out, lse, ref_out, ref_lse, what=f"h_q={h_q} s_q={s_q}")
+
+
+@pytest.mark.parametrize("kv_format", [synth.KV_BF16, synth.KV_FP8_656])
+def test_edge_lengths(kv_format):
+    """Empty sequences, one token, page boundaries, causal with L < s_q."""
+    w = synth.make_workload("t", batch=7, h_q=32, s_q=2, seqlens=[0, 1, 63, 64, 65, 128, 2],
+                            seed=33, is_causal=1, kv_format=kv_format)
+    out, lse = run(w, num_parts=5)
+    ref_out, ref_lse = oracle.mla_decode(w)
+    assert_close(out, lse, ref_out, ref_lse, what="edges")
+    assert np.all(lse[0] == -np.inf) and np.all(out[0] == 0)
+    assert np.all(lse[1, 0] == -np.inf) and np.all(out[1, 0] == 0)  # L=1, s_q=2: query 0 sees nothing
+
+
+def test_empty_batch_entries_only():
+    w = synth.make_workload("t", batch=3, h_q=16, s_q=1, seqlens=[0, 0, 0], seed=34)
+    out, lse = run(w)
+    assert np.all(lse == -np.inf) and np.all(out == 0)
+
+
+@pytest.mark.parametrize("topk", [1, 63, 64, 65, 200])
+def test_sparse_topk_sizes(topk):
+    w = synth.make_workload("t", batch=2, h_q=128, s_q=2, seqlens=[300, 1000], seed=35,
+                            kv_format=synth.KV_FP8_656, topk=topk)
+    out, lse = run(w)
+    ref_out, ref_lse = oracle.mla_decode(w)
+    assert_close(out, lse, ref_out, ref_lse, what=f"topk={topk}")
+
+
+def test_sparse_invalid_and_duplicate_indices():
+    sp = synth.make_workload("t", batch=2, h_q=64, s_q=2, seqlens=[300, 90], seed=36,
+                             kv_format=synth.KV_FP8_656, topk=80)
+    # same shapes with every cache row filled, so edited indices reach data
+    w = synth.make_workload("t", batch=2, h_q=64, s_q=2, seqlens=[300, 90], seed=36,
+                            kv_format=synth.KV_FP8_656)
+    w.topk = 80
+    idx = sp.indices.copy()
+    idx[0, 0, ::7] = -1
+    idx[0, 1, 5:20] = 299          # duplicates of a valid position
+    idx[1, 0, :] = -1              # nothing visible
+    idx[1, 1, 3] = 90              # == L: skipped
+    idx[1, 1, 4] = 2 ** 30         # far out of range: skipped
+    w.indices = idx
+    out, lse = run(w)
+    ref_out, ref_lse = oracle.mla_decode(w)
+    assert_close(out, lse, ref_out, ref_lse, what="sparse invalid/dup")
+    assert np.all(lse[1, 0] == -np.inf)
+
+
+def test_bf16_sparse():
+    w = synth.make_workload("t", batch=2, h_q=32, s_q=1, seqlens=[500, 70], seed=37, topk=100)
+    out, lse = run(w)
+    ref_out, ref_lse = oracle.mla_decode(w)
+    assert_close(out, lse, ref_out, ref_lse, what="bf16 sparse")
+
+
+# ------------------------------------------------------ bit-exact probes ---
+
+@pytest.mark.parametrize("kv_format", [synth.KV_BF16, synth.KV_FP8_656])
+def test_single_key_returns_dequantised_row_bit_exact(kv_format):
+    """topk = 1: weight is exactly 1, so out is the bf16 latent row itself."""
+    L = 200
+    # a dense workload references (and fills) every token; then use it sparsely
+    full = synth.make_workload("t", batch=1, h_q=16, s_q=6, seqlens=[L], seed=38, kv_format=kv_format)
+    full.topk = 1
+    full.indices = np.array([[[0], [63], [64], [65], [127], [L - 1]]], dtype=np.int32)
+    out, lse = run(full)
+    for i, t in enumerate(full.indices[0, :, 0]):
+        page = full.block_table[0, t // 64]
+        row = oracle.decode_row(full.kv[page, t % 64], kv_format)
+        assert np.array_equal(out[0, i], np.broadcast_to(row[:512], (16, 512))), f"token {t}"
+
+
+def test_fp8_codes_all_values_bit_exact():
+    """Every finite e4m3 code, under several scales, dequantises exactly as
+    the oracle's codec does (read back through a one-key attention)."""
+    w = synth.make_workload("t", batch=1, h_q=16, s_q=4, seqlens=[64], seed=39,
+                            kv_format=synth.KV_FP8_656, slack=0)  # every row filled
+    w.topk = 1
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    kv = w.kv.copy()
+    scales = np.array([1.0, 2.0 ** -7, 3.3e-3, 0.731], dtype=np.float32)
+    for slot in range(4):
+        row = np.zeros(656, dtype=np.uint8)
+        row[:254] = codes
+        row[254:508] = codes
+        row[508:512] = codes[:4]
+        row[512:528] = np.roll(scales, slot).view(np.uint8)
+        row[528:] = kv[0, slot, 528:]
+        kv[0, slot] = row
+    w.kv = kv
+    w.indices = np.array([[[0], [1], [2], [3]]], dtype=np.int32)
+    out, lse = run(w)
+    for i in range(4):
+        ref = oracle.decode_row(kv[0, i], synth.KV_FP8_656)
+        assert np.array_equal(out[0, i, 0], ref[:512])
+
+
+def test_lse_one_hot_probe_bit_exact():
+    """q one-hot at RoPE dim h with scale 1 and one key: lse == K[512+h] exactly."""
+    w = synth.make_workload("t", batch=1, h_q=64, s_q=1, seqlens=[100], seed=40)  # every row filled
+    w.topk = 1
+    q = np.zeros_like(w.q)
+    for h in range(64):
+        q[0, 0, h, 512 + h] = 0x3F80  # bf16 1.0
+    w.q = q
+    w.indices = np.array([[[77]]], dtype=np.int32)
+    out, lse = run(w, softmax_scale=1.0)
+    page = w.block_table[0, 77 // 64]
+    row = oracle.decode_row(w.kv[page, 77 % 64], 0)
+    assert np.array_equal(lse[0, 0], row[512:576])
+
+
+# --------------------------------------------------------- invariances ---
+
+@pytest.mark.parametrize("kv_format", [synth.KV_BF16, synth.KV_FP8_656])
+def test_page_permutation_bit_identical(kv_format):
+    w = synth.make_workload("t", batch=3, h_q=128, s_q=2, seqlens=[300, 64, 129], seed=41,
+                            kv_format=kv_format, is_causal=1)
+    out1, lse1 = run(w)
+    perm = np.random.default_rng(5).permutation(w.num_pages)
+    kv2 = np.empty_like(w.kv)
+    kv2[perm] = w.kv
+    w.block_table = np.where(w.block_table >= 0, perm[np.maximum(w.block_table, 0)], -1).astype(np.int32)
+    w.kv = kv2
+    out2, lse2 = run(w)
+    assert np.array_equal(out1, out2) and np.array_equal(lse1, lse2)
+
+
+def test_repeat_runs_bit_identical():
+    w = synth.config_workload(2, batch=4)
+    t = to_device(w)
+    a = run(w, tensors=t)
+    b = run(w, tensors=t)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("n", [2, 4, 5])
+def test_metadata_matches_cpu_reference(n):
+    w = synth.config_workload(n, batch=16)
+    out, lse, sched, splits, parts = run(w, return_meta=True)
+    nb = blocks_per_unit(w.cache_seqlens, w.s_q, w.topk)
+    ref_sched, ref_splits = schedule(nb, parts, int(sched[6]))
+    assert np.array_equal(sched.reshape(parts, 8), np.array(ref_sched, dtype=np.int32))
+    assert np.array_equal(splits, np.array(ref_splits, dtype=np.int32))
+
+
+def test_flush_path_growing_scores():
+    """Scores that climb by far more than the lazy-rescale threshold across
+    tiles force the flush path; results must still match the oracle."""
+    L = 640
+    w = synth.make_workload("t", batch=2, h_q=128, s_q=1, seqlens=[L, 300], seed=42, slack=0)
+    kv = w.kv.copy()
+    for b in range(2):
+        for t in range(int(w.cache_seqlens[b])):
+            page, slot = w.block_table[b, t // 64], t % 64
+            x = np.full(576, 0.05 * t, dtype=np.float32)  # scores grow ~ linearly in t
+            x[:512] += np.float32(np.sin(t))
+            kv[page, slot] = synth.bf16_bits_from_f32(x).view(np.uint8)
+    w.kv = kv
+    q = np.full(w.q.shape, 0x3F80, dtype=np.uint16)  # all-ones queries
+    w.q = q
+    for parts in (None, 3):
+        out, lse = run(w, num_parts=parts, softmax_scale=0.02)
+        ref_out, ref_lse = oracle.mla_decode(w, softmax_scale=0.02)
+        assert_close(out, lse, ref_out, ref_lse, what=f"flush parts={parts}")
