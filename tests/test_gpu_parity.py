@@ -106,7 +106,7 @@ def test_sparse_invalid_and_duplicate_indices():
 
 
 def test_bf16_sparse():
-    w = synth.make_workload("t", batch=2, h_q=32, s_q=1, seqlens=[500, 70], seed=37, topk=100)
+    w = synth.make_workload("t", batch=2, h_q=32, s_q=1, seqlens=[500, 170], seed=37, topk=100)
     out, lse = run(w)
     ref_out, ref_lse = oracle.mla_decode(w)
     assert_close(out, lse, ref_out, ref_lse, what="bf16 sparse")
