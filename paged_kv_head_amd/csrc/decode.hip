@@ -9,32 +9,39 @@
 // Work decomposition.  A workgroup of 4 waves owns 128 query rows of one
 // work unit (all heads of a query token share the single latent KV head, so
 // one latent tile feeds 128 rows) and walks the (unit, block) range its
-// split-KV part was given by the scheduler.  Wave w owns rows 32w..32w+31;
-// each lane keeps one row's Q (36 bf16x8 MFMA operands) in VGPRs and 256
-// fp32 output columns of that row in AGPRs.  One wave per SIMD: all latency
-// hiding comes from instruction-level overlap inside the wave.
+// split-KV part was given by the scheduler.  The two products split the
+// workgroup differently:
+//   * scores: wave w owns rows 32w..32w+31; each lane keeps one row's Q (36
+//     bf16x8 MFMA operands) in VGPRs and computes S^T = K Q^T, so it holds
+//     32 keys of ONE row and the row max / row sum are lane-local plus one
+//     exchange with lane^32;
+//   * output: wave w owns output columns 128w..128w+127 of all 128 rows
+//     (16 fp32 32x32 accumulator blocks in AGPRs) and computes
+//     O^T += V^T P^T, with P^T of every row read from LDS.
+// The output split makes each wave read only its quarter of V, so the V
+// tile crosses the LDS once per workgroup instead of once per wave; V^T
+// operands need transposing LDS reads, which move half the bytes of a plain
+// 16-byte read, and they were the bottleneck of a row split.
 //
-// Per 64-token tile:
+// Per 64-token tile (two halves of 32 keys):
 //   1. Rows are resolved two tiles ahead: position t -> page = table[t / 64],
 //      slot = t % 64 ("Modular Platform 设计文档全景导读", section 四), or for
 //      sparse units through the index list first.
-//   2. The tile is copied one tile ahead, straight from global memory into
-//      LDS (global_load_lds_dwordx4, no registers).  bf16 tiles are double
-//      buffered; FP8 rows land in a staging buffer and are dequantised into
-//      the bf16 tile: bf16(float(e4m3) * tile scale) (FlashMLA page, section
-//      设计 2).  Keys that are not visible are copied from a zero row, so
-//      masked keys contribute exactly 0 to P*V.
-//   3. S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = 32 keys x 16 dims from
-//      LDS, B = 16 dims x 32 rows from registers).  The transposed product
-//      leaves each lane holding 32 keys of ONE query row, so the row max and
-//      row sum are lane-local plus one exchange with lane^32.
-//   4. Online softmax in base 2 with a lazily refreshed running max: the
-//      running output is never rescaled in the loop; if some row's max grows
-//      by more than 8 the wave parks its partial result in a per-lane flush
-//      record and restarts (rare), merged back exactly in the epilogue.
-//   5. O^T += V^T P^T with the same MFMA: B = P^T straight from the S^T
-//      accumulators (keys permuted consistently on both operands), A = V^T
-//      read from the same tile with LDS transpose reads (V = first 512 dims).
+//   2. The next tile is copied straight from global memory into LDS
+//      (global_load_lds_dwordx4, no registers) while this one is computed.
+//      bf16 tiles are double buffered; FP8 rows land in a staging buffer and
+//      are dequantised into the bf16 tile: bf16(float(e4m3) * tile scale)
+//      (FlashMLA page, section 设计 2).  Keys that are not visible are copied
+//      from a zero row, so masked keys contribute exactly 0 to P*V.
+//   3. S^T for half 0, then S^T for half 1 with the softmax of half 0
+//      interleaved between its MFMAs: mask, scale, max, exp2, row sum, and
+//      the bf16 P^T of the half written to LDS.
+//   4. Barrier; O^T += V^T P^T for half 0 with the softmax of half 1
+//      interleaved; barrier; O^T += V^T P^T for half 1.
+//   Online softmax in base 2 with a lazily refreshed running max: the
+//   running output is never rescaled in the loop; if some row's max grows by
+//   more than 8, every wave parks its partial outputs in a per-lane flush
+//   record and restarts them from zero (rare), merged back exactly at the end.
 // Epilogue: a unit processed in one segment writes bf16 out and lse; a split
 // unit writes normalised fp32 partials and their lse to the workspace for the
 // combine kernel.
@@ -49,7 +56,13 @@
 // rotation keeps both read patterns free of bank conflicts: 16 consecutive
 // rows at one chunk (K operand reads, 16 lanes of 16 bytes per cycle) and
 // 4 consecutive rows x 4 adjacent chunks (transpose reads of V, 32 lanes of
-// 8 bytes per cycle) each touch the 16 groups once.
+// 8 bytes per cycle) each touch the 16 groups once.  Chunk group 8 holds the
+// 64 RoPE dims, which only the score product reads; once every wave is past
+// the scores of a tile, it holds the P^T of the tile's second half.
+//
+// P^T layout.  Half a tile of probabilities is 128 rows x 32 keys of bf16,
+// 4 chunks per row; chunk c of row r sits at chunk r*4 + (c ^ ((r/4)%4)),
+// which keeps 16 consecutive rows at one chunk on 16 distinct bank groups.
 #include "internal.h"
 
 #include <type_traits>
@@ -71,16 +84,30 @@ constexpr int kQSteps = kDqk / 16;   // 36 MFMA k-steps over the 576 dims
 constexpr float kRescaleThreshold = 8.0f;
 constexpr int kTileBytes = kPage * kDqk * 2;  // 73728: 72 chunk groups of 1 KiB
 constexpr int kTileLoads = kTileBytes / 1024;  // 72 direct copies, 18 per wave
+constexpr int kRopeOffset = 8 * 512 * 16;      // chunk group 8: dims 512..575
 constexpr int kStageGroups = 6;                // raw FP8 row: 41 chunks in 6 groups of 8
 constexpr int kStageBytes = kStageGroups * 8 * 16 * kPage;  // 49152
 constexpr int kStageLoads = kStageBytes / 1024;             // 48, 12 per wave
+constexpr int kPHalfBytes = kRowsPerGroup * 32 * 2;         // 8192: P^T of half a tile
 
 template <typename T>
 __device__ inline __attribute__((address_space(3))) T* lds_ptr(const void* p) {
   return (__attribute__((address_space(3))) T*)(p);
 }
 
-__device__ inline float wave_max_pair(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
+// (x of this lane) combined with (x of lane ^ 32), as two swapped copies.
+__device__ inline f32x2 swap_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return f32x2{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ inline float wave_max_pair(float x) {
+  const f32x2 p = swap_halves(x);
+  return fmaxf(p[0], p[1]);
+}
+__device__ inline float wave_sum_pair(float x) {
+  const f32x2 p = swap_halves(x);
+  return p[0] + p[1];
+}
 
 __device__ inline uint16_t bf16_bits(float x) {
   __bf16 h = (__bf16)x;  // v_cvt_pk_bf16_f32: round to nearest even
@@ -101,60 +128,95 @@ __device__ inline int tile_chunk(int r, int c) {
   return ((c >> 3) * 512 + r * 8 + ((c + swz(r)) & 7)) * 16;
 }
 
+// Byte offset of 16-byte chunk c (< 4) of query row r in a P^T half buffer.
+__device__ inline int p_chunk(int r, int c) { return (r * 4 + (c ^ ((r >> 2) & 3))) * 16; }
+
 // Zero bytes that stand in for the cache row of a key that is not visible.
 __device__ __attribute__((aligned(16))) const uint8_t g_zero_row[1168] = {};
 
-// 16 bytes per lane from global memory straight into LDS at
-// M0 + 16 * lane (lane layout checked on the device).  Issued from inline
-// assembly so the compiler's wait-count bookkeeping does not see it: it
-// would otherwise treat every later LDS read as unordered and wait for all
-// of them.  Completion is tracked by hand with MLA_WAIT_VMCNT.
-__device__ inline void lds_dma16(const void* g, void* lds_wave_base) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_wave_base);
+// LDS byte address of a __shared__ object (wave-uniform).
+__device__ inline uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p);
+}
+
+// 16 bytes per lane from global memory straight into LDS at m0 + 16 * lane
+// (lane layout checked on the device; no instruction offset, which would
+// move the LDS destination too).  Issued from inline assembly so the
+// compiler's wait-count bookkeeping does not see it: it would otherwise
+// treat every later LDS read as unordered and wait for all of them.
+// Completion is tracked by hand with MLA_WAIT_VMCNT.
+__device__ inline void lds_dma16(const void* g, uint32_t m0) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :: "v"(g), "s"(m0) : "memory", "m0");
 }
 
-// Copy of one bf16 tile.  Copy I = 4*t + wave (t < 18) fills chunk group
-// g = t/2 of rows 8*(I%8) .. +7: lane L takes row 32*(t%2) + 8*wave + L/8
-// and tile position L%8 of that row's group, i.e. source chunk
-// 8*g + ((L%8 - swz(row)) mod 8).
-__device__ inline void issue_tile_bf16(const uint8_t* __restrict__ kv, const int64_t* rowoff,
-                                       uint8_t* buf, int wave, int lane) {
-  asm volatile("" : "+v"(lane), "+v"(wave));  // keep the address math inside the tile loop
-  const uint8_t* base[2];
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const int row = 32 * half + 8 * wave + (lane >> 3);
-    const int c8 = ((lane & 7) - swz(row)) & 7;
-    const int64_t off = rowoff[row];
-    base[half] = (off >= 0 ? kv + off : g_zero_row) + 16 * c8;
-  }
-#pragma unroll
-  for (int t = 0; t < kTileLoads / 4; ++t) {
-    lds_dma16(base[t & 1] + 128 * (t >> 1), buf + 1024 * (4 * t + wave));
-  }
+// Cache byte offset of key `row` of a tile, from the lane that resolved it
+// (lane k of every wave holds the offset of key k; -1: not visible).
+__device__ inline int64_t row_offset(int64_t off_lane, int row) {
+  const int lo = __shfl((int)(uint32_t)off_lane, row);
+  const int hi = __shfl((int)(uint32_t)((uint64_t)off_lane >> 32), row);
+  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
 }
 
-// Copy of 64 raw 656-byte FP8 rows into the staging buffer, laid out as
-// [group g < 6][row][8 chunks]: chunk c of a row is at g = c/8, slot c%8
-// (chunks 41..47 do not exist and are copied from the zero row).
-__device__ inline void issue_tile_fp8(const uint8_t* __restrict__ kv, const int64_t* rowoff,
-                                      uint8_t* stage, int wave, int lane) {
-  asm volatile("" : "+v"(lane), "+v"(wave));
-  const uint8_t* base[2];
+// Copy of one tile, issued one 1 KiB copy at a time so the copies can be
+// spread between MFMAs.  bf16: copy I = 4*t + wave (t < 18) fills chunk
+// group g = t/2 of rows 8*(I%8) .. +7: lane L takes row 32*(t%2) + 8*wave +
+// L/8 and tile position L%8 of that row's group, i.e. source chunk
+// 8*g + ((L%8 - swz(row)) mod 8).  FP8: 64 raw 656-byte rows go to the
+// staging buffer laid out as [group g < 6][row][8 chunks], chunk c of a row
+// at g = c/8, slot c%8 (chunks 41..47 do not exist and are copied from the
+// zero row); copy I = 4*t + wave (t < 12) covers group t/2 of the same rows.
+template <int FMT>
+struct TileCopy {
+  static constexpr int kCopies = FMT == 0 ? kTileLoads / 4 : kStageLoads / 4;  // per wave
+  const uint8_t* base[2];  // this lane's source for rows 8*wave + L/8 and 32 + 8*wave + L/8
+  uint32_t dst;            // LDS address of copy 0 of this wave
+
+  __device__ inline void prepare(const uint8_t* __restrict__ kv, int64_t off_lane, uint32_t buf,
+                                 int wave, int lane) {
+    asm volatile("" : "+v"(lane), "+v"(wave));  // keep the address math inside the tile loop
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const int64_t off = rowoff[32 * half + 8 * wave + (lane >> 3)];
-    base[half] = (off >= 0 ? kv + off : g_zero_row) + 16 * (lane & 7);
+    for (int half = 0; half < 2; ++half) {
+      const int row = 32 * half + 8 * wave + (lane >> 3);
+      const int64_t off = row_offset(off_lane, row);
+      const int c8 = FMT == 0 ? ((lane & 7) - swz(row)) & 7 : (lane & 7);
+      base[half] = (off >= 0 ? kv + off : g_zero_row) + 16 * c8;
+    }
+    dst = __builtin_amdgcn_readfirstlane(buf + 1024 * wave);  // wave-uniform
   }
-  const bool tail_real = (lane & 7) == 0;  // chunk 40, the last RoPE chunk
-#pragma unroll
-  for (int t = 0; t < kStageLoads / 4; ++t) {
-    const uint8_t* src = base[t & 1] + 128 * (t >> 1);
-    if ((t >> 1) == 5) src = tail_real ? src : g_zero_row;
-    lds_dma16(src, stage + 1024 * (4 * t + wave));
+  // Copy t: source chunk group t/2 (128*(t/2) + 16*7 + 16 <= 1168, so a
+  // masked row's source stays inside the zero row).
+  template <int T>
+  __device__ inline void issue(int lane) const {
+    const uint8_t* src = base[T & 1] + 128 * (T >> 1);
+    if (FMT == 1 && (T >> 1) == 5)  // chunk 40 only; 41..47 from the zero row
+      src = (lane & 7) == 0 ? src : g_zero_row + 16 * (lane & 7);
+    lds_dma16(src, dst + 4096 * T);
+  }
+  template <int T = 0>
+  __device__ inline void issue_all(int lane) const {
+    if constexpr (T < kCopies) {
+      issue<T>(lane);
+      issue_all<T + 1>(lane);
+    }
+  }
+  // Copies spread over two score chains (step ST of chain CHAIN): bf16
+  // every 4th step, FP8 every 6th.
+  template <int CHAIN, int ST>
+  __device__ inline void issue_step(int lane) const {
+    constexpr int kEvery = FMT == 0 ? 4 : 6;
+    if constexpr (ST % kEvery == 1 && ST / kEvery < kCopies / 2)
+      issue<CHAIN * (kCopies / 2) + ST / kEvery>(lane);
+  }
+};
+
+// f(integral_constant<I>) for I = B .. E-1, unrolled at compile time.
+template <int B, int E, class F>
+__device__ inline __attribute__((always_inline)) void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
   }
 }
 
@@ -198,8 +260,8 @@ __device__ inline void dequant_stage(const uint8_t* stage, uint8_t* ks) {
 
 // Workgroup barrier without a memory fence: the compiler's fence would wait
 // for every outstanding global->LDS copy, including the next tile's.  LDS
-// reads issued before it are complete (their values were consumed); the
-// asm memory clobber keeps the compiler from moving LDS accesses across it.
+// accesses issued before it are complete (lgkmcnt(0)); the asm memory
+// clobber keeps the compiler from moving LDS accesses across it.
 #define MLA_BARRIER_NO_FENCE() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
 
 // s_waitcnt with only the vector-memory counter limited to n (n < 64).
@@ -213,14 +275,45 @@ __device__ inline void dequant_stage(const uint8_t* stage, uint8_t* ks) {
 // Back-to-back MFMAs chained through srcC need no wait states; the drain
 // below pads the chain before any VALU reads the result (an MFMA result read
 // by the VALU needs wait states the compiler cannot see through asm).
+// The leading s_nop 1 covers a VALU write of an operand register right
+// before the MFMA (two wait states), which the compiler cannot see either.
 __device__ inline void mfma_s_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a), "v"(b));
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a), "v"(b));
 }
 __device__ inline void mfma_s_acc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
 __device__ inline void mfma_s_drain(f32x16& acc) {
   asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15" : "+v"(acc));
+}
+
+// S^T for 32 keys (rows of the tile at kb) against this lane's Q row, with
+// hook(integral_constant<st>) emitted after the MFMA of k-step st (independent VALU work that
+// runs while the matrix core is busy).  K operands are read kPrefetch steps
+// ahead of their MFMA so the LDS latency hides behind the chain.
+template <class Hook>
+__device__ inline __attribute__((always_inline)) void score_chain(f32x16& acc, const uint8_t* kb,
+                                                                  const int* k_off,
+                                                                  const bf16x8* qf, Hook&& hook) {
+  auto kload = [&](int st) {
+    return *reinterpret_cast<const bf16x8*>(kb + k_off[st & 3] + 8192 * (st >> 2));
+  };
+  constexpr int kPrefetch = 4;
+  bf16x8 kf[kPrefetch];
+#pragma unroll
+  for (int st = 0; st < kPrefetch; ++st) kf[st] = kload(st);
+  static_for<0, kQSteps>([&](auto st_c) __attribute__((always_inline)) {
+    constexpr int st = decltype(st_c)::value;
+    const bf16x8 cur_k = kf[st % kPrefetch];
+    if constexpr (st + kPrefetch < kQSteps) kf[st % kPrefetch] = kload(st + kPrefetch);
+    if constexpr (st == 0)
+      mfma_s_first(acc, cur_k, qf[st]);
+    else
+      mfma_s_acc(acc, cur_k, qf[st]);
+    hook(st_c);
+    __builtin_amdgcn_sched_barrier(0);
+  });
+  mfma_s_drain(acc);
 }
 
 // Four accumulator values of a lane, copied out through the lane's private
@@ -235,33 +328,19 @@ __device__ inline f32x4 acc_quad(const f32x16& acc, int q4, f32x4* slot) {
   return v;
 }
 
-// Move a lane's (O, m, l) into its flush record, merging with what is
-// already there (two partial sums with references m1, m2 merge as
-// M = max, each scaled by 2^(m_i - M)), and restart O and l from zero.
-__device__ inline __attribute__((always_inline)) void flush_rows(float* rec, bool had, f32x16* o,
-                                                                 float m, float& l, f32x4* slot) {
-  float a = 0.0f, c = 1.0f, M = m;
-  if (had) {
-    const float mf = rec[257];
-    M = fmaxf(mf, m);
-    a = __builtin_amdgcn_exp2f(mf - M);
-    c = __builtin_amdgcn_exp2f(m - M);
-  }
-#pragma unroll
-  for (int cb = 0; cb < 16; ++cb) {
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      f32x4* dst = reinterpret_cast<f32x4*>(rec + cb * 16 + 4 * q4);
-      const f32x4 old = had ? *dst * a : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      *dst = old + acc_quad(o[cb], q4, slot) * c;
-    }
-    // zero through the MFMA unit: keeps the accumulators in AGPRs
-    o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf16x8{}, bf16x8{}, f32x16{}, 0, 0, 0);
-  }
-  rec[256] = (had ? rec[256] * a : 0.0f) + l * c;
-  rec[257] = M;
-  l = 0.0f;
+// exp2(x - M) for a merge of partial sums, 0 for a part that saw no key.
+__device__ inline float merge_factor(float x, float M) {
+  return x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(x - M);
 }
+
+// Per-half softmax state of a lane (its row, its 16 keys of the half).
+struct HalfSoftmax {
+  float tmax;   // max of the masked, scaled scores
+  float mo;     // running max before this half's update
+  float muse;   // reference the probabilities are taken against
+  float lh;     // this half's part of the row sum
+  bf16x8 pf[2]; // bf16 probabilities, MFMA operand order
+};
 
 template <int FMT, bool SPARSE>
 __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
@@ -271,8 +350,9 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
   // other.
   __shared__ __attribute__((aligned(16))) uint8_t lds0[kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t lds1[FMT == 0 ? kTileBytes : kStageBytes];
-  __shared__ int64_t rowoff[2][kPage];
-  __shared__ uint32_t vmask[2][2];
+  __shared__ __attribute__((aligned(16))) uint8_t pbuf[kPHalfBytes];  // P^T of half 0
+  __shared__ float mold_s[2][kRowsPerGroup];  // per row: running max before each half's update
+  __shared__ __attribute__((aligned(16))) uint32_t gflag[2][4];  // per wave: some row grew
   __shared__ f32x4 oslots[kThreads];  // per-lane slot for copying accumulators
   f32x4* const oslot = &oslots[threadIdx.x];
 
@@ -292,21 +372,23 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int n = lane & 31;    // row within the wave / key-slot group
+  const int n = lane & 31;    // row within a 32-row block / key-slot group
   const int h = lane >> 5;    // half of the wave
   const int j16 = lane & 15;  // lane within its 16-lane group
-  const int r = grp * kRowsPerGroup + wave * 32 + n;  // query row in unit
+  const int rs = wave * 32 + n;                 // score row of this lane, in the group
+  const int r = grp * kRowsPerGroup + rs;       // ... in the unit
   const bool row_ok = r < s.rows;
-  // per-lane flush record: 256 output columns, l, m
-  float* flush = a.ws_flush + ((int64_t)(part * s.groups + grp) * kThreads + threadIdx.x) * kFlushFloats;
+  // per-lane flush record: 256 output values (block (cb, rb) at 16*(4cb+rb)),
+  // the 4 output rows' maxima, the score row's sum and maximum
+  float* rec = a.ws_flush + ((int64_t)(part * s.groups + grp) * kThreads + threadIdx.x) * kFlushFloats;
 
   // Lane-constant parts of the LDS operand addresses (tile layout above).
   // K operand, step st: row 32*kb2 + n, chunk 2*st + h.
   int k_off[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) k_off[i] = n * 128 + 16 * ((2 * i + h + swz(n)) & 7);
-  // V^T operand (transpose read), column block cb, key sub-block (kb2, sp,
-  // e4): row 32*kb2 + 16*sp + 8*e4 + 4*h + j16/4, chunk 4*cb + 2*(n/16) +
+  // V^T operand (transpose read), column block cbg, key sub-block (kb2, sp,
+  // e4): row 32*kb2 + 16*sp + 8*e4 + 4*h + j16/4, chunk 4*cbg + 2*(n/16) +
   // (j16%4)/2, byte 8*(j16%2) inside the chunk.  The row rotation depends on
   // e4 but not on kb2 or sp.
   int v_off[2][2];
@@ -317,6 +399,10 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
     for (int p = 0; p < 2; ++p)
       v_off[p][e4] = (8 * e4 + 4 * h + (j16 >> 2)) * 128 + 16 * ((4 * p + y) & 7) + 8 * (j16 & 1);
   }
+  // P^T operand / P^T store: row 32*rb + n, chunk 2*sp + h.
+  int p_off[2];
+#pragma unroll
+  for (int sp = 0; sp < 2; ++sp) p_off[sp] = p_chunk(n, 2 * sp + h);
 
   for (int u = ub; u < s.units && (u < ue || (u == ue && ke > 0)); ++u) {
     const int b = SPARSE ? u / s.s_q : u;
@@ -328,26 +414,42 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
     const int seg = (u == ub) ? split0 : 0;
     const int nsplit = a.num_splits[u + 1] - a.num_splits[u];
 
-    // Q operand fragments of this lane's row: dims 16*st + 8*h .. +8
+    // Q operand fragments of this lane's score row: dims 16*st + 8*h .. +8
     bf16x8 qf[kQSteps];
     {
       const uint16_t* qrow = a.q + ((int64_t)u * s.rows + (row_ok ? r : 0)) * kDqk + 8 * h;
 #pragma unroll
       for (int st = 0; st < kQSteps; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(qrow + 16 * st);
+      // The kernel works with a positive score scale: scale * (q.k) equals
+      // |scale| * ((-q).k) for a negative scale (a sign flip of bf16 is
+      // exact) and 1 * (0.k) = 0 for a zero scale.
+      if (s.scale_log2 <= 0.0f) {
+        const uint32_t flip = s.scale_log2 < 0.0f ? 0x80008000u : 0u;
+        const uint32_t keep = s.scale_log2 < 0.0f ? 0xffffffffu : 0u;
+#pragma unroll
+        for (int st = 0; st < kQSteps; ++st) {
+          u32x4 w = __builtin_bit_cast(u32x4, qf[st]);
+          w = (w & keep) ^ flip;
+          qf[st] = __builtin_bit_cast(bf16x8, w);
+        }
+      }
     }
+    const float scale = s.scale_log2 == 0.0f ? 1.0f : fabsf(s.scale_log2);  // > 0
     // last visible position for this row (dense causal)
     int tlim = L - 1;
     if (!SPARSE && s.is_causal) tlim = L - s.s_q + (r / s.h_q);
 
-    float m = -INFINITY;  // running (possibly stale) max, log2 units
+    float m = -INFINITY;  // running (possibly stale) max of the score row, log2 units
     float l = 0.0f;       // running sum of this lane's half of the keys
-    bool flushed = false; // wave-uniform: rows parked in the flush area
-    f32x16 o[16];
+    bool flushed = false; // workgroup-uniform: outputs parked in the flush records
+    f32x16 o[4][4];       // O^T block (column block cb of this wave, row block rb)
 #pragma unroll
-    for (int cb = 0; cb < 16; ++cb) o[cb] = f32x16{};
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) o[cb][rb] = f32x16{};
 
-    // Row resolution.  Every wave resolves (redundantly, so that all waves
-    // issue the same number of memory operations); wave 0 publishes.
+    // Row resolution.  Every wave resolves all 64 keys of a tile (lane k:
+    // key k) and takes the rows it copies from the resolving lanes.
     //   res_t:   logical position of key `lane` in tile kt+2
     //   res_off: cache byte offset of key `lane` in tile kt+1 (-1: masked)
     const int32_t* idx_row = SPARSE ? a.indices + (int64_t)u * s.topk : nullptr;
@@ -366,31 +468,25 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
       return visible(t) ? ((int64_t)page * kPage + (t & 63)) * kRowBytes : (int64_t)-1;
     };
     constexpr int kResolveLoads = SPARSE ? 2 : 1;  // per thread per tile
-    auto publish = [&](int slot, int64_t off) {
-      if (wave == 0) {
-        rowoff[slot][lane] = off;
-        const uint64_t bal = __ballot(off >= 0);
-        if (lane == 0) { vmask[slot][0] = (uint32_t)bal; vmask[slot][1] = (uint32_t)(bal >> 32); }
-      }
-    };
     int res_t, pg2 = 0, t3 = -1;
     int64_t res_off;
-    __syncthreads();  // the previous segment's last tile is fully consumed
+    uint64_t vm_cur;  // keys of the current tile that are visible (sparse masking)
+    __syncthreads();  // the previous segment is fully consumed (tiles, P^T, epilogue slots)
     {
       const int t0 = position(kfirst);
       const int t1 = position(kfirst + 1);
       res_t = position(kfirst + 2);
-      publish(0, offset_of(t0, page_of(t0)));
+      const int64_t off0 = offset_of(t0, page_of(t0));
       res_off = offset_of(t1, page_of(t1));
-    }
-    __syncthreads();
-    if constexpr (FMT == 0) {
-      issue_tile_bf16(a.kv, rowoff[0], lds0, wave, lane);
-    } else {
-      issue_tile_fp8(a.kv, rowoff[0], lds1, wave, lane);
-      MLA_WAIT_VMCNT(0);
-      __syncthreads();
-      dequant_stage(lds1, lds0);
+      vm_cur = __ballot(off0 >= 0);
+      TileCopy<FMT> first;
+      first.prepare(a.kv, off0, lds_addr(FMT == 0 ? lds0 : lds1), wave, lane);
+      first.issue_all(lane);
+      if constexpr (FMT == 1) {
+        MLA_WAIT_VMCNT(0);
+        __syncthreads();
+        dequant_stage(lds1, lds0);
+      }
     }
     // Everything loaded so far (Q, rows, the first tile) is needed before the
     // first compute anyway.  Waiting here also keeps the compiler from
@@ -398,191 +494,274 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
     // would stall on the next tile's copies that it cannot see.
     MLA_WAIT_VMCNT(0);
 
-    // One tile: the copy of tile kt+1 and the row resolution of kt+2/kt+3
-    // are issued, then tile kt is computed.  CUR is the tile buffer holding
-    // tile kt (bf16 path; the loop is unrolled by two so it is static).
-    auto tile_step = [&](auto cur_c, int kt) {
-      constexpr int cur = decltype(cur_c)::value;
-      const bool has_next = kt + 1 < kend;
-      // 1. publish the rows of tile kt+1, then start copying it
-      publish(cur ^ 1, res_off);
-      __syncthreads();  // rows visible; FP8: dequantised tile kt visible
-      if (has_next) {
-        if constexpr (FMT == 0)
-          issue_tile_bf16(a.kv, rowoff[cur ^ 1], cur ? lds0 : lds1, wave, lane);
-        else
-          issue_tile_fp8(a.kv, rowoff[cur ^ 1], lds1, wave, lane);
+    // Park this lane's outputs (all 16 blocks) and its score row's sum in
+    // the flush record and restart them from zero.  Two partial results
+    // with references m1, m2 merge as M = max, each scaled by 2^(m_i - M).
+    // Every party to a row applies the same sequence of maxima, so the
+    // copies of a row's record maximum stay identical.
+    auto flush = [&](int half, float mo_own) __attribute__((always_inline)) {
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const float mo = mold_s[half][32 * rb + n];
+        float M = mo, fa = 0.0f, fc = 1.0f;
+        if (flushed) {
+          const float mr = rec[256 + rb];
+          M = fmaxf(mr, mo);
+          fa = merge_factor(mr, M);
+          fc = merge_factor(mo, M);
+        }
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            f32x4* dst = reinterpret_cast<f32x4*>(rec + (4 * cb + rb) * 16 + 4 * q4);
+            const f32x4 old = flushed ? *dst * fa : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            *dst = old + acc_quad(o[cb][rb], q4, oslot) * fc;
+          }
+          // zero through the MFMA unit: keeps the accumulators in AGPRs
+          o[cb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf16x8{}, bf16x8{}, f32x16{}, 0, 0, 0);
+        }
+        rec[256 + rb] = M;
       }
-      asm volatile("" ::: "memory");  // keep the resolve loads after the copies
-      // 2. resolve tile kt+2 (page lookup) and kt+3 (index)
+      float M = mo_own, fa = 0.0f, fc = 1.0f;
+      if (flushed) {
+        const float mr = rec[261];
+        M = fmaxf(mr, mo_own);
+        fa = merge_factor(mr, M);
+        fc = merge_factor(mo_own, M);
+      }
+      rec[260] = (flushed ? rec[260] * fa : 0.0f) + l * fc;
+      rec[261] = M;
+      l = 0.0f;
+      flushed = true;
+    };
+
+    // One tile: the copy of tile kt+1 and the row resolution of kt+2/kt+3
+    // are issued, then tile kt is computed.  bf16 tiles alternate between
+    // the two buffers, starting with lds0.
+    for (int kt = kfirst; kt < kend; ++kt) {
+      const bool odd = ((kt - kfirst) & 1) != 0;
+      const bool has_next = __builtin_amdgcn_readfirstlane(kt + 1 < kend ? 1 : 0) != 0;
+      // 1. tile kt has landed (this thread's copies, then everyone's); every
+      //    wave is done with tile kt-1, its buffer and both P^T halves
+      if constexpr (FMT == 0) MLA_WAIT_VMCNT(kResolveLoads);
+      MLA_BARRIER_NO_FENCE();
+      const uint64_t vm = vm_cur;
+      // 2. sources of tile kt+1's copy; the copies themselves are issued
+      //    between the MFMAs of the first score chain
+      TileCopy<FMT> next;
+      next.prepare(a.kv, res_off, lds_addr(FMT == 1 ? lds1 : (odd ? lds0 : lds1)), wave, lane);
+      vm_cur = __ballot(res_off >= 0);
+
+      uint8_t* ks = (FMT == 0 && odd) ? lds1 : lds0;
+      uint32_t lanemask[2];  // sparse: visibility of keys 32*kb2 + 4*h + (0..31)
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) lanemask[kb2] = SPARSE ? (uint32_t)(vm >> (kb2 * 32 + 4 * h)) : 0u;
+      const int jlim = SPARSE ? 63 : min(63, tlim - kt * kPage);  // keys j <= jlim may count
+
+      // One slice of the softmax of half kb2 (raw scores in sc; scores in
+      // log2 units are scale * raw with scale > 0), emitted between MFMAs:
+      // slice 0 masks the half if any of its keys is not visible, slices
+      // 0..7 take the max of scores 2*st, 2*st+1; slice 8 updates the running
+      // max and publishes it; slices 9..16 turn scores 2*(st-9), +1 into
+      // probabilities; slice 17 stores the half's P^T.
+      auto softmax_slice = [&](int kb2, f32x16& sc, HalfSoftmax& hs, int st) __attribute__((always_inline)) {
+        if (st == 0) {
+          // dense: visible keys are a prefix of the tile (tail and causal
+          // limits folded into jlim); sparse: the per-key validity mask
+          // (bit 8*(v/4) + v%4 of the lane's mask word is key
+          // 32*kb2 + 8*(v/4) + 4*h + v%4)
+          const bool full = SPARSE ? (uint32_t)(vm >> (32 * kb2)) == 0xffffffffu
+                                   : __builtin_amdgcn_readfirstlane(__all(jlim >= 32 * kb2 + 31) ? 1 : 0) != 0;
+          if (!full) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int key = kb2 * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+              const bool ok = SPARSE ? ((lanemask[kb2] >> (8 * (v >> 2) + (v & 3))) & 1) != 0 : key <= jlim;
+              sc[v] = ok ? sc[v] : -INFINITY;
+            }
+          }
+        }
+        if (st < 8) {
+          const float x = fmaxf(sc[2 * st], sc[2 * st + 1]);
+          hs.tmax = st == 0 ? x : fmaxf(hs.tmax, x);
+        } else if (st == 8) {
+          // scale > 0 keeps the max; -inf (no visible key) stays -inf
+          const float mnew = fmaxf(m, wave_max_pair(hs.tmax) * scale);
+          // A row that has seen no visible key yet holds O = 0 and l = 0:
+          // it adopts the new max for free.
+          if (m == -INFINITY) m = mnew;
+          const bool grow = mnew > m + kRescaleThreshold;
+          hs.mo = m;
+          if (grow) m = mnew;
+          hs.muse = (m == -INFINITY) ? 0.0f : m;
+          hs.lh = 0.0f;
+          const bool any_grow = __ballot(grow) != 0;
+          if (h == 0) mold_s[kb2][rs] = hs.mo;
+          if (lane == 0) gflag[kb2][wave] = any_grow ? 1u : 0u;
+        } else if (st < 17) {
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int v = 2 * (st - 9) + e;
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[v], scale, -hs.muse));
+            hs.lh += p;
+            hs.pf[v >> 3][v & 7] = (__bf16)p;
+          }
+        } else if (st == 17) {
+          uint8_t* pb = kb2 == 0 ? pbuf : ks + kRopeOffset;
+#pragma unroll
+          for (int sp = 0; sp < 2; ++sp)
+            *reinterpret_cast<bf16x8*>(pb + 2048 * wave + p_off[sp]) = hs.pf[sp];
+        }
+      };
+
+      // After the barrier that publishes a half: if any wave saw a row grow,
+      // every wave parks its outputs; then this lane's row sum takes the
+      // half's part.
+      auto settle = [&](int kb2, const HalfSoftmax& hs) __attribute__((always_inline)) {
+        const u32x4 g = *reinterpret_cast<const u32x4*>(gflag[kb2]);
+        if ((g[0] | g[1] | g[2] | g[3]) != 0) flush(kb2, hs.mo);
+        l += hs.lh;
+      };
+
+      // O^T += V^T P^T for half kb2 over this wave's 4 column blocks and the
+      // 4 row blocks, hook(g) after MFMA group g (8 groups of 4).  Within
+      // each 16-lane group, transpose read: lane j points at 4 consecutive
+      // columns of one key row (key j/4 of the group's 4) and lane i
+      // receives column i of those 4 keys.  k slot (h, e) <-> key
+      // 32*kb2 + 16*sp + 8*(e/4) + 4*h + e%4.
+      auto pv_half = [&](int kb2, const uint8_t* pb, auto&& pre, auto&& hook) __attribute__((always_inline)) {
+        auto load_v = [&](int sp, int cb) {
+          const uint8_t* vb = ks + 8192 * (2 * wave + (cb >> 1)) + 4096 * kb2 + 2048 * sp;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_ptr<i16x4>(vb + v_off[cb & 1][0]));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_ptr<i16x4>(vb + v_off[cb & 1][1]));
+          return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        auto load_p = [&](int sp, int rb) {
+          return *reinterpret_cast<const bf16x8*>(pb + 2048 * rb + p_off[sp]);
+        };
+        bf16x8 pfr[4];
+        bf16x8 vf[2];
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) pfr[rb] = load_p(0, rb);
+        vf[0] = load_v(0, 0);
+        pre();  // runs while the first operands are in flight
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+          const int cb = g & 3;
+          // read ahead: the next group's V^T block
+          if (g + 1 < 8) vf[(g + 1) & 1] = load_v((g + 1) >> 2, (g + 1) & 3);
+#pragma unroll
+          for (int rb = 0; rb < 4; ++rb)
+            o[cb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[g & 1], pfr[rb], o[cb][rb], 0, 0, 0);
+          // the second key step's P^T, once the first step's last MFMAs are issued
+          if (g == 3) {
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) pfr[rb] = load_p(1, rb);
+          }
+          hook(g);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+
+      HalfSoftmax hs0, hs1;
+      f32x16 sacc0, sacc1;
+      // 3. scores of half 0; scores of half 1 with the softmax of half 0
+      score_chain(sacc0, ks, k_off, qf, [&](auto st_c) __attribute__((always_inline)) {
+        if (has_next) next.template issue_step<0, decltype(st_c)::value>(lane);
+      });
+      score_chain(sacc1, ks + 32 * 128, k_off, qf, [&](auto st_c) __attribute__((always_inline)) {
+        if (has_next) next.template issue_step<1, decltype(st_c)::value>(lane);
+        constexpr int st = decltype(st_c)::value;  // slice i at step 2i+1
+        if constexpr (st % 2 == 1) softmax_slice(0, sacc0, hs0, st / 2);
+      });
+      // resolve kt+2 (page lookup) and kt+3 after the last copy: the wait at
+      // the top of the next tile counts these loads as the only ones newer
+      // than the copies
+      asm volatile("" ::: "memory");
       pg2 = page_of(res_t);
       t3 = position(kt + 3);
       asm volatile("" ::: "memory");
-      // 3. bf16: wait for this thread's copies of tile kt (issued one
-      //    iteration earlier; the newer copies and resolve loads may stay in
-      //    flight), then for every thread's
-      if constexpr (FMT == 0) {
-        if (has_next) MLA_WAIT_VMCNT(kTileLoads / 4 + kResolveLoads);
-        else MLA_WAIT_VMCNT(kResolveLoads);
-        MLA_BARRIER_NO_FENCE();
-      }
-      const uint8_t* ks = (FMT == 0 && cur) ? lds1 : lds0;
-      const uint64_t vm = (uint64_t)vmask[cur][0] | ((uint64_t)vmask[cur][1] << 32);
-      const int jlim = SPARSE ? 63 : min(63, tlim - kt * kPage);  // keys j <= jlim may count
+      // 4. half 0's P^T and maxima visible; every wave is past the scores,
+      //    so the RoPE chunk group is free for half 1's P^T
+      MLA_BARRIER_NO_FENCE();
+      pv_half(0, pbuf, [&] { settle(0, hs0); }, [&](int g) {
+        constexpr int kEdges[9] = {0, 2, 5, 7, 9, 11, 14, 16, 18};
+#pragma unroll
+        for (int st = 0; st < 18; ++st)
+          if (st >= kEdges[g] && st < kEdges[g + 1]) softmax_slice(1, sacc1, hs1, st);
+      });
+      MLA_BARRIER_NO_FENCE();  // half 1's P^T and maxima visible
+      pv_half(1, ks + kRopeOffset, [&] { settle(1, hs1); }, [](int) {});
 
-      // The tile is consumed as two 32-key halves to bound register use.
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
-        // ---- S^T = K Q^T for keys 32*kb2 .. 32*kb2+31.  K operands are read
-        // kPrefetch steps ahead of their MFMA so the LDS latency hides behind
-        // the MFMA chain.
-        f32x16 sacc;
-        {
-          const uint8_t* kb = ks + kb2 * 32 * 128;
-          auto kload = [&](int st) {
-            return *reinterpret_cast<const bf16x8*>(kb + k_off[st & 3] + 8192 * (st >> 2));
-          };
-          constexpr int kPrefetch = 3;
-          bf16x8 kf[kPrefetch];
-#pragma unroll
-          for (int st = 0; st < kPrefetch; ++st) kf[st] = kload(st);
-#pragma unroll
-          for (int st = 0; st < kQSteps; ++st) {
-            const bf16x8 cur_k = kf[st % kPrefetch];
-            if (st + kPrefetch < kQSteps) kf[st % kPrefetch] = kload(st + kPrefetch);
-            if (st == 0)
-              mfma_s_first(sacc, cur_k, qf[st]);
-            else
-              mfma_s_acc(sacc, cur_k, qf[st]);
-            __builtin_amdgcn_sched_barrier(0);
-          }
-          mfma_s_drain(sacc);
-        }
-        // ---- mask, scale, max over this half
-        float tmax = -INFINITY;
-        const uint32_t lanemask = SPARSE ? (uint32_t)(vm >> (kb2 * 32 + 4 * h)) : 0u;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = kb2 * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-          // dense: visible keys are a prefix of the tile (tail and causal
-          // limits folded into jlim); sparse: the per-key validity mask
-          const bool ok = SPARSE ? ((lanemask >> (8 * (v >> 2) + (v & 3))) & 1) != 0 : key <= jlim;
-          const float x = ok ? sacc[v] * s.scale_log2 : -INFINITY;
-          sacc[v] = x;
-          tmax = fmaxf(tmax, x);
-        }
-        tmax = wave_max_pair(tmax);
-        const float mnew = fmaxf(m, tmax);
-        // A row that has seen no visible key yet holds O = 0 and l = 0: it
-        // adopts the new max for free.
-        if (m == -INFINITY) m = mnew;
-        const bool grow = mnew > m + kRescaleThreshold;
-        if (__any(grow)) {
-          // Rare: park this wave's rows in the flush area and restart them
-          // from zero (O never goes through a loop-carried rescale).
-          flush_rows(flush, flushed, o, m, l, oslot);
-          flushed = true;
-          if (grow) m = mnew;
-        }
-        const float muse = (m == -INFINITY) ? 0.0f : m;
-        // ---- probabilities -> bf16 P^T operands (key-slot order = S^T order)
-        bf16x8 pf[2];
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float p = __builtin_amdgcn_exp2f(sacc[v] - muse);
-          l += p;
-          pf[v >> 3][v & 7] = (__bf16)p;
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        // ---- O^T += V^T P^T over 16 column blocks of 32.  Within each
-        // 16-lane group, transpose read: lane j points at 4 consecutive
-        // columns of one key row (key j/4 of the group's 4) and lane i
-        // receives column i of those 4 keys.  k slot (h, e) <-> key
-        // 32*kb2 + 16*sp + 8*(e/4) + 4*h + e%4.
-        auto load_v = [&](int cb, i16x8* vv) {
-#pragma unroll
-          for (int sp = 0; sp < 2; ++sp) {
-            const uint8_t* vb = ks + 8192 * (cb >> 1) + 4096 * kb2 + 2048 * sp;
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_ptr<i16x4>(vb + v_off[cb & 1][0]));
-            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_ptr<i16x4>(vb + v_off[cb & 1][1]));
-            vv[sp] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          }
-        };
-        i16x8 vbuf[2][2];
-        load_v(0, vbuf[0]);
-#pragma unroll
-        for (int cb = 0; cb < 16; ++cb) {
-          if (cb + 1 < 16) load_v(cb + 1, vbuf[(cb + 1) & 1]);
-#pragma unroll
-          for (int sp = 0; sp < 2; ++sp)
-            o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vbuf[cb & 1][sp]),
-                                                            pf[sp], o[cb], 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-      // 4. finish resolving tile kt+2
+      // 5. finish resolving tile kt+2
       res_off = offset_of(res_t, pg2);
       res_t = t3;
-      if constexpr (FMT == 0) {
-        MLA_BARRIER_NO_FENCE();  // tile kt consumed: its buffer may be refilled
-      } else {
+      if constexpr (FMT == 1) {
         if (has_next) {
           MLA_WAIT_VMCNT(0);
           __syncthreads();  // staged rows complete, bf16 tile consumed
           dequant_stage(lds1, lds0);
         }
       }
-    };
-    for (int kt = kfirst; kt < kend; kt += 2) {
-      tile_step(std::integral_constant<int, 0>{}, kt);
-      if (kt + 1 < kend) tile_step(std::integral_constant<int, 1>{}, kt + 1);
     }
 
-    // ---- epilogue: fold in a flush record (if any), normalise, store.
+    // ---- epilogue.  The score-row owner folds in its flush record and
+    // publishes the row's output factors; every wave then normalises and
+    // stores its column blocks.
     float fa = 0.0f, fc = 1.0f, mfin = m, lfin = l;
     if (flushed) {
-      const float mf = flush[257];
+      const float mf = rec[261];
       mfin = fmaxf(mf, m);
-      fa = __builtin_amdgcn_exp2f(mf - mfin);
-      fc = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - mfin);
-      lfin = flush[256] * fa + l * fc;
+      fa = merge_factor(mf, mfin);
+      fc = merge_factor(m, mfin);
+      lfin = rec[260] * fa + l * fc;
     }
-    const float ltot = lfin + __shfl_xor(lfin, 32);
+    const float ltot = wave_sum_pair(lfin);
     const float lse2 = ltot > 0.0f ? mfin + log2f(ltot) : -INFINITY;
     const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
-    const float ca = fa * inv, cc = fc * inv;
-    if (row_ok) {
-      const int64_t row = (int64_t)u * s.rows + r;
-      const bool direct = nsplit == 1;
-      const int64_t wrow = direct ? 0 : ((int64_t)a.num_splits[u] + seg) * s.rows + r;
-      uint16_t* orow16 = a.out + row * kDv + 4 * h;
-      float* orow32 = a.ws_o + wrow * kDv + 4 * h;
+    // half 0's P^T buffer is free: every wave is past the last tile's final barrier
+    f32x2* epi = reinterpret_cast<f32x2*>(pbuf);
+    if (h == 0) epi[rs] = f32x2{fc * inv, fa * inv};
+    MLA_BARRIER_NO_FENCE();
+    const bool direct = nsplit == 1;
 #pragma unroll
-      for (int cb = 0; cb < 16; ++cb) {
+    for (int rb = 0; rb < 4; ++rb) {
+      const int ro = grp * kRowsPerGroup + 32 * rb + n;  // output row in unit
+      if (ro < s.rows) {
+        const f32x2 f = epi[32 * rb + n];
+        const int64_t row = (int64_t)u * s.rows + ro;
+        const int64_t wrow = direct ? 0 : ((int64_t)a.num_splits[u] + seg) * s.rows + ro;
+        uint16_t* orow16 = a.out + row * kDv + 128 * wave + 4 * h;
+        float* orow32 = a.ws_o + wrow * kDv + 128 * wave + 4 * h;
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int col = 32 * cb + 8 * q4;  // + 4*h folded into the row pointers
-          f32x4 v = acc_quad(o[cb], q4, oslot) * cc;
-          if (flushed) {
-            const f32x4 f = *reinterpret_cast<const f32x4*>(flush + cb * 16 + 4 * q4);
-            v += f * ca;
+        for (int cb = 0; cb < 4; ++cb) {
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int col = 32 * cb + 8 * q4;  // + 128*wave + 4*h folded into the row pointers
+            f32x4 v = acc_quad(o[cb][rb], q4, oslot) * f[0];
+            if (flushed) {
+              const f32x4 fr = *reinterpret_cast<const f32x4*>(rec + (4 * cb + rb) * 16 + 4 * q4);
+              v += fr * f[1];
+            }
+            if (direct) {
+              const uint32_t w0 = (uint32_t)bf16_bits(v[0]) | ((uint32_t)bf16_bits(v[1]) << 16);
+              const uint32_t w1 = (uint32_t)bf16_bits(v[2]) | ((uint32_t)bf16_bits(v[3]) << 16);
+              *reinterpret_cast<uint2*>(orow16 + col) = make_uint2(w0, w1);
+            } else {
+              *reinterpret_cast<f32x4*>(orow32 + col) = v;
+            }
           }
-          if (direct) {
-            const uint32_t w0 = (uint32_t)bf16_bits(v[0]) | ((uint32_t)bf16_bits(v[1]) << 16);
-            const uint32_t w1 = (uint32_t)bf16_bits(v[2]) | ((uint32_t)bf16_bits(v[3]) << 16);
-            *reinterpret_cast<uint2*>(orow16 + col) = make_uint2(w0, w1);
-          } else {
-            *reinterpret_cast<f32x4*>(orow32 + col) = v;
-          }
+          __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
       }
-      if (h == 0) {
-        if (direct)
-          a.lse[row] = s.natural ? lse2 * 0.69314718055994531f : lse2;
-        else
-          a.ws_lse[wrow] = lse2;
-      }
+    }
+    if (row_ok && h == 0) {
+      const int64_t row = (int64_t)u * s.rows + r;
+      if (direct)
+        a.lse[row] = s.natural ? lse2 * 0.69314718055994531f : lse2;
+      else
+        a.ws_lse[((int64_t)a.num_splits[u] + seg) * s.rows + r] = lse2;
     }
   }
 }

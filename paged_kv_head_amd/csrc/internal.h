@@ -35,15 +35,16 @@ struct DecodeArgs {
   int32_t num_parts;
   float* ws_lse;  // [slots * R]
   float* ws_o;    // [slots * R * 512]
-  float* ws_flush;  // [num_parts * groups * 256 threads * 258]
+  float* ws_flush;  // [num_parts * groups * 256 threads * kFlushFloats]
   uint16_t* out;
   float* lse;
 };
 
 // Workspace layout: split lse block, split output block (both for
 // num_parts + U slots of R rows), then one flush record per decode thread
-// (num_parts * groups workgroups of 256 threads, 258 floats each).
-constexpr int kFlushFloats = 258;
+// (num_parts * groups workgroups of 256 threads, kFlushFloats floats each:
+// 256 output values, 4 row maxima, a row sum and its maximum, padding).
+constexpr int kFlushFloats = 264;
 inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 inline size_t ws_slots(int32_t num_parts, int32_t units) { return (size_t)num_parts + (size_t)units; }
 inline size_t ws_lse_bytes(size_t slots, int32_t rows) {

@@ -25,8 +25,20 @@ __device__ inline int blocks_of(const Shape& s, const int32_t* seqlens, int u) {
   return (L + kPage - 1) / kPage;
 }
 
+// Inclusive prefix sum across the 64 lanes of a wave.
+__device__ inline int wave_inclusive_scan(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
 // In-place exclusive scan of v[0..n) in LDS by the whole block; returns the
-// total.  Each thread scans a contiguous chunk, then the chunk sums.
+// total.  Each thread scans a contiguous chunk; chunk sums are scanned with
+// wave shuffles (16 waves), then the 16 wave totals by one wave.
 __device__ int block_exclusive_scan(int* v, int n, int* partial) {
   const int tid = threadIdx.x;
   const int per = (n + kThreads - 1) / kThreads;
@@ -34,26 +46,26 @@ __device__ int block_exclusive_scan(int* v, int n, int* partial) {
   const int hi = min(n, lo + per);
   int sum = 0;
   for (int i = lo; i < hi; ++i) sum += v[i];
-  partial[tid] = sum;
+  const int incl = wave_inclusive_scan(sum);
+  const int wave = tid >> 6;
+  if ((tid & 63) == 63) partial[wave] = incl;
   __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int i = 0; i < kThreads; ++i) {
-      int x = partial[i];
-      partial[i] = run;
-      run += x;
-    }
-    partial[kThreads] = run;
+  if (tid < 64) {
+    const int t = tid < kThreads / 64 ? partial[tid] : 0;
+    const int ti = wave_inclusive_scan(t);
+    if (tid < kThreads / 64) partial[kThreads / 64 + tid] = ti - t;  // exclusive wave offsets
+    if (tid == kThreads / 64 - 1) partial[2 * (kThreads / 64)] = ti;  // total
   }
   __syncthreads();
-  int run = partial[tid];
+  int run = partial[kThreads / 64 + wave] + incl - sum;
   for (int i = lo; i < hi; ++i) {
-    int x = v[i];
+    const int x = v[i];
     v[i] = run;
     run += x;
   }
+  const int total = partial[2 * (kThreads / 64)];
   __syncthreads();
-  return partial[kThreads];
+  return total;
 }
 
 // First block whose cost position is >= x: (unit, block), or (U, 0).
@@ -78,7 +90,7 @@ metadata_kernel(Shape s, const int32_t* __restrict__ seqlens, int32_t num_parts,
                 int32_t* __restrict__ sched, int32_t* __restrict__ num_splits) {
   __shared__ int nb[kMaxUnits];
   __shared__ int C[kMaxUnits + 1];
-  __shared__ int partial[kThreads + 1];
+  __shared__ int partial[2 * (kThreads / 64) + 1];
   const int U = s.units;
   const int pen = kSplitPenalty;
   for (int u = threadIdx.x; u < U; u += kThreads) {
