@@ -41,6 +41,17 @@ def test_natural_base(n):
     assert_close(out, lse / math.log(2), ref_out, ref_lse / math.log(2), what="natural")
 
 
+@pytest.mark.parametrize("n,scale", [(1, -1.0 / 24), (1, 0.0), (3, -0.3), (3, 0.0), (5, -1.0 / 24), (4, 0.0)])
+def test_scale_sign_and_zero(n, scale):
+    """Any finite softmax_scale: negative scales and zero take their own
+    kernel path (a sign flip or zeroing of Q); the oracle uses the scale as
+    given (zero: uniform weights, lse = log2 of the visible count)."""
+    w = synth.config_workload(n, batch=2)
+    out, lse = run(w, softmax_scale=scale)
+    ref_out, ref_lse = oracle.mla_decode(w, softmax_scale=scale)
+    assert_close(out, lse, ref_out, ref_lse, what=f"config {n} scale {scale}")
+
+
 @pytest.mark.parametrize("parts", [1, 2, 3, 7, 64, 300, 1000])
 def test_forced_split_counts(parts):
     w = synth.make_workload("t", batch=3, h_q=128, s_q=2, seqlens=[700, 129, 1], seed=31, is_causal=1)
