@@ -201,13 +201,13 @@ struct TileCopy {
       issue_all<T + 1>(lane);
     }
   }
-  // Copies spread over two score chains (step ST of chain CHAIN): bf16
-  // every 4th step, FP8 every 6th.
-  template <int CHAIN, int ST>
+  // Copies spread over a score chain: the i-th after the MFMA of step
+  // 2i+1.  FP8 issues copies 10 and 11 (the RoPE group, which needs the
+  // zero-row source) first, so that source is not held across the chain.
+  template <int ST>
   __device__ inline void issue_step(int lane) const {
-    constexpr int kEvery = FMT == 0 ? 4 : 6;
-    if constexpr (ST % kEvery == 1 && ST / kEvery < kCopies / 2)
-      issue<CHAIN * (kCopies / 2) + ST / kEvery>(lane);
+    if constexpr (ST % 2 == 1 && ST / 2 < kCopies)
+      issue<FMT == 1 ? (ST / 2 + 10) % kCopies : ST / 2>(lane);
   }
 };
 
@@ -335,12 +335,15 @@ __device__ inline float merge_factor(float x, float M) {
 
 // Per-half softmax state of a lane (its row, its 16 keys of the half).
 struct HalfSoftmax {
-  float tmax;   // max of the masked, scaled scores
+  float tmax;   // max of the masked raw scores, then of the scaled row
+  float mnew;   // candidate running max
+  bool grow;    // the row's max grew past the refresh threshold
   float mo;     // running max before this half's update
-  float muse;   // reference the probabilities are taken against
+  float nmuse;  // minus the reference the probabilities are taken against
   float lh;     // this half's part of the row sum
   bf16x8 pf[2]; // bf16 probabilities, MFMA operand order
 };
+constexpr int kSoftmaxSteps = 28;
 
 template <int FMT, bool SPARSE>
 __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
@@ -548,7 +551,8 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
       MLA_BARRIER_NO_FENCE();
       const uint64_t vm = vm_cur;
       // 2. sources of tile kt+1's copy; the copies themselves are issued
-      //    between the MFMAs of the first score chain
+      //    between the MFMAs of the first score chain (res_off is -1 for
+      //    every key past the unit's last tile)
       TileCopy<FMT> next;
       next.prepare(a.kv, res_off, lds_addr(FMT == 1 ? lds1 : (odd ? lds0 : lds1)), wave, lane);
       vm_cur = __ballot(res_off >= 0);
@@ -559,14 +563,19 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
       for (int kb2 = 0; kb2 < 2; ++kb2) lanemask[kb2] = SPARSE ? (uint32_t)(vm >> (kb2 * 32 + 4 * h)) : 0u;
       const int jlim = SPARSE ? 63 : min(63, tlim - kt * kPage);  // keys j <= jlim may count
 
-      // One slice of the softmax of half kb2 (raw scores in sc; scores in
-      // log2 units are scale * raw with scale > 0), emitted between MFMAs:
-      // slice 0 masks the half if any of its keys is not visible, slices
-      // 0..7 take the max of scores 2*st, 2*st+1; slice 8 updates the running
-      // max and publishes it; slices 9..16 turn scores 2*(st-9), +1 into
-      // probabilities; slice 17 stores the half's P^T.
-      auto softmax_slice = [&](int kb2, f32x16& sc, HalfSoftmax& hs, int st) __attribute__((always_inline)) {
-        if (st == 0) {
+      // The softmax of half kb2 (raw scores in sc; scores in log2 units are
+      // scale * raw with scale > 0), cut into kSoftmaxSteps small steps of a
+      // few VALU instructions each.  One step goes between two MFMAs: an
+      // MFMA cannot issue while the matrix core is busy, and only the
+      // independent instructions that precede it in program order run in
+      // the shadow of the previous one.
+      //   0..3   mask the half if any of its keys is not visible (step 0),
+      //          max of the raw scores
+      //   4..9   row max across the lane pair, running max update, publish
+      //   10..25 probability of score u-10, row sum, bf16 operand
+      //   26, 27 store the half's P^T
+      auto softmax_step = [&](int kb2, f32x16& sc, HalfSoftmax& hs, int u) __attribute__((always_inline)) {
+        if (u == 0) {
           // dense: visible keys are a prefix of the tile (tail and causal
           // limits folded into jlim); sparse: the per-key validity mask
           // (bit 8*(v/4) + v%4 of the lane's mask word is key
@@ -581,37 +590,37 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
               sc[v] = ok ? sc[v] : -INFINITY;
             }
           }
-        }
-        if (st < 8) {
-          const float x = fmaxf(sc[2 * st], sc[2 * st + 1]);
-          hs.tmax = st == 0 ? x : fmaxf(hs.tmax, x);
-        } else if (st == 8) {
-          // scale > 0 keeps the max; -inf (no visible key) stays -inf
-          const float mnew = fmaxf(m, wave_max_pair(hs.tmax) * scale);
+          hs.tmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+        } else if (u < 4) {
+          hs.tmax = fmaxf(fmaxf(hs.tmax, sc[4 * u]), fmaxf(sc[4 * u + 1], fmaxf(sc[4 * u + 2], sc[4 * u + 3])));
+        } else if (u == 4) {
+          hs.tmax = wave_max_pair(hs.tmax) * scale;  // scale > 0 keeps the max; -inf stays -inf
+        } else if (u == 5) {
+          hs.mnew = fmaxf(m, hs.tmax);
           // A row that has seen no visible key yet holds O = 0 and l = 0:
           // it adopts the new max for free.
-          if (m == -INFINITY) m = mnew;
-          const bool grow = mnew > m + kRescaleThreshold;
+          if (m == -INFINITY) m = hs.mnew;
+        } else if (u == 6) {
+          hs.grow = hs.mnew > m + kRescaleThreshold;
           hs.mo = m;
-          if (grow) m = mnew;
-          hs.muse = (m == -INFINITY) ? 0.0f : m;
+          if (hs.grow) m = hs.mnew;
+        } else if (u == 7) {
+          hs.nmuse = (m == -INFINITY) ? 0.0f : -m;
           hs.lh = 0.0f;
-          const bool any_grow = __ballot(grow) != 0;
+        } else if (u == 8) {
           if (h == 0) mold_s[kb2][rs] = hs.mo;
+        } else if (u == 9) {
+          const bool any_grow = __ballot(hs.grow) != 0;
           if (lane == 0) gflag[kb2][wave] = any_grow ? 1u : 0u;
-        } else if (st < 17) {
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int v = 2 * (st - 9) + e;
-            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[v], scale, -hs.muse));
-            hs.lh += p;
-            hs.pf[v >> 3][v & 7] = (__bf16)p;
-          }
-        } else if (st == 17) {
+        } else if (u < 26) {
+          const int v = u - 10;
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[v], scale, hs.nmuse));
+          hs.lh += p;
+          hs.pf[v >> 3][v & 7] = (__bf16)p;
+        } else if (u < 28) {
+          const int sp = u - 26;
           uint8_t* pb = kb2 == 0 ? pbuf : ks + kRopeOffset;
-#pragma unroll
-          for (int sp = 0; sp < 2; ++sp)
-            *reinterpret_cast<bf16x8*>(pb + 2048 * wave + p_off[sp]) = hs.pf[sp];
+          *reinterpret_cast<bf16x8*>(pb + 2048 * wave + p_off[sp]) = hs.pf[sp];
         }
       };
 
@@ -625,7 +634,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
       };
 
       // O^T += V^T P^T for half kb2 over this wave's 4 column blocks and the
-      // 4 row blocks, hook(g) after MFMA group g (8 groups of 4).  Within
+      // 4 row blocks, hook(j) after MFMA j (32 of them).  Within
       // each 16-lane group, transpose read: lane j points at 4 consecutive
       // columns of one key row (key j/4 of the group's 4) and lane i
       // receives column i of those 4 keys.  k slot (h, e) <-> key
@@ -652,28 +661,28 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
           // read ahead: the next group's V^T block
           if (g + 1 < 8) vf[(g + 1) & 1] = load_v((g + 1) >> 2, (g + 1) & 3);
 #pragma unroll
-          for (int rb = 0; rb < 4; ++rb)
+          for (int rb = 0; rb < 4; ++rb) {
             o[cb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[g & 1], pfr[rb], o[cb][rb], 0, 0, 0);
+            hook(4 * g + rb);
+            __builtin_amdgcn_sched_barrier(0);
+          }
           // the second key step's P^T, once the first step's last MFMAs are issued
           if (g == 3) {
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb) pfr[rb] = load_p(1, rb);
           }
-          hook(g);
-          __builtin_amdgcn_sched_barrier(0);
         }
       };
 
       HalfSoftmax hs0, hs1;
       f32x16 sacc0, sacc1;
       // 3. scores of half 0; scores of half 1 with the softmax of half 0
+      // Issued unconditionally: after a unit's last tile every key of "tile
+      // kt+1" resolves to the zero row, so the copies fill the free buffer
+      // with zeros, which nothing reads; the next unit starts with a barrier
+      // that waits for them.  No branch keeps the chain's registers simple.
       score_chain(sacc0, ks, k_off, qf, [&](auto st_c) __attribute__((always_inline)) {
-        if (has_next) next.template issue_step<0, decltype(st_c)::value>(lane);
-      });
-      score_chain(sacc1, ks + 32 * 128, k_off, qf, [&](auto st_c) __attribute__((always_inline)) {
-        if (has_next) next.template issue_step<1, decltype(st_c)::value>(lane);
-        constexpr int st = decltype(st_c)::value;  // slice i at step 2i+1
-        if constexpr (st % 2 == 1) softmax_slice(0, sacc0, hs0, st / 2);
+        next.template issue_step<decltype(st_c)::value>(lane);
       });
       // resolve kt+2 (page lookup) and kt+3 after the last copy: the wait at
       // the top of the next tile counts these loads as the only ones newer
@@ -682,14 +691,16 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
       pg2 = page_of(res_t);
       t3 = position(kt + 3);
       asm volatile("" ::: "memory");
+      score_chain(sacc1, ks + 32 * 128, k_off, qf, [&](auto st_c) __attribute__((always_inline)) {
+        constexpr int st = decltype(st_c)::value;
+        if constexpr (st < kSoftmaxSteps) softmax_step(0, sacc0, hs0, st);
+      });
+
       // 4. half 0's P^T and maxima visible; every wave is past the scores,
       //    so the RoPE chunk group is free for half 1's P^T
       MLA_BARRIER_NO_FENCE();
-      pv_half(0, pbuf, [&] { settle(0, hs0); }, [&](int g) {
-        constexpr int kEdges[9] = {0, 2, 5, 7, 9, 11, 14, 16, 18};
-#pragma unroll
-        for (int st = 0; st < 18; ++st)
-          if (st >= kEdges[g] && st < kEdges[g + 1]) softmax_slice(1, sacc1, hs1, st);
+      pv_half(0, pbuf, [&] { settle(0, hs0); }, [&](int j) {
+        if (j < kSoftmaxSteps) softmax_step(1, sacc1, hs1, j);
       });
       MLA_BARRIER_NO_FENCE();  // half 1's P^T and maxima visible
       pv_half(1, ks + kRopeOffset, [&] { settle(1, hs1); }, [](int) {});
