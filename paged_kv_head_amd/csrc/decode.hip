@@ -201,15 +201,45 @@ struct TileCopy {
       issue_all<T + 1>(lane);
     }
   }
-  // Copies spread over a score chain: the i-th after the MFMA of step
-  // 2i+1.  FP8 issues copies 10 and 11 (the RoPE group, which needs the
-  // zero-row source) first, so that source is not held across the chain.
-  template <int ST>
-  __device__ inline void issue_step(int lane) const {
-    if constexpr (ST % 2 == 1 && ST / 2 < kCopies)
-      issue<FMT == 1 ? (ST / 2 + 10) % kCopies : ST / 2>(lane);
+  // Copies are spread thinly over most of a tile: a CU holds only so many
+  // copies in flight at HBM latency, and a burst stalls instruction issue
+  // until the first ones return.  bf16: 7 copies in each score chain (after
+  // the MFMAs of steps 2, 7, .., 32) and 4 early in the first P*V half
+  // (after MFMAs 2, 7, 12, 17); FP8 (whose rows are needed by the
+  // dequantisation at the end of the tile): 6 in each score chain.  FP8
+  // issues copies 10 and 11 (the RoPE group, which needs the zero-row
+  // source) first, so that source is not held long.
+  static constexpr int slot(int phase, int step) {
+    if (FMT == 0) {
+      if (step % 5 != 2) return -1;
+      if (phase < 2) return 7 * phase + step / 5;
+      return step / 5 < 4 ? 14 + step / 5 : -1;
+    }
+    if (phase == 2 || step % 6 != 2) return -1;
+    return (6 * phase + step / 6 + 10) % kCopies;
+  }
+  // every copy is issued exactly once (phases: 36, 36 and 32 steps)
+  static constexpr bool slots_cover_copies() {
+    int seen[kCopies] = {};
+    for (int phase = 0; phase < 3; ++phase)
+      for (int step = 0; step < (phase < 2 ? 36 : 32); ++step) {
+        const int t = slot(phase, step);
+        if (t >= kCopies) return false;
+        if (t >= 0) ++seen[t];
+      }
+    for (int t = 0; t < kCopies; ++t)
+      if (seen[t] != 1) return false;
+    return true;
+  }
+  template <int PHASE, int STEP>
+  __device__ inline void issue_at(int lane) const {
+    constexpr int t = slot(PHASE, STEP);
+    if constexpr (t >= 0) issue<t>(lane);
   }
 };
+
+static_assert(TileCopy<0>::slots_cover_copies() && TileCopy<1>::slots_cover_copies(),
+              "copy schedule must issue every copy of a tile once");
 
 // f(integral_constant<I>) for I = B .. E-1, unrolled at compile time.
 template <int B, int E, class F>
@@ -655,23 +685,23 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
         for (int rb = 0; rb < 4; ++rb) pfr[rb] = load_p(0, rb);
         vf[0] = load_v(0, 0);
         pre();  // runs while the first operands are in flight
-#pragma unroll
-        for (int g = 0; g < 8; ++g) {
-          const int cb = g & 3;
+        static_for<0, 8>([&](auto g_c) __attribute__((always_inline)) {
+          constexpr int g = decltype(g_c)::value;
+          constexpr int cb = g & 3;
           // read ahead: the next group's V^T block
-          if (g + 1 < 8) vf[(g + 1) & 1] = load_v((g + 1) >> 2, (g + 1) & 3);
-#pragma unroll
-          for (int rb = 0; rb < 4; ++rb) {
+          if constexpr (g + 1 < 8) vf[(g + 1) & 1] = load_v((g + 1) >> 2, (g + 1) & 3);
+          static_for<0, 4>([&](auto rb_c) __attribute__((always_inline)) {
+            constexpr int rb = decltype(rb_c)::value;
             o[cb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[g & 1], pfr[rb], o[cb][rb], 0, 0, 0);
-            hook(4 * g + rb);
+            hook(std::integral_constant<int, 4 * g + rb>{});
             __builtin_amdgcn_sched_barrier(0);
-          }
+          });
           // the second key step's P^T, once the first step's last MFMAs are issued
-          if (g == 3) {
+          if constexpr (g == 3) {
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb) pfr[rb] = load_p(1, rb);
           }
-        }
+        });
       };
 
       HalfSoftmax hs0, hs1;
@@ -682,7 +712,21 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
       // with zeros, which nothing reads; the next unit starts with a barrier
       // that waits for them.  No branch keeps the chain's registers simple.
       score_chain(sacc0, ks, k_off, qf, [&](auto st_c) __attribute__((always_inline)) {
-        next.template issue_step<decltype(st_c)::value>(lane);
+        next.template issue_at<0, decltype(st_c)::value>(lane);
+      });
+      score_chain(sacc1, ks + 32 * 128, k_off, qf, [&](auto st_c) __attribute__((always_inline)) {
+        constexpr int st = decltype(st_c)::value;
+        next.template issue_at<1, st>(lane);
+        if constexpr (st < kSoftmaxSteps) softmax_step(0, sacc0, hs0, st);
+      });
+
+      // 4. half 0's P^T and maxima visible; every wave is past the scores,
+      //    so the RoPE chunk group is free for half 1's P^T
+      MLA_BARRIER_NO_FENCE();
+      pv_half(0, pbuf, [&] { settle(0, hs0); }, [&](auto j_c) __attribute__((always_inline)) {
+        constexpr int j = decltype(j_c)::value;
+        next.template issue_at<2, j>(lane);
+        if constexpr (j < kSoftmaxSteps) softmax_step(1, sacc1, hs1, j);
       });
       // resolve kt+2 (page lookup) and kt+3 after the last copy: the wait at
       // the top of the next tile counts these loads as the only ones newer
@@ -691,19 +735,8 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
       pg2 = page_of(res_t);
       t3 = position(kt + 3);
       asm volatile("" ::: "memory");
-      score_chain(sacc1, ks + 32 * 128, k_off, qf, [&](auto st_c) __attribute__((always_inline)) {
-        constexpr int st = decltype(st_c)::value;
-        if constexpr (st < kSoftmaxSteps) softmax_step(0, sacc0, hs0, st);
-      });
-
-      // 4. half 0's P^T and maxima visible; every wave is past the scores,
-      //    so the RoPE chunk group is free for half 1's P^T
-      MLA_BARRIER_NO_FENCE();
-      pv_half(0, pbuf, [&] { settle(0, hs0); }, [&](int j) {
-        if (j < kSoftmaxSteps) softmax_step(1, sacc1, hs1, j);
-      });
       MLA_BARRIER_NO_FENCE();  // half 1's P^T and maxima visible
-      pv_half(1, ks + kRopeOffset, [&] { settle(1, hs1); }, [](int) {});
+      pv_half(1, ks + kRopeOffset, [&] { settle(1, hs1); }, [](auto) {});
 
       // 5. finish resolving tile kt+2
       res_off = offset_of(res_t, pg2);
