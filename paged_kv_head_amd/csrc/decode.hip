@@ -261,10 +261,15 @@ __device__ inline void dequant_stage(const uint8_t* stage, uint8_t* ks) {
     return stage + ((c >> 3) * 512 + key * 8 + (c & 7)) * 16;
   };
   const f32x4 scales = *reinterpret_cast<const f32x4*>(stage_chunk(32));
+  // all eight code chunks are read before any is converted, so the reads
+  // overlap instead of each waiting out the LDS latency
+  u32x4 raw[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) raw[j] = *reinterpret_cast<const u32x4*>(stage_chunk(sub + 4 * j));
 #pragma unroll
   for (int j = 0; j < 8; ++j) {  // code chunk cc = sub + 4*j: dims 16*cc .. 16*cc+15
     const int cc = sub + 4 * j;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(stage_chunk(cc));
+    const u32x4 v = raw[j];
     const float sc = scales[j >> 1];
     u32x4 lo, hi;
 #pragma unroll
@@ -278,7 +283,6 @@ __device__ inline void dequant_stage(const uint8_t* stage, uint8_t* ks) {
     }
     *reinterpret_cast<u32x4*>(ks + tile_chunk(key, 2 * cc)) = lo;
     *reinterpret_cast<u32x4*>(ks + tile_chunk(key, 2 * cc + 1)) = hi;
-    __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {  // RoPE: bf16 chunks 64..71 <- raw chunks 33..40
@@ -413,7 +417,13 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
   const bool row_ok = r < s.rows;
   // per-lane flush record: 256 output values (block (cb, rb) at 16*(4cb+rb)),
   // the 4 output rows' maxima, the score row's sum and maximum
-  float* rec = a.ws_flush + ((int64_t)(part * s.groups + grp) * kThreads + threadIdx.x) * kFlushFloats;
+  // (recomputed where used, so no register holds it through the tile loop)
+  const int64_t rec_wg = (int64_t)(part * s.groups + grp) * kThreads;
+  auto flush_rec = [&]() -> float* {
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    return a.ws_flush + (rec_wg + tid) * kFlushFloats;
+  };
 
   // Lane-constant parts of the LDS operand addresses (tile layout above).
   // K operand, step st: row 32*kb2 + n, chunk 2*st + h.
@@ -533,6 +543,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
     // Every party to a row applies the same sequence of maxima, so the
     // copies of a row's record maximum stay identical.
     auto flush = [&](int half, float mo_own) __attribute__((always_inline)) {
+      float* rec = flush_rec();
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
         const float mo = mold_s[half][32 * rb + n];
@@ -580,6 +591,16 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
       if constexpr (FMT == 0) MLA_WAIT_VMCNT(kResolveLoads);
       MLA_BARRIER_NO_FENCE();
       const uint64_t vm = vm_cur;
+      // Sparse: address of tile kt+2's page-table entry.  res_t was loaded
+      // during the previous tile; using it here, where only that tile's two
+      // resolve loads can still be in flight, keeps the wait the compiler
+      // places for it from also waiting for this tile's copies.  (Dense
+      // positions are arithmetic: no wait, no early address needed.)
+      const int32_t* pg_ptr = bt_row;
+      if constexpr (SPARSE) {
+        pg_ptr = bt_row + (visible(res_t) ? (res_t >> 6) : 0);
+        asm volatile("" : "+v"(pg_ptr));
+      }
       // 2. sources of tile kt+1's copy; the copies themselves are issued
       //    between the MFMAs of the first score chain (res_off is -1 for
       //    every key past the unit's last tile)
@@ -610,8 +631,9 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
           // limits folded into jlim); sparse: the per-key validity mask
           // (bit 8*(v/4) + v%4 of the lane's mask word is key
           // 32*kb2 + 8*(v/4) + 4*h + v%4)
-          const bool full = SPARSE ? (uint32_t)(vm >> (32 * kb2)) == 0xffffffffu
-                                   : __builtin_amdgcn_readfirstlane(__all(jlim >= 32 * kb2 + 31) ? 1 : 0) != 0;
+          const bool full =
+              SPARSE ? __builtin_amdgcn_readfirstlane((uint32_t)(vm >> (32 * kb2))) == 0xffffffffu
+                     : __builtin_amdgcn_readfirstlane(__all(jlim >= 32 * kb2 + 31) ? 1 : 0) != 0;
           if (!full) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
@@ -638,10 +660,15 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
           hs.nmuse = (m == -INFINITY) ? 0.0f : -m;
           hs.lh = 0.0f;
         } else if (u == 8) {
-          if (h == 0) mold_s[kb2][rs] = hs.mo;
+          // the row index is recomputed here rather than kept in a register
+          int tid = threadIdx.x;
+          asm volatile("" : "+v"(tid));
+          if (h == 0) mold_s[kb2][((tid >> 6) << 5) + (tid & 31)] = hs.mo;
         } else if (u == 9) {
           const bool any_grow = __ballot(hs.grow) != 0;
-          if (lane == 0) gflag[kb2][wave] = any_grow ? 1u : 0u;
+          int tid = threadIdx.x;  // (address recomputed, not kept in a register)
+          asm volatile("" : "+v"(tid));
+          if ((tid & 63) == 0) gflag[kb2][tid >> 6] = any_grow ? 1u : 0u;
         } else if (u < 26) {
           const int v = u - 10;
           const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[v], scale, hs.nmuse));
@@ -732,7 +759,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
       // the top of the next tile counts these loads as the only ones newer
       // than the copies
       asm volatile("" ::: "memory");
-      pg2 = page_of(res_t);
+      pg2 = SPARSE ? *pg_ptr : page_of(res_t);
       t3 = position(kt + 3);
       asm volatile("" ::: "memory");
       MLA_BARRIER_NO_FENCE();  // half 1's P^T and maxima visible
@@ -754,6 +781,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
     // publishes the row's output factors; every wave then normalises and
     // stores its column blocks.
     float fa = 0.0f, fc = 1.0f, mfin = m, lfin = l;
+    float* rec = flush_rec();
     if (flushed) {
       const float mf = rec[261];
       mfin = fmaxf(mf, m);
