@@ -512,6 +512,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
     };
     constexpr int kResolveLoads = SPARSE ? 2 : 1;  // per thread per tile
     int res_t, pg2 = 0, t3 = -1;
+    bool t3_ok = false;  // sparse: tile kt+3's slot of this lane holds an index
     int64_t res_off;
     uint64_t vm_cur;  // keys of the current tile that are visible (sparse masking)
     __syncthreads();  // the previous segment is fully consumed (tiles, P^T, epilogue slots)
@@ -596,10 +597,10 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
       // resolve loads can still be in flight, keeps the wait the compiler
       // places for it from also waiting for this tile's copies.  (Dense
       // positions are arithmetic: no wait, no early address needed.)
-      const int32_t* pg_ptr = bt_row;
+      int pg_idx = 0;
       if constexpr (SPARSE) {
-        pg_ptr = bt_row + (visible(res_t) ? (res_t >> 6) : 0);
-        asm volatile("" : "+v"(pg_ptr));
+        pg_idx = visible(res_t) ? (res_t >> 6) : 0;
+        asm volatile("" : "+v"(pg_idx));
       }
       // 2. sources of tile kt+1's copy; the copies themselves are issued
       //    between the MFMAs of the first score chain (res_off is -1 for
@@ -759,15 +760,27 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
       // the top of the next tile counts these loads as the only ones newer
       // than the copies
       asm volatile("" ::: "memory");
-      pg2 = SPARSE ? *pg_ptr : page_of(res_t);
-      t3 = position(kt + 3);
+      pg2 = SPARSE ? bt_row[pg_idx] : page_of(res_t);
+      if constexpr (SPARSE) {
+        // The raw index of tile kt+3, loaded from assembly and waited for
+        // at the end of the tile: a compiler-visible load next to its use
+        // gets a wait right here, which also waits for every copy issued
+        // before it.  Validity is applied at the end of the tile.
+        const int k = (kt + 3) * kPage + lane;
+        const int32_t* ip = idx_row + (k < s.topk ? k : s.topk - 1);
+        asm volatile("global_load_dword %0, %1, off" : "=v"(t3) : "v"(ip) : "memory");
+        t3_ok = kt + 3 < kend && k < s.topk;
+      } else {
+        t3 = position(kt + 3);
+      }
       asm volatile("" ::: "memory");
       MLA_BARRIER_NO_FENCE();  // half 1's P^T and maxima visible
       pv_half(1, ks + kRopeOffset, [&] { settle(1, hs1); }, [](auto) {});
 
       // 5. finish resolving tile kt+2
       res_off = offset_of(res_t, pg2);
-      res_t = t3;
+      if constexpr (SPARSE) asm volatile("s_waitcnt vmcnt(0)" : "+v"(t3) :: "memory");
+      res_t = (!SPARSE || t3_ok) ? t3 : -1;
       if constexpr (FMT == 1) {
         if (has_next) {
           MLA_WAIT_VMCNT(0);
