@@ -205,8 +205,8 @@ struct TileCopy {
   // copies in flight at HBM latency, and a burst stalls instruction issue
   // until the first ones return.  bf16: 7 copies in each score chain (after
   // the MFMAs of steps 2, 7, .., 32) and 4 early in the first P*V half
-  // (after MFMAs 2, 7, 12, 17); FP8 (whose rows are needed by the
-  // dequantisation at the end of the tile): 6 in each score chain.  FP8
+  // (after MFMAs 2, 7, 12, 17); FP8 (whose rows are dequantised from the
+  // second P*V half on): 6 in each score chain.  FP8
   // issues copies 10 and 11 (the RoPE group, which needs the zero-row
   // source) first, so that source is not held long.
   static constexpr int slot(int phase, int step) {
@@ -250,47 +250,57 @@ __device__ inline __attribute__((always_inline)) void static_for(F&& f) {
   }
 }
 
-// Dequantise the staged FP8 rows into the bf16 tile: value =
-// bf16(float(e4m3) * scale of its 1x128 tile), RoPE bf16 copied through.
-__device__ inline void dequant_stage(const uint8_t* stage, uint8_t* ks) {
-  int tid = threadIdx.x;
-  asm volatile("" : "+v"(tid));
-  const int key = tid >> 2;
-  const int sub = tid & 3;
-  auto stage_chunk = [&](int c) -> const uint8_t* {
-    return stage + ((c >> 3) * 512 + key * 8 + (c & 7)) * 16;
-  };
-  const f32x4 scales = *reinterpret_cast<const f32x4*>(stage_chunk(32));
-  // all eight code chunks are read before any is converted, so the reads
-  // overlap instead of each waiting out the LDS latency
-  u32x4 raw[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) raw[j] = *reinterpret_cast<const u32x4*>(stage_chunk(sub + 4 * j));
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {  // code chunk cc = sub + 4*j: dims 16*cc .. 16*cc+15
-    const int cc = sub + 4 * j;
-    const u32x4 v = raw[j];
-    const float sc = scales[j >> 1];
-    u32x4 lo, hi;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8(v[w], false);
-      const auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8(v[w], true);
-      const bf16x2 p01 = __builtin_convertvector(f32x2{f01[0] * sc, f01[1] * sc}, bf16x2);
-      const bf16x2 p23 = __builtin_convertvector(f32x2{f23[0] * sc, f23[1] * sc}, bf16x2);
-      const uint32_t w01 = __builtin_bit_cast(uint32_t, p01), w23 = __builtin_bit_cast(uint32_t, p23);
-      if (w < 2) { lo[2 * w] = w01; lo[2 * w + 1] = w23; } else { hi[2 * w - 4] = w01; hi[2 * w - 3] = w23; }
-    }
-    *reinterpret_cast<u32x4*>(ks + tile_chunk(key, 2 * cc)) = lo;
-    *reinterpret_cast<u32x4*>(ks + tile_chunk(key, 2 * cc + 1)) = hi;
+// Dequantisation of 32 staged FP8 rows (row0 .. row0+31) into the bf16
+// tile: value = bf16(float(e4m3) * scale of its 1x128 tile), RoPE bf16
+// copied through (FlashMLA page, section 设计 2).  Thread t handles row
+// row0 + t/8: code chunks sub + 8j (j < 4, dims 16*(sub+8j) .. +15, scale
+// j) and RoPE chunk sub, sub = t%8.  Split into load(), 32 convert parts of
+// four VALU instructions each (part p: chunk p/8, half of word (p/2)%4) with
+// a store after every 8th, and store_rope(), so the work can be spread
+// between MFMAs.
+struct HalfDequant {
+  u32x4 raw[2];  // code chunks j (in raw[j%2]); chunk j+1 is read while j is converted
+  u32x4 rope;
+  f32x4 scales;
+  u32x4 out;     // bf16 pairs of the half chunk being converted
+  const uint8_t* src;
+  int row, sub;
+
+  __device__ inline const uint8_t* stage_chunk(int c) const {
+    return src + ((c >> 3) * 512 + row * 8 + (c & 7)) * 16;
   }
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {  // RoPE: bf16 chunks 64..71 <- raw chunks 33..40
-    const int i = sub + 4 * j;
-    *reinterpret_cast<u32x4*>(ks + tile_chunk(key, 64 + i)) =
-        *reinterpret_cast<const u32x4*>(stage_chunk(33 + i));
+  __device__ inline void load(const uint8_t* stage, int row0) {
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    src = stage;
+    row = row0 + (tid >> 3);
+    sub = tid & 7;
+    scales = *reinterpret_cast<const f32x4*>(stage_chunk(32));
+    raw[0] = *reinterpret_cast<const u32x4*>(stage_chunk(sub));
   }
-}
+  __device__ inline void load_rope() { rope = *reinterpret_cast<const u32x4*>(stage_chunk(33 + sub)); }
+  template <int P>
+  __device__ inline void convert(uint8_t* ks) {
+    constexpr int j = P >> 3, w = (P >> 1) & 3, hw = P & 1;
+    if constexpr ((P & 7) == 0 && j + 1 < 4)
+      raw[(j + 1) & 1] = *reinterpret_cast<const u32x4*>(stage_chunk(sub + 8 * (j + 1)));
+    const float sc = scales[j];
+    const auto f = __builtin_amdgcn_cvt_pk_f32_fp8(raw[j & 1][w], hw != 0);
+    const bf16x2 b = __builtin_convertvector(f32x2{f[0] * sc, f[1] * sc}, bf16x2);
+    out[2 * (w & 1) + hw] = __builtin_bit_cast(uint32_t, b);
+    if constexpr ((P & 3) == 3)  // words 0-1 (bf16 chunk 2cc) or 2-3 (2cc+1) done
+      *reinterpret_cast<u32x4*>(ks + tile_chunk(row, 2 * (sub + 8 * j) + (w >> 1))) = out;
+  }
+  __device__ inline void store_rope(uint8_t* ks) {
+    *reinterpret_cast<u32x4*>(ks + tile_chunk(row, 64 + sub)) = rope;  // bf16 chunks 64..71
+  }
+  __device__ inline void all(const uint8_t* stage, uint8_t* ks, int row0) {
+    load(stage, row0);
+    static_for<0, 32>([&](auto p) __attribute__((always_inline)) { convert<decltype(p)::value>(ks); });
+    load_rope();
+    store_rope(ks);
+  }
+};
 
 // Workgroup barrier without a memory fence: the compiler's fence would wait
 // for every outstanding global->LDS copy, including the next tile's.  LDS
@@ -388,6 +398,10 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds0[kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t lds1[FMT == 0 ? kTileBytes : kStageBytes];
   __shared__ __attribute__((aligned(16))) uint8_t pbuf[kPHalfBytes];  // P^T of half 0
+  // FP8: P^T of half 1 (bf16 keeps it in the tile's RoPE chunk group; FP8
+  // overwrites rows 0..31 of the tile, RoPE chunks included, during the
+  // second P*V half)
+  __shared__ __attribute__((aligned(16))) uint8_t pbuf1[FMT == 1 ? kPHalfBytes : 16];
   __shared__ float mold_s[2][kRowsPerGroup];  // per row: running max before each half's update
   __shared__ __attribute__((aligned(16))) uint32_t gflag[2][4];  // per wave: some row grew
   __shared__ f32x4 oslots[kThreads];  // per-lane slot for copying accumulators
@@ -529,7 +543,9 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
       if constexpr (FMT == 1) {
         MLA_WAIT_VMCNT(0);
         __syncthreads();
-        dequant_stage(lds1, lds0);
+        HalfDequant dq;
+        dq.all(lds1, lds0, 0);
+        dq.all(lds1, lds0, 32);
       }
     }
     // Everything loaded so far (Q, rows, the first tile) is needed before the
@@ -632,9 +648,14 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
           // limits folded into jlim); sparse: the per-key validity mask
           // (bit 8*(v/4) + v%4 of the lane's mask word is key
           // 32*kb2 + 8*(v/4) + 4*h + v%4)
-          const bool full =
-              SPARSE ? __builtin_amdgcn_readfirstlane((uint32_t)(vm >> (32 * kb2))) == 0xffffffffu
-                     : __builtin_amdgcn_readfirstlane(__all(jlim >= 32 * kb2 + 31) ? 1 : 0) != 0;
+          bool full;
+          if constexpr (SPARSE) {
+            uint32_t word = (uint32_t)(vm >> (32 * kb2));
+            asm volatile("" : "+s"(word));  // a 32-bit scalar test, not a 64-bit constant compare
+            full = word == 0xffffffffu;
+          } else {
+            full = __builtin_amdgcn_readfirstlane(__all(jlim >= 32 * kb2 + 31) ? 1 : 0) != 0;
+          }
           if (!full) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
@@ -677,7 +698,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
           hs.pf[v >> 3][v & 7] = (__bf16)p;
         } else if (u < 28) {
           const int sp = u - 26;
-          uint8_t* pb = kb2 == 0 ? pbuf : ks + kRopeOffset;
+          uint8_t* pb = kb2 == 0 ? pbuf : (FMT == 1 ? pbuf1 : ks + kRopeOffset);
           *reinterpret_cast<bf16x8*>(pb + 2048 * wave + p_off[sp]) = hs.pf[sp];
         }
       };
@@ -774,8 +795,26 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
         t3 = position(kt + 3);
       }
       asm volatile("" ::: "memory");
+      // FP8: this thread's copies of tile kt+1 are complete (only the
+      // resolve loads may be newer), so after the barrier every staged row
+      // is visible to the dequantisation below
+      if constexpr (FMT == 1) MLA_WAIT_VMCNT(kResolveLoads);
       MLA_BARRIER_NO_FENCE();  // half 1's P^T and maxima visible
-      pv_half(1, ks + kRopeOffset, [&] { settle(1, hs1); }, [](auto) {});
+      if constexpr (FMT == 0) {
+        pv_half(1, ks + kRopeOffset, [&] { settle(1, hs1); }, [](auto) {});
+      } else {
+        // rows 0..31 of tile kt are no longer read (half 0 is done): the
+        // staged rows 0..31 of tile kt+1 are dequantised into them between
+        // the MFMAs of half 1 (after a unit's last tile they are zero rows
+        // written into a tile nothing reads any more)
+        HalfDequant dq;
+        pv_half(1, pbuf1, [&] { dq.load(lds1, 0); settle(1, hs1); },
+                [&](auto j_c) __attribute__((always_inline)) {
+                  dq.template convert<decltype(j_c)::value>(ks);
+                  if constexpr (decltype(j_c)::value == 24) dq.load_rope();
+                  if constexpr (decltype(j_c)::value == 31) dq.store_rope(ks);
+                });
+      }
 
       // 5. finish resolving tile kt+2
       res_off = offset_of(res_t, pg2);
@@ -783,9 +822,9 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
       res_t = (!SPARSE || t3_ok) ? t3 : -1;
       if constexpr (FMT == 1) {
         if (has_next) {
-          MLA_WAIT_VMCNT(0);
-          __syncthreads();  // staged rows complete, bf16 tile consumed
-          dequant_stage(lds1, lds0);
+          __syncthreads();  // rows 32..63 of tile kt consumed
+          HalfDequant dq;
+          dq.all(lds1, lds0, 32);
         }
       }
     }
