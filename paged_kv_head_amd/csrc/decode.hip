@@ -185,6 +185,21 @@ struct TileCopy {
     }
     dst = __builtin_amdgcn_readfirstlane(buf + 1024 * wave);  // wave-uniform
   }
+  // Dense tiles are pages: key row r of tile `tile` is row r of physical
+  // page `page`, visible while tile*64 + r < vis (vis = the sequence length,
+  // or 0 to copy zero rows only).  No cross-lane exchange is needed.
+  __device__ inline void prepare_page(const uint8_t* __restrict__ kv, int page, int tile, int vis,
+                                      uint32_t buf, int wave, int lane) {
+    asm volatile("" : "+v"(lane), "+v"(wave));
+    const uint8_t* pbase = kv + (int64_t)page * (kPage * RowBytes<FMT>::value);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int row = 32 * half + 8 * wave + (lane >> 3);
+      const int c8 = FMT == 0 ? ((lane & 7) - swz(row)) & 7 : (lane & 7);
+      base[half] = (tile * kPage + row < vis ? pbase + row * RowBytes<FMT>::value : g_zero_row) + 16 * c8;
+    }
+    dst = __builtin_amdgcn_readfirstlane(buf + 1024 * wave);  // wave-uniform
+  }
   // Copy t: source chunk group t/2 (128*(t/2) + 16*7 + 16 <= 1168, so a
   // masked row's source stays inside the zero row).
   template <int T>
@@ -505,8 +520,9 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) o[cb][rb] = f32x16{};
 
-    // Row resolution.  Every wave resolves all 64 keys of a tile (lane k:
-    // key k) and takes the rows it copies from the resolving lanes.
+    // Row resolution of sparse tiles.  Every wave resolves all 64 keys of a
+    // tile (lane k: key k) and takes the rows it copies from the resolving
+    // lanes.
     //   res_t:   logical position of key `lane` in tile kt+2
     //   res_off: cache byte offset of key `lane` in tile kt+1 (-1: masked)
     const int32_t* idx_row = SPARSE ? a.indices + (int64_t)u * s.topk : nullptr;
@@ -524,21 +540,29 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
     auto offset_of = [&](int t, int page) -> int64_t {
       return visible(t) ? ((int64_t)page * kPage + (t & 63)) * kRowBytes : (int64_t)-1;
     };
-    constexpr int kResolveLoads = SPARSE ? 2 : 1;  // per thread per tile
-    int res_t, pg2 = 0, t3 = -1;
+    // Dense: the page of tile kt+1 (wave-uniform, a scalar load issued one
+    // tile ahead).  Sparse: the per-key resolution below.
+    int pg_next = 0;
+    constexpr int kResolveLoads = SPARSE ? 2 : 0;  // vector loads per thread per tile
+    int res_t = -1, pg2 = 0, t3 = -1;
     bool t3_ok = false;  // sparse: tile kt+3's slot of this lane holds an index
-    int64_t res_off;
-    uint64_t vm_cur;  // keys of the current tile that are visible (sparse masking)
+    int64_t res_off = -1;
+    uint64_t vm_cur = 0;  // keys of the current tile that are visible (sparse masking)
     __syncthreads();  // the previous segment is fully consumed (tiles, P^T, epilogue slots)
     {
-      const int t0 = position(kfirst);
-      const int t1 = position(kfirst + 1);
-      res_t = position(kfirst + 2);
-      const int64_t off0 = offset_of(t0, page_of(t0));
-      res_off = offset_of(t1, page_of(t1));
-      vm_cur = __ballot(off0 >= 0);
       TileCopy<FMT> first;
-      first.prepare(a.kv, off0, lds_addr(FMT == 0 ? lds0 : lds1), wave, lane);
+      if constexpr (SPARSE) {
+        const int t0 = position(kfirst);
+        const int t1 = position(kfirst + 1);
+        res_t = position(kfirst + 2);
+        const int64_t off0 = offset_of(t0, page_of(t0));
+        res_off = offset_of(t1, page_of(t1));
+        vm_cur = __ballot(off0 >= 0);
+        first.prepare(a.kv, off0, lds_addr(FMT == 0 ? lds0 : lds1), wave, lane);
+      } else {
+        first.prepare_page(a.kv, bt_row[kfirst], kfirst, L, lds_addr(FMT == 0 ? lds0 : lds1), wave, lane);
+        pg_next = bt_row[min(kfirst + 1, nb - 1)];
+      }
       first.issue_all(lane);
       if constexpr (FMT == 1) {
         MLA_WAIT_VMCNT(0);
@@ -622,8 +646,15 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
       //    between the MFMAs of the first score chain (res_off is -1 for
       //    every key past the unit's last tile)
       TileCopy<FMT> next;
-      next.prepare(a.kv, res_off, lds_addr(FMT == 1 ? lds1 : (odd ? lds0 : lds1)), wave, lane);
-      vm_cur = __ballot(res_off >= 0);
+      const uint32_t next_buf = lds_addr(FMT == 1 ? lds1 : (odd ? lds0 : lds1));
+      if constexpr (SPARSE) {
+        next.prepare(a.kv, res_off, next_buf, wave, lane);
+        vm_cur = __ballot(res_off >= 0);
+      } else {
+        // tile kt+1 past the segment: zero rows
+        next.prepare_page(a.kv, pg_next, kt + 1, kt + 1 < kend ? L : 0, next_buf, wave, lane);
+        pg_next = bt_row[min(kt + 2, nb - 1)];  // for the next tile; a scalar load
+      }
 
       uint8_t* ks = (FMT == 0 && odd) ? lds1 : lds0;
       uint32_t lanemask[2];  // sparse: visibility of keys 32*kb2 + 4*h + (0..31)
@@ -781,8 +812,8 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
       // the top of the next tile counts these loads as the only ones newer
       // than the copies
       asm volatile("" ::: "memory");
-      pg2 = SPARSE ? bt_row[pg_idx] : page_of(res_t);
       if constexpr (SPARSE) {
+        pg2 = bt_row[pg_idx];
         // The raw index of tile kt+3, loaded from assembly and waited for
         // at the end of the tile: a compiler-visible load next to its use
         // gets a wait right here, which also waits for every copy issued
@@ -791,8 +822,6 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
         const int32_t* ip = idx_row + (k < s.topk ? k : s.topk - 1);
         asm volatile("global_load_dword %0, %1, off" : "=v"(t3) : "v"(ip) : "memory");
         t3_ok = kt + 3 < kend && k < s.topk;
-      } else {
-        t3 = position(kt + 3);
       }
       asm volatile("" ::: "memory");
       // FP8: this thread's copies of tile kt+1 are complete (only the
@@ -817,9 +846,11 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
       }
 
       // 5. finish resolving tile kt+2
-      res_off = offset_of(res_t, pg2);
-      if constexpr (SPARSE) asm volatile("s_waitcnt vmcnt(0)" : "+v"(t3) :: "memory");
-      res_t = (!SPARSE || t3_ok) ? t3 : -1;
+      if constexpr (SPARSE) {
+        res_off = offset_of(res_t, pg2);
+        asm volatile("s_waitcnt vmcnt(0)" : "+v"(t3) :: "memory");
+        res_t = t3_ok ? t3 : -1;
+      }
       if constexpr (FMT == 1) {
         if (has_next) {
           __syncthreads();  // rows 32..63 of tile kt consumed
