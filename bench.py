@@ -45,7 +45,26 @@ def parse():
     ap.add_argument("--num-parts", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-units", type=int, default=None)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run three 1 GiB device-to-device copies (reference for the HBM byte "
+                         "counters under rocprofv3), print nothing else")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """Three copies of a 1 GiB device buffer: a kernel of known traffic
+    (1 GiB read and 1 GiB written per dispatch) that calibrates rocprofv3's
+    FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
 
 
 def traffic_record(config_name: str):
@@ -92,6 +111,9 @@ def cpu_baseline(w, sample_units, min_seconds=10.0, max_reps=6):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); "
               "the path shards by batch or by query head with no exchange, so N GPUs "
