@@ -322,6 +322,11 @@ struct HalfDequant {
 // accesses issued before it are complete (lgkmcnt(0)); the asm memory
 // clobber keeps the compiler from moving LDS accesses across it.
 #define MLA_BARRIER_NO_FENCE() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
+// The same barrier with the n most recent LDS reads of this wave still in
+// flight.  LDS instructions of a wave complete in issue order, so every LDS
+// access issued before those n is complete when the barrier is signalled
+// (outstanding scalar loads, which also count here, only make it stricter).
+#define MLA_BARRIER_NO_FENCE_KEEP(n) asm volatile("s_waitcnt lgkmcnt(%0)\n\ts_barrier" ::"n"(n) : "memory")
 
 // s_waitcnt with only the vector-memory counter limited to n (n < 64).
 #define MLA_WAIT_VMCNT(n) \
@@ -403,6 +408,8 @@ struct HalfSoftmax {
   bf16x8 pf[2]; // bf16 probabilities, MFMA operand order
 };
 constexpr int kSoftmaxSteps = 28;
+// P*V reads V^T this many column groups (4 MFMAs each) ahead of its use.
+constexpr int kVAhead = 2;
 
 template <int FMT, bool SPARSE>
 __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
@@ -726,6 +733,10 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
           const int v = u - 10;
           const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[v], scale, hs.nmuse));
           hs.lh += p;
+          // keeps the add in this step: otherwise the compiler sinks all 16
+          // into one dependent chain at the row-sum update, with every
+          // probability held in a register until then
+          asm volatile("" : "+v"(hs.lh));
           hs.pf[v >> 3][v & 7] = (__bf16)p;
         } else if (u < 28) {
           const int sp = u - 26;
@@ -744,43 +755,47 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
       };
 
       // O^T += V^T P^T for half kb2 over this wave's 4 column blocks and the
-      // 4 row blocks, hook(j) after MFMA j (32 of them).  Within
-      // each 16-lane group, transpose read: lane j points at 4 consecutive
-      // columns of one key row (key j/4 of the group's 4) and lane i
-      // receives column i of those 4 keys.  k slot (h, e) <-> key
-      // 32*kb2 + 16*sp + 8*(e/4) + 4*h + e%4.
-      auto pv_half = [&](int kb2, const uint8_t* pb, auto&& pre, auto&& hook) __attribute__((always_inline)) {
-        auto load_v = [&](int sp, int cb) {
-          const uint8_t* vb = ks + 8192 * (2 * wave + (cb >> 1)) + 4096 * kb2 + 2048 * sp;
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_ptr<i16x4>(vb + v_off[cb & 1][0]));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_ptr<i16x4>(vb + v_off[cb & 1][1]));
-          return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        };
+      // 4 row blocks: 8 groups g = (key step sp = g/4, column block cb = g%4)
+      // of 4 MFMAs, hook(j) after MFMA j (32 of them).  Within each 16-lane
+      // group, transpose read: lane j points at 4 consecutive columns of one
+      // key row (key j/4 of the group's 4) and lane i receives column i of
+      // those 4 keys.  k slot (h, e) <-> key 32*kb2 + 16*sp + 8*(e/4) + 4*h +
+      // e%4.  V^T operands rotate through kVAhead + 1 registers; the first
+      // kVAhead groups' operands are tile data and are read before the
+      // barrier that publishes the half's P^T (pv_prefetch).
+      auto load_v = [&](int kb2, int g) {
+        const int sp = g >> 2, cb = g & 3;
+        const uint8_t* vb = ks + 8192 * (2 * wave + (cb >> 1)) + 4096 * kb2 + 2048 * sp;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_ptr<i16x4>(vb + v_off[cb & 1][0]));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_ptr<i16x4>(vb + v_off[cb & 1][1]));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      constexpr int kVRegs = kVAhead + 1;
+      constexpr int kVPrefetchReads = 2 * kVAhead;  // LDS reads issued by pv_prefetch
+      auto pv_prefetch = [&](int kb2, bf16x8* vf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int g = 0; g < kVAhead; ++g) vf[g] = load_v(kb2, g);
+      };
+      auto pv_half = [&](int kb2, const uint8_t* pb, bf16x8* vf, auto&& pre, auto&& hook) __attribute__((always_inline)) {
         auto load_p = [&](int sp, int rb) {
           return *reinterpret_cast<const bf16x8*>(pb + 2048 * rb + p_off[sp]);
         };
         bf16x8 pfr[4];
-        bf16x8 vf[2];
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) pfr[rb] = load_p(0, rb);
-        vf[0] = load_v(0, 0);
         pre();  // runs while the first operands are in flight
         static_for<0, 8>([&](auto g_c) __attribute__((always_inline)) {
           constexpr int g = decltype(g_c)::value;
           constexpr int cb = g & 3;
-          // read ahead: the next group's V^T block
-          if constexpr (g + 1 < 8) vf[(g + 1) & 1] = load_v((g + 1) >> 2, (g + 1) & 3);
+          if constexpr (g + kVAhead < 8) vf[(g + kVAhead) % kVRegs] = load_v(kb2, g + kVAhead);
           static_for<0, 4>([&](auto rb_c) __attribute__((always_inline)) {
             constexpr int rb = decltype(rb_c)::value;
-            o[cb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[g & 1], pfr[rb], o[cb][rb], 0, 0, 0);
+            o[cb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[g % kVRegs], pfr[rb], o[cb][rb], 0, 0, 0);
+            // the second key step's P^T block rb, right after its last use
+            if constexpr (g == 3) pfr[rb] = load_p(1, rb);
             hook(std::integral_constant<int, 4 * g + rb>{});
             __builtin_amdgcn_sched_barrier(0);
           });
-          // the second key step's P^T, once the first step's last MFMAs are issued
-          if constexpr (g == 3) {
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb) pfr[rb] = load_p(1, rb);
-          }
         });
       };
 
@@ -802,8 +817,10 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
 
       // 4. half 0's P^T and maxima visible; every wave is past the scores,
       //    so the RoPE chunk group is free for half 1's P^T
-      MLA_BARRIER_NO_FENCE();
-      pv_half(0, pbuf, [&] { settle(0, hs0); }, [&](auto j_c) __attribute__((always_inline)) {
+      bf16x8 vf[kVRegs];
+      pv_prefetch(0, vf);
+      MLA_BARRIER_NO_FENCE_KEEP(kVPrefetchReads);
+      pv_half(0, pbuf, vf, [&] { settle(0, hs0); }, [&](auto j_c) __attribute__((always_inline)) {
         constexpr int j = decltype(j_c)::value;
         next.template issue_at<2, j>(lane);
         if constexpr (j < kSoftmaxSteps) softmax_step(1, sacc1, hs1, j);
@@ -828,16 +845,17 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
       // resolve loads may be newer), so after the barrier every staged row
       // is visible to the dequantisation below
       if constexpr (FMT == 1) MLA_WAIT_VMCNT(kResolveLoads);
-      MLA_BARRIER_NO_FENCE();  // half 1's P^T and maxima visible
+      pv_prefetch(1, vf);
+      MLA_BARRIER_NO_FENCE_KEEP(kVPrefetchReads);  // half 1's P^T and maxima visible
       if constexpr (FMT == 0) {
-        pv_half(1, ks + kRopeOffset, [&] { settle(1, hs1); }, [](auto) {});
+        pv_half(1, ks + kRopeOffset, vf, [&] { settle(1, hs1); }, [](auto) {});
       } else {
         // rows 0..31 of tile kt are no longer read (half 0 is done): the
         // staged rows 0..31 of tile kt+1 are dequantised into them between
         // the MFMAs of half 1 (after a unit's last tile they are zero rows
         // written into a tile nothing reads any more)
         HalfDequant dq;
-        pv_half(1, pbuf1, [&] { dq.load(lds1, 0); settle(1, hs1); },
+        pv_half(1, pbuf1, vf, [&] { dq.load(lds1, 0); settle(1, hs1); },
                 [&](auto j_c) __attribute__((always_inline)) {
                   dq.template convert<decltype(j_c)::value>(ks);
                   if constexpr (decltype(j_c)::value == 24) dq.load_rope();
