@@ -251,10 +251,57 @@ struct TileCopy {
     constexpr int t = slot(PHASE, STEP);
     if constexpr (t >= 0) issue<t>(lane);
   }
+  // Schedule of dense bf16 tiles, whose P*V runs half a tile behind the
+  // scores.  During the first score chain: rows 0..31 of chunk groups 0..7
+  // (copies 0, 2, .., 14, after MFMAs 2, 6, .., 30).  During the second:
+  // the RoPE group of rows 0..31 (copy 16) first, then rows 32..63 of
+  // groups 0..7 (copies 1, 3, .., 15) and their RoPE group (17), after
+  // MFMAs 1, 4, .., 28.  Rows 0..31 of the tile are complete once at most
+  // kLateCopies copies are in flight; all of it once at most kEarlyCopies
+  // (those of the next tile's first chain) are.
+  static constexpr int kEarlyCopies = 8;
+  static constexpr int kLateCopies = 9;
+  static constexpr int slot_split(int phase, int step) {
+    if (phase == 0) return (step % 4 == 2 && step / 4 < kEarlyCopies) ? 2 * (step / 4) : -1;
+    if (step % 3 != 1 || step / 3 > kLateCopies) return -1;
+    const int i = step / 3;
+    return i == 0 ? 16 : (i == kLateCopies ? 17 : 2 * i - 1);
+  }
+  static constexpr bool split_slots_cover_copies() {
+    int seen[kCopies] = {};
+    for (int phase = 0; phase < 2; ++phase)
+      for (int step = 0; step < 36; ++step) {
+        const int t = slot_split(phase, step);
+        if (t >= kCopies) return false;
+        if (t >= 0) ++seen[t];
+      }
+    for (int t = 0; t < kCopies; ++t)
+      if (seen[t] != 1) return false;
+    // rows 0..31 (even copies) before rows 32..63, and copy 16 first in the
+    // second chain: exactly kLateCopies follow it
+    int after16 = 0;
+    bool past16 = false;
+    for (int step = 0; step < 36; ++step) {
+      const int t = slot_split(1, step);
+      if (t < 0) continue;
+      if (past16) ++after16;
+      if (t == 16) past16 = true;
+      else if (!past16) return false;
+      else if (t % 2 == 0) return false;
+    }
+    return after16 == kLateCopies;
+  }
+  template <int PHASE, int STEP>
+  __device__ inline void issue_split(int lane) const {
+    constexpr int t = slot_split(PHASE, STEP);
+    if constexpr (t >= 0) issue<t>(lane);
+  }
 };
 
 static_assert(TileCopy<0>::slots_cover_copies() && TileCopy<1>::slots_cover_copies(),
               "copy schedule must issue every copy of a tile once");
+static_assert(TileCopy<0>::split_slots_cover_copies(),
+              "split copy schedule must issue every copy of a tile once, rows 0..31 first");
 
 // f(integral_constant<I>) for I = B .. E-1, unrolled at compile time.
 template <int B, int E, class F>
@@ -405,9 +452,10 @@ struct HalfSoftmax {
   float mo;     // running max before this half's update
   float nmuse;  // minus the reference the probabilities are taken against
   float lh;     // this half's part of the row sum
+  float x, e;   // scaled score and probability in flight between steps
   bf16x8 pf[2]; // bf16 probabilities, MFMA operand order
 };
-constexpr int kSoftmaxSteps = 28;
+constexpr int kSoftmaxSteps = 29;
 // P*V reads V^T this many column groups (4 MFMAs each) ahead of its use.
 constexpr int kVAhead = 2;
 
@@ -425,12 +473,15 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
   // second P*V half)
   __shared__ __attribute__((aligned(16))) uint8_t pbuf1[FMT == 1 ? kPHalfBytes : 16];
   __shared__ float mold_s[2][kRowsPerGroup];  // per row: running max before each half's update
-  __shared__ __attribute__((aligned(16))) uint32_t gflag[2][4];  // per wave: some row grew
+  // per half, wave and lane: some row of the wave grew (every lane writes
+  // the wave's value to its own word, so the write needs no branch)
+  __shared__ uint32_t gflag[2][4][64];
   __shared__ f32x4 oslots[kThreads];  // per-lane slot for copying accumulators
   f32x4* const oslot = &oslots[threadIdx.x];
 
   const Shape& s = a.s;
   constexpr int kRowBytes = RowBytes<FMT>::value;
+  constexpr bool kPipelined = FMT == 0 && !SPARSE;  // tile loop order, below
 
   // Workgroup -> (part, row group).  Workgroups are dealt round-robin to
   // the 8 XCDs, so the row groups of one part get ids congruent mod 8 and
@@ -628,17 +679,237 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
       flushed = true;
     };
 
+    // Per-tile state read by the softmax and P*V steps below.
+    uint8_t* ks = lds0;               // buffer of the tile being scored
+    uint64_t vm = 0;                  // sparse: visible keys of that tile
+    uint32_t lanemask[2] = {0u, 0u};  // sparse: visibility of keys 32*kb2 + 4*h + (0..31)
+    int jlim = 63;                    // dense: keys j <= jlim of that tile may count
+
+    // The softmax of half kb2 (raw scores in sc; scores in log2 units are
+    // scale * raw with scale > 0), cut into kSoftmaxSteps small steps of a
+    // few VALU instructions each.  One step goes between two MFMAs: an
+    // MFMA cannot issue while the matrix core is busy, and only the
+    // independent instructions that precede it in program order run in
+    // the shadow of the previous one.
+    //   0..3   mask the half if any of its keys is not visible (step 0),
+    //          max of the raw scores
+    //   4..9   row max across the lane pair, running max update, publish
+    //   9..26  probabilities, software-pipelined so no step waits on a
+    //          result of the same step: step 10+v takes the exponential of
+    //          score v, the scaled score v+1 and the row sum and bf16
+    //          operand of probability v-1
+    //   27, 28 store the half's P^T
+    auto softmax_step = [&](int kb2, f32x16& sc, HalfSoftmax& hs, int u) __attribute__((always_inline)) {
+      if (u == 0) {
+        // dense: visible keys are a prefix of the tile (tail and causal
+        // limits folded into jlim); sparse: the per-key validity mask
+        // (bit 8*(v/4) + v%4 of the lane's mask word is key
+        // 32*kb2 + 8*(v/4) + 4*h + v%4)
+        bool full;
+        if constexpr (SPARSE) {
+          uint32_t word = (uint32_t)(vm >> (32 * kb2));
+          asm volatile("" : "+s"(word));  // a 32-bit scalar test, not a 64-bit constant compare
+          full = word == 0xffffffffu;
+        } else {
+          full = __builtin_amdgcn_readfirstlane(__all(jlim >= 32 * kb2 + 31) ? 1 : 0) != 0;
+        }
+        if (!full) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int key = kb2 * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+            const bool ok = SPARSE ? ((lanemask[kb2] >> (8 * (v >> 2) + (v & 3))) & 1) != 0 : key <= jlim;
+            sc[v] = ok ? sc[v] : -INFINITY;
+          }
+        }
+        hs.tmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+      } else if (u < 4) {
+        hs.tmax = fmaxf(fmaxf(hs.tmax, sc[4 * u]), fmaxf(sc[4 * u + 1], fmaxf(sc[4 * u + 2], sc[4 * u + 3])));
+      } else if (u == 4) {
+        hs.tmax = wave_max_pair(hs.tmax) * scale;  // scale > 0 keeps the max; -inf stays -inf
+      } else if (u == 5) {
+        hs.mnew = fmaxf(m, hs.tmax);
+        // A row that has seen no visible key yet holds O = 0 and l = 0:
+        // it adopts the new max for free.
+        if (m == -INFINITY) m = hs.mnew;
+      } else if (u == 6) {
+        hs.grow = hs.mnew > m + kRescaleThreshold;
+        hs.mo = m;
+        if (hs.grow) m = hs.mnew;
+      } else if (u == 7) {
+        hs.nmuse = (m == -INFINITY) ? 0.0f : -m;
+        hs.lh = 0.0f;
+      } else if (u == 8) {
+        // the row index is recomputed here rather than kept in a register
+        // (both lanes of a row pair hold the same maximum and write it)
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        mold_s[kb2][((tid >> 6) << 5) + (tid & 31)] = hs.mo;
+      } else if (u == 9) {
+        const bool any_grow = __ballot(hs.grow) != 0;
+        int tid = threadIdx.x;  // (address recomputed, not kept in a register)
+        asm volatile("" : "+v"(tid));
+        gflag[kb2][tid >> 6][tid & 63] = any_grow ? 1u : 0u;
+        hs.x = __builtin_fmaf(sc[0], scale, hs.nmuse);
+      } else if (u < 27) {
+        const int v = u - 10;  // 0..16
+        float e = 0.0f;
+        if (v < 16) e = __builtin_amdgcn_exp2f(hs.x);
+        if (v < 15) hs.x = __builtin_fmaf(sc[v + 1], scale, hs.nmuse);
+        if (v > 0) {
+          hs.lh += hs.e;
+          // keeps the add in this step: otherwise the compiler sinks all 16
+          // into one dependent chain at the row-sum update, with every
+          // probability held in a register until then
+          asm volatile("" : "+v"(hs.lh));
+          hs.pf[(v - 1) >> 3][(v - 1) & 7] = (__bf16)hs.e;
+        }
+        hs.e = e;
+      } else if (u < 29) {
+        const int sp = u - 27;
+        uint8_t* pb = kb2 == 0 ? pbuf : (FMT == 1 ? pbuf1 : ks + kRopeOffset);
+        *reinterpret_cast<bf16x8*>(pb + 2048 * wave + p_off[sp]) = hs.pf[sp];
+      }
+    };
+
+    // After the barrier that publishes a half: if any wave saw a row grow,
+    // every wave parks its outputs; then this lane's row sum takes the
+    // half's part.
+    auto settle = [&](int kb2, float mo, float lh) __attribute__((always_inline)) {
+      if ((gflag[kb2][0][0] | gflag[kb2][1][0] | gflag[kb2][2][0] | gflag[kb2][3][0]) != 0) flush(kb2, mo);
+      l += lh;
+    };
+
+    // O^T += V^T P^T for half kb2 of the tile in buffer vt, over this wave's
+    // 4 column blocks and the 4 row blocks: 8 groups g = (key step sp = g/4, column block cb = g%4)
+    // of 4 MFMAs, hook(j) after MFMA j (32 of them).  Within each 16-lane
+    // group, transpose read: lane j points at 4 consecutive columns of one
+    // key row (key j/4 of the group's 4) and lane i receives column i of
+    // those 4 keys.  k slot (h, e) <-> key 32*kb2 + 16*sp + 8*(e/4) + 4*h +
+    // e%4.  V^T operands rotate through kVAhead + 1 registers; the first
+    // kVAhead groups' operands are tile data and are read before the
+    // barrier that publishes the half's P^T (pv_prefetch).
+    auto load_v = [&](const uint8_t* vt, int kb2, int g) {
+      const int sp = g >> 2, cb = g & 3;
+      const uint8_t* vb = vt + 8192 * (2 * wave + (cb >> 1)) + 4096 * kb2 + 2048 * sp;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_ptr<i16x4>(vb + v_off[cb & 1][0]));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_ptr<i16x4>(vb + v_off[cb & 1][1]));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    constexpr int kVRegs = kVAhead + 1;
+    constexpr int kVPrefetchReads = 2 * kVAhead;  // LDS reads issued by pv_prefetch
+    auto pv_prefetch = [&](const uint8_t* vt, int kb2, bf16x8* vf) __attribute__((always_inline)) {
+#pragma unroll
+      for (int g = 0; g < kVAhead; ++g) vf[g] = load_v(vt, kb2, g);
+    };
+    auto pv_half = [&](int kb2, const uint8_t* vt, const uint8_t* pb, bf16x8* vf, auto&& pre,
+                       auto&& hook) __attribute__((always_inline)) {
+      auto load_p = [&](int sp, int rb) {
+        return *reinterpret_cast<const bf16x8*>(pb + 2048 * rb + p_off[sp]);
+      };
+      bf16x8 pfr[4];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) pfr[rb] = load_p(0, rb);
+      pre();  // runs while the first operands are in flight
+      static_for<0, 8>([&](auto g_c) __attribute__((always_inline)) {
+        constexpr int g = decltype(g_c)::value;
+        constexpr int cb = g & 3;
+        if constexpr (g + kVAhead < 8) vf[(g + kVAhead) % kVRegs] = load_v(vt, kb2, g + kVAhead);
+        static_for<0, 4>([&](auto rb_c) __attribute__((always_inline)) {
+          constexpr int rb = decltype(rb_c)::value;
+          o[cb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[g % kVRegs], pfr[rb], o[cb][rb], 0, 0, 0);
+          // the second key step's P^T block rb, right after its last use
+          if constexpr (g == 3) pfr[rb] = load_p(1, rb);
+          hook(std::integral_constant<int, 4 * g + rb>{});
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      });
+    };
+
+    // Dense bf16 tiles run one P*V half behind the scores, so that both
+    // softmax halves sit between P*V MFMAs (register-fed, with room for
+    // VALU work) rather than between score MFMAs (which wait on LDS):
+    //   B1 | scores 0 of kt (copies: rows 0..31 of kt+1)
+    //      | P*V 1 of kt-1 + softmax 0 of kt
+    //   B2 | scores 1 of kt (copies: RoPE group and rows 32..63 of kt+1)
+    //   B3 | P*V 0 of kt + softmax 1 of kt (its P^T into kt's RoPE group)
+    // The copies of rows 32..63 and of the RoPE group overwrite what P*V 1
+    // of kt-1 reads, so they wait for B2; they need to land only by B1 / B2
+    // of kt+1.
+    if constexpr (kPipelined) {
+      const __attribute__((address_space(4))) int32_t* bt_const =
+          (const __attribute__((address_space(4))) int32_t*)bt_row;  // scalar loads
+      float prev_mo = -INFINITY, prev_lh = 0.0f;  // softmax 1 of tile kt-1, for its P*V
+      bf16x8 vf[kVRegs];
+      for (int kt = kfirst; kt < kend; ++kt) {
+        const bool odd = ((kt - kfirst) & 1) != 0;
+        // 1. rows 0..31 (with their RoPE chunks) of tile kt have landed:
+        //    only the copies issued after that RoPE group may still be in
+        //    flight.  Every wave is done with P*V 0 of tile kt-1 (P^T half 0
+        //    and its maxima are free); softmax 1 of tile kt-1 is published.
+        MLA_WAIT_VMCNT(TileCopy<0>::kLateCopies);
+        MLA_BARRIER_NO_FENCE();
+        TileCopy<0> next;
+        const uint32_t next_buf = lds_addr(odd ? lds0 : lds1);
+        next.prepare_page(a.kv, pg_next, kt + 1, kt + 1 < kend ? L : 0, next_buf, wave, lane);
+        pg_next = bt_const[min(kt + 2, nb - 1)];  // for the next tile
+        ks = odd ? lds1 : lds0;
+        const uint8_t* kprev = odd ? lds0 : lds1;
+        jlim = min(63, tlim - kt * kPage);
+
+        HalfSoftmax hs0, hs1;
+        f32x16 sacc0, sacc1;
+        score_chain(sacc0, ks, k_off, qf, [&](auto st_c) __attribute__((always_inline)) {
+          next.template issue_split<0, decltype(st_c)::value>(lane);
+        });
+        if (kt > kfirst) {
+          pv_prefetch(kprev, 1, vf);
+          pv_half(1, kprev, kprev + kRopeOffset, vf, [&] { settle(1, prev_mo, prev_lh); },
+                  [&](auto j_c) __attribute__((always_inline)) {
+                    constexpr int j = decltype(j_c)::value;
+                    if constexpr (j < kSoftmaxSteps) softmax_step(0, sacc0, hs0, j);
+                  });
+        } else {
+          static_for<0, kSoftmaxSteps>([&](auto u_c) __attribute__((always_inline)) {
+            softmax_step(0, sacc0, hs0, decltype(u_c)::value);
+          });
+        }
+        // 2. half 0's P^T and maxima visible; the other buffer (tile kt-1)
+        //    is free; rows 32..63 of tile kt have landed (only the copies
+        //    issued during scores 0 may still be in flight)
+        MLA_WAIT_VMCNT(TileCopy<0>::kEarlyCopies);
+        MLA_BARRIER_NO_FENCE();
+        score_chain(sacc1, ks + 32 * 128, k_off, qf, [&](auto st_c) __attribute__((always_inline)) {
+          next.template issue_split<1, decltype(st_c)::value>(lane);
+        });
+        // 3. every wave is past the scores of tile kt: its RoPE chunk group
+        //    takes half 1's P^T
+        pv_prefetch(ks, 0, vf);
+        MLA_BARRIER_NO_FENCE_KEEP(kVPrefetchReads);
+        pv_half(0, ks, pbuf, vf, [&] { settle(0, hs0.mo, hs0.lh); },
+                [&](auto j_c) __attribute__((always_inline)) {
+                  constexpr int j = decltype(j_c)::value;
+                  if constexpr (j < kSoftmaxSteps) softmax_step(1, sacc1, hs1, j);
+                });
+        prev_mo = hs1.mo;
+        prev_lh = hs1.lh;
+      }
+      // P*V 1 of the last tile
+      pv_prefetch(ks, 1, vf);
+      MLA_BARRIER_NO_FENCE_KEEP(kVPrefetchReads);
+      pv_half(1, ks, ks + kRopeOffset, vf, [&] { settle(1, prev_mo, prev_lh); }, [](auto) {});
+    }
+
     // One tile: the copy of tile kt+1 and the row resolution of kt+2/kt+3
     // are issued, then tile kt is computed.  bf16 tiles alternate between
     // the two buffers, starting with lds0.
-    for (int kt = kfirst; kt < kend; ++kt) {
+    for (int kt = kfirst; kt < kend && !kPipelined; ++kt) {
       const bool odd = ((kt - kfirst) & 1) != 0;
       const bool has_next = __builtin_amdgcn_readfirstlane(kt + 1 < kend ? 1 : 0) != 0;
       // 1. tile kt has landed (this thread's copies, then everyone's); every
       //    wave is done with tile kt-1, its buffer and both P^T halves
       if constexpr (FMT == 0) MLA_WAIT_VMCNT(kResolveLoads);
       MLA_BARRIER_NO_FENCE();
-      const uint64_t vm = vm_cur;
+      vm = vm_cur;
       // Sparse: address of tile kt+2's page-table entry.  res_t was loaded
       // during the previous tile; using it here, where only that tile's two
       // resolve loads can still be in flight, keeps the wait the compiler
@@ -663,141 +934,10 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
         pg_next = bt_row[min(kt + 2, nb - 1)];  // for the next tile; a scalar load
       }
 
-      uint8_t* ks = (FMT == 0 && odd) ? lds1 : lds0;
-      uint32_t lanemask[2];  // sparse: visibility of keys 32*kb2 + 4*h + (0..31)
+      ks = (FMT == 0 && odd) ? lds1 : lds0;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) lanemask[kb2] = SPARSE ? (uint32_t)(vm >> (kb2 * 32 + 4 * h)) : 0u;
-      const int jlim = SPARSE ? 63 : min(63, tlim - kt * kPage);  // keys j <= jlim may count
-
-      // The softmax of half kb2 (raw scores in sc; scores in log2 units are
-      // scale * raw with scale > 0), cut into kSoftmaxSteps small steps of a
-      // few VALU instructions each.  One step goes between two MFMAs: an
-      // MFMA cannot issue while the matrix core is busy, and only the
-      // independent instructions that precede it in program order run in
-      // the shadow of the previous one.
-      //   0..3   mask the half if any of its keys is not visible (step 0),
-      //          max of the raw scores
-      //   4..9   row max across the lane pair, running max update, publish
-      //   10..25 probability of score u-10, row sum, bf16 operand
-      //   26, 27 store the half's P^T
-      auto softmax_step = [&](int kb2, f32x16& sc, HalfSoftmax& hs, int u) __attribute__((always_inline)) {
-        if (u == 0) {
-          // dense: visible keys are a prefix of the tile (tail and causal
-          // limits folded into jlim); sparse: the per-key validity mask
-          // (bit 8*(v/4) + v%4 of the lane's mask word is key
-          // 32*kb2 + 8*(v/4) + 4*h + v%4)
-          bool full;
-          if constexpr (SPARSE) {
-            uint32_t word = (uint32_t)(vm >> (32 * kb2));
-            asm volatile("" : "+s"(word));  // a 32-bit scalar test, not a 64-bit constant compare
-            full = word == 0xffffffffu;
-          } else {
-            full = __builtin_amdgcn_readfirstlane(__all(jlim >= 32 * kb2 + 31) ? 1 : 0) != 0;
-          }
-          if (!full) {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const int key = kb2 * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-              const bool ok = SPARSE ? ((lanemask[kb2] >> (8 * (v >> 2) + (v & 3))) & 1) != 0 : key <= jlim;
-              sc[v] = ok ? sc[v] : -INFINITY;
-            }
-          }
-          hs.tmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-        } else if (u < 4) {
-          hs.tmax = fmaxf(fmaxf(hs.tmax, sc[4 * u]), fmaxf(sc[4 * u + 1], fmaxf(sc[4 * u + 2], sc[4 * u + 3])));
-        } else if (u == 4) {
-          hs.tmax = wave_max_pair(hs.tmax) * scale;  // scale > 0 keeps the max; -inf stays -inf
-        } else if (u == 5) {
-          hs.mnew = fmaxf(m, hs.tmax);
-          // A row that has seen no visible key yet holds O = 0 and l = 0:
-          // it adopts the new max for free.
-          if (m == -INFINITY) m = hs.mnew;
-        } else if (u == 6) {
-          hs.grow = hs.mnew > m + kRescaleThreshold;
-          hs.mo = m;
-          if (hs.grow) m = hs.mnew;
-        } else if (u == 7) {
-          hs.nmuse = (m == -INFINITY) ? 0.0f : -m;
-          hs.lh = 0.0f;
-        } else if (u == 8) {
-          // the row index is recomputed here rather than kept in a register
-          int tid = threadIdx.x;
-          asm volatile("" : "+v"(tid));
-          if (h == 0) mold_s[kb2][((tid >> 6) << 5) + (tid & 31)] = hs.mo;
-        } else if (u == 9) {
-          const bool any_grow = __ballot(hs.grow) != 0;
-          int tid = threadIdx.x;  // (address recomputed, not kept in a register)
-          asm volatile("" : "+v"(tid));
-          if ((tid & 63) == 0) gflag[kb2][tid >> 6] = any_grow ? 1u : 0u;
-        } else if (u < 26) {
-          const int v = u - 10;
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[v], scale, hs.nmuse));
-          hs.lh += p;
-          // keeps the add in this step: otherwise the compiler sinks all 16
-          // into one dependent chain at the row-sum update, with every
-          // probability held in a register until then
-          asm volatile("" : "+v"(hs.lh));
-          hs.pf[v >> 3][v & 7] = (__bf16)p;
-        } else if (u < 28) {
-          const int sp = u - 26;
-          uint8_t* pb = kb2 == 0 ? pbuf : (FMT == 1 ? pbuf1 : ks + kRopeOffset);
-          *reinterpret_cast<bf16x8*>(pb + 2048 * wave + p_off[sp]) = hs.pf[sp];
-        }
-      };
-
-      // After the barrier that publishes a half: if any wave saw a row grow,
-      // every wave parks its outputs; then this lane's row sum takes the
-      // half's part.
-      auto settle = [&](int kb2, const HalfSoftmax& hs) __attribute__((always_inline)) {
-        const u32x4 g = *reinterpret_cast<const u32x4*>(gflag[kb2]);
-        if ((g[0] | g[1] | g[2] | g[3]) != 0) flush(kb2, hs.mo);
-        l += hs.lh;
-      };
-
-      // O^T += V^T P^T for half kb2 over this wave's 4 column blocks and the
-      // 4 row blocks: 8 groups g = (key step sp = g/4, column block cb = g%4)
-      // of 4 MFMAs, hook(j) after MFMA j (32 of them).  Within each 16-lane
-      // group, transpose read: lane j points at 4 consecutive columns of one
-      // key row (key j/4 of the group's 4) and lane i receives column i of
-      // those 4 keys.  k slot (h, e) <-> key 32*kb2 + 16*sp + 8*(e/4) + 4*h +
-      // e%4.  V^T operands rotate through kVAhead + 1 registers; the first
-      // kVAhead groups' operands are tile data and are read before the
-      // barrier that publishes the half's P^T (pv_prefetch).
-      auto load_v = [&](int kb2, int g) {
-        const int sp = g >> 2, cb = g & 3;
-        const uint8_t* vb = ks + 8192 * (2 * wave + (cb >> 1)) + 4096 * kb2 + 2048 * sp;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_ptr<i16x4>(vb + v_off[cb & 1][0]));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_ptr<i16x4>(vb + v_off[cb & 1][1]));
-        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      };
-      constexpr int kVRegs = kVAhead + 1;
-      constexpr int kVPrefetchReads = 2 * kVAhead;  // LDS reads issued by pv_prefetch
-      auto pv_prefetch = [&](int kb2, bf16x8* vf) __attribute__((always_inline)) {
-#pragma unroll
-        for (int g = 0; g < kVAhead; ++g) vf[g] = load_v(kb2, g);
-      };
-      auto pv_half = [&](int kb2, const uint8_t* pb, bf16x8* vf, auto&& pre, auto&& hook) __attribute__((always_inline)) {
-        auto load_p = [&](int sp, int rb) {
-          return *reinterpret_cast<const bf16x8*>(pb + 2048 * rb + p_off[sp]);
-        };
-        bf16x8 pfr[4];
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) pfr[rb] = load_p(0, rb);
-        pre();  // runs while the first operands are in flight
-        static_for<0, 8>([&](auto g_c) __attribute__((always_inline)) {
-          constexpr int g = decltype(g_c)::value;
-          constexpr int cb = g & 3;
-          if constexpr (g + kVAhead < 8) vf[(g + kVAhead) % kVRegs] = load_v(kb2, g + kVAhead);
-          static_for<0, 4>([&](auto rb_c) __attribute__((always_inline)) {
-            constexpr int rb = decltype(rb_c)::value;
-            o[cb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[g % kVRegs], pfr[rb], o[cb][rb], 0, 0, 0);
-            // the second key step's P^T block rb, right after its last use
-            if constexpr (g == 3) pfr[rb] = load_p(1, rb);
-            hook(std::integral_constant<int, 4 * g + rb>{});
-            __builtin_amdgcn_sched_barrier(0);
-          });
-        });
-      };
+      jlim = SPARSE ? 63 : min(63, tlim - kt * kPage);
 
       HalfSoftmax hs0, hs1;
       f32x16 sacc0, sacc1;
@@ -818,9 +958,9 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
       // 4. half 0's P^T and maxima visible; every wave is past the scores,
       //    so the RoPE chunk group is free for half 1's P^T
       bf16x8 vf[kVRegs];
-      pv_prefetch(0, vf);
+      pv_prefetch(ks, 0, vf);
       MLA_BARRIER_NO_FENCE_KEEP(kVPrefetchReads);
-      pv_half(0, pbuf, vf, [&] { settle(0, hs0); }, [&](auto j_c) __attribute__((always_inline)) {
+      pv_half(0, ks, pbuf, vf, [&] { settle(0, hs0.mo, hs0.lh); }, [&](auto j_c) __attribute__((always_inline)) {
         constexpr int j = decltype(j_c)::value;
         next.template issue_at<2, j>(lane);
         if constexpr (j < kSoftmaxSteps) softmax_step(1, sacc1, hs1, j);
@@ -845,17 +985,17 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
       // resolve loads may be newer), so after the barrier every staged row
       // is visible to the dequantisation below
       if constexpr (FMT == 1) MLA_WAIT_VMCNT(kResolveLoads);
-      pv_prefetch(1, vf);
+      pv_prefetch(ks, 1, vf);
       MLA_BARRIER_NO_FENCE_KEEP(kVPrefetchReads);  // half 1's P^T and maxima visible
       if constexpr (FMT == 0) {
-        pv_half(1, ks + kRopeOffset, vf, [&] { settle(1, hs1); }, [](auto) {});
+        pv_half(1, ks, ks + kRopeOffset, vf, [&] { settle(1, hs1.mo, hs1.lh); }, [](auto) {});
       } else {
         // rows 0..31 of tile kt are no longer read (half 0 is done): the
         // staged rows 0..31 of tile kt+1 are dequantised into them between
         // the MFMAs of half 1 (after a unit's last tile they are zero rows
         // written into a tile nothing reads any more)
         HalfDequant dq;
-        pv_half(1, pbuf1, vf, [&] { dq.load(lds1, 0); settle(1, hs1); },
+        pv_half(1, ks, pbuf1, vf, [&] { dq.load(lds1, 0); settle(1, hs1.mo, hs1.lh); },
                 [&](auto j_c) __attribute__((always_inline)) {
                   dq.template convert<decltype(j_c)::value>(ks);
                   if constexpr (decltype(j_c)::value == 24) dq.load_rope();
@@ -898,36 +1038,56 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
     if (h == 0) epi[rs] = f32x2{fc * inv, fa * inv};
     MLA_BARRIER_NO_FENCE();
     const bool direct = nsplit == 1;
+    // Output rows and columns come from the thread index again rather than
+    // from values kept through the tile loop: those come back as spill
+    // reloads, and a reload waits for every store issued before it.
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int ow = tid >> 6, on = tid & 31, oh = (tid >> 5) & 1;
+    const int64_t orow0 = direct ? (int64_t)u * s.rows : ((int64_t)a.num_splits[u] + seg) * s.rows;
+    auto store_rows = [&](auto direct_c, auto flushed_c) __attribute__((always_inline)) {
+      constexpr bool kDirect = decltype(direct_c)::value;
+      constexpr bool kFlushed = decltype(flushed_c)::value;
+      const float* recp = flush_rec();
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      const int ro = grp * kRowsPerGroup + 32 * rb + n;  // output row in unit
-      if (ro < s.rows) {
-        const f32x2 f = epi[32 * rb + n];
-        const int64_t row = (int64_t)u * s.rows + ro;
-        const int64_t wrow = direct ? 0 : ((int64_t)a.num_splits[u] + seg) * s.rows + ro;
-        uint16_t* orow16 = a.out + row * kDv + 128 * wave + 4 * h;
-        float* orow32 = a.ws_o + wrow * kDv + 128 * wave + 4 * h;
+      for (int rb = 0; rb < 4; ++rb) {
+        const int ro = grp * kRowsPerGroup + 32 * rb + on;  // output row in unit
+        if (ro < s.rows) {
+          const f32x2 f = epi[32 * rb + on];
+          // the row block's parked values, all loaded before any store
+          f32x4 fr[16];
+          if constexpr (kFlushed) {
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
+            for (int k = 0; k < 16; ++k)
+              fr[k] = *reinterpret_cast<const f32x4*>(recp + (4 * (k >> 2) + rb) * 16 + 4 * (k & 3));
+          }
+          const int64_t off = (orow0 + ro) * kDv + 128 * ow + 4 * oh;
 #pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const int col = 32 * cb + 8 * q4;  // + 128*wave + 4*h folded into the row pointers
-            f32x4 v = acc_quad(o[cb][rb], q4, oslot) * f[0];
-            if (flushed) {
-              const f32x4 fr = *reinterpret_cast<const f32x4*>(rec + (4 * cb + rb) * 16 + 4 * q4);
-              v += fr * f[1];
-            }
-            if (direct) {
-              const uint32_t w0 = (uint32_t)bf16_bits(v[0]) | ((uint32_t)bf16_bits(v[1]) << 16);
-              const uint32_t w1 = (uint32_t)bf16_bits(v[2]) | ((uint32_t)bf16_bits(v[3]) << 16);
-              *reinterpret_cast<uint2*>(orow16 + col) = make_uint2(w0, w1);
-            } else {
-              *reinterpret_cast<f32x4*>(orow32 + col) = v;
+          for (int cb = 0; cb < 4; ++cb) {
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              const int col = 32 * cb + 8 * q4;
+              f32x4 v = f32x4{o[cb][rb][4 * q4], o[cb][rb][4 * q4 + 1], o[cb][rb][4 * q4 + 2],
+                              o[cb][rb][4 * q4 + 3]} * f[0];
+              if constexpr (kFlushed) v += fr[4 * cb + q4] * f[1];
+              if constexpr (kDirect) {
+                const uint32_t w0 = (uint32_t)bf16_bits(v[0]) | ((uint32_t)bf16_bits(v[1]) << 16);
+                const uint32_t w1 = (uint32_t)bf16_bits(v[2]) | ((uint32_t)bf16_bits(v[3]) << 16);
+                *reinterpret_cast<uint2*>(a.out + off + col) = make_uint2(w0, w1);
+              } else {
+                *reinterpret_cast<f32x4*>(a.ws_o + off + col) = v;
+              }
             }
           }
-          __builtin_amdgcn_sched_barrier(0);
         }
       }
+    };
+    using True = std::integral_constant<bool, true>;
+    using False = std::integral_constant<bool, false>;
+    if (direct) {
+      if (flushed) store_rows(True{}, True{}); else store_rows(True{}, False{});
+    } else {
+      if (flushed) store_rows(False{}, True{}); else store_rows(False{}, False{});
     }
     if (row_ok && h == 0) {
       const int64_t row = (int64_t)u * s.rows + r;
