@@ -225,7 +225,7 @@ mla_status mla_decode_paged(const mla_problem* p, const void* q, const void* kv_
   a.num_parts = num_parts;
   const size_t slots = mla::ws_slots(num_parts, s.units);
   a.ws_lse = (float*)workspace;
-  a.ws_o = (float*)((char*)workspace + mla::ws_lse_bytes(slots, s.rows));
+  a.ws_o = (uint16_t*)((char*)workspace + mla::ws_lse_bytes(slots, s.rows));
   a.ws_flush = (float*)((char*)workspace + mla::ws_lse_bytes(slots, s.rows) + mla::ws_o_bytes(slots, s.rows));
   a.out = (uint16_t*)out;
   a.lse = lse;
@@ -274,7 +274,7 @@ mla_status mla_decode_combine(const mla_problem* p, int32_t num_parts, const int
   if (s.units == 0) return ok();
   const size_t slots = mla::ws_slots(num_parts, s.units);
   const float* ws_lse = (const float*)workspace;
-  const float* ws_o = (const float*)((const char*)workspace + mla::ws_lse_bytes(slots, s.rows));
+  const uint16_t* ws_o = (const uint16_t*)((const char*)workspace + mla::ws_lse_bytes(slots, s.rows));
   return hip_status(mla::launch_combine(s, num_splits, ws_lse, ws_o, (uint16_t*)out, lse,
                                         (hipStream_t)stream),
                     "combine kernel launch");

@@ -1,5 +1,5 @@
 // Combine: merges the split partial results of one query row.  Each split s
-// holds its normalised output O_s and lse_s (log2 units); with
+// holds its normalised output O_s (bf16) and lse_s (fp32, log2 units); with
 // M = max_s lse_s the merged row is
 //   lse = M + log2(sum_s 2^(lse_s - M)),   out = sum_s 2^(lse_s - lse) * O_s,
 // the online-softmax merge of results over disjoint key ranges ("Modular
@@ -14,7 +14,6 @@
 namespace mla {
 namespace {
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kRowsPerBlock = 4;
 
 __device__ inline uint16_t bf16_bits(float x) {
@@ -24,7 +23,7 @@ __device__ inline uint16_t bf16_bits(float x) {
 
 __global__ void __launch_bounds__(64 * kRowsPerBlock)
 combine_kernel(Shape s, const int32_t* __restrict__ num_splits, const float* __restrict__ ws_lse,
-               const float* __restrict__ ws_o, uint16_t* __restrict__ out,
+               const uint16_t* __restrict__ ws_o, uint16_t* __restrict__ out,
                float* __restrict__ lse) {
   const int u = blockIdx.y;
   const int r = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
@@ -46,12 +45,12 @@ combine_kernel(Shape s, const int32_t* __restrict__ num_splits, const float* __r
       const int64_t wrow = (int64_t)(first + sp) * s.rows + r;
       const float w = __builtin_amdgcn_exp2f(ws_lse[wrow] - M);
       tot += w;
-      const f32x4* src = reinterpret_cast<const f32x4*>(ws_o + wrow * kDv + lane * 8);
-      const f32x4 a0 = src[0], a1 = src[1];
+      const uint4 src = *reinterpret_cast<const uint4*>(ws_o + wrow * kDv + lane * 8);
+      const uint32_t words[4] = {src.x, src.y, src.z, src.w};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        acc[c] += w * a0[c];
-        acc[4 + c] += w * a1[c];
+      for (int c = 0; c < 4; ++c) {  // bf16 -> fp32 is exact: the high half of the word
+        acc[2 * c] += w * __uint_as_float(words[c] << 16);
+        acc[2 * c + 1] += w * __uint_as_float(words[c] & 0xffff0000u);
       }
     }
     const float inv = 1.0f / tot;
@@ -71,7 +70,7 @@ combine_kernel(Shape s, const int32_t* __restrict__ num_splits, const float* __r
 }  // namespace
 
 hipError_t launch_combine(const Shape& s, const int32_t* num_splits, const float* ws_lse,
-                          const float* ws_o, uint16_t* out, float* lse, hipStream_t stream) {
+                          const uint16_t* ws_o, uint16_t* out, float* lse, hipStream_t stream) {
   dim3 grid((s.rows + kRowsPerBlock - 1) / kRowsPerBlock, s.units);
   hipLaunchKernelGGL(combine_kernel, grid, dim3(64 * kRowsPerBlock), 0, stream, s, num_splits,
                      ws_lse, ws_o, out, lse);

@@ -1045,50 +1045,67 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
     asm volatile("" : "+v"(tid));
     const int ow = tid >> 6, on = tid & 31, oh = (tid >> 5) & 1;
     const int64_t orow0 = direct ? (int64_t)u * s.rows : ((int64_t)a.num_splits[u] + seg) * s.rows;
-    auto store_rows = [&](auto direct_c, auto flushed_c) __attribute__((always_inline)) {
-      constexpr bool kDirect = decltype(direct_c)::value;
+    // Rows go out through LDS so that each store writes one whole 1 KiB
+    // output row: per row block, every wave writes its 32 x 128 slice
+    // (normalised, bf16) into a staging area of the last tile's buffer (free
+    // after the barrier above; two areas in turn), then wave w stores rows
+    // 8w .. 8w+7 of the block.  16-byte chunk c of staged row r sits at chunk
+    // c ^ (r % 16), which spreads both the slice writes and the row reads
+    // over all banks.
+    uint16_t* const obase = direct ? a.out : a.ws_o;  // final rows or bf16 split partials
+    auto store_rows = [&](auto flushed_c) __attribute__((always_inline)) {
       constexpr bool kFlushed = decltype(flushed_c)::value;
       const float* recp = flush_rec();
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
-        const int ro = grp * kRowsPerGroup + 32 * rb + on;  // output row in unit
-        if (ro < s.rows) {
+        uint8_t* const stg = ks + 32768 * (rb & 1);
+        {
           const f32x2 f = epi[32 * rb + on];
-          // the row block's parked values, all loaded before any store
-          f32x4 fr[16];
+          f32x4 fr[16];  // the row block's parked values, loaded before use
           if constexpr (kFlushed) {
 #pragma unroll
             for (int k = 0; k < 16; ++k)
               fr[k] = *reinterpret_cast<const f32x4*>(recp + (4 * (k >> 2) + rb) * 16 + 4 * (k & 3));
           }
-          const int64_t off = (orow0 + ro) * kDv + 128 * ow + 4 * oh;
 #pragma unroll
           for (int cb = 0; cb < 4; ++cb) {
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
-              const int col = 32 * cb + 8 * q4;
               f32x4 v = f32x4{o[cb][rb][4 * q4], o[cb][rb][4 * q4 + 1], o[cb][rb][4 * q4 + 2],
                               o[cb][rb][4 * q4 + 3]} * f[0];
               if constexpr (kFlushed) v += fr[4 * cb + q4] * f[1];
-              if constexpr (kDirect) {
-                const uint32_t w0 = (uint32_t)bf16_bits(v[0]) | ((uint32_t)bf16_bits(v[1]) << 16);
-                const uint32_t w1 = (uint32_t)bf16_bits(v[2]) | ((uint32_t)bf16_bits(v[3]) << 16);
-                *reinterpret_cast<uint2*>(a.out + off + col) = make_uint2(w0, w1);
-              } else {
-                *reinterpret_cast<f32x4*>(a.ws_o + off + col) = v;
-              }
+              const uint32_t w0 = (uint32_t)bf16_bits(v[0]) | ((uint32_t)bf16_bits(v[1]) << 16);
+              const uint32_t w1 = (uint32_t)bf16_bits(v[2]) | ((uint32_t)bf16_bits(v[3]) << 16);
+              const int chunk = (16 * ow + 4 * cb + q4) ^ (on & 15);  // columns 128ow + 32cb + 8q4 ..
+              *reinterpret_cast<uint2*>(stg + on * 1024 + chunk * 16 + 8 * oh) = make_uint2(w0, w1);
             }
+          }
+        }
+        MLA_BARRIER_NO_FENCE();  // the block is staged; the other area is free again
+        const int ln = tid & 63;
+        const int ows = __builtin_amdgcn_readfirstlane(ow);  // wave-uniform row tests below
+        const int ro8 = grp * kRowsPerGroup + 32 * rb + 8 * ows;  // first output row in the unit
+        auto row_chunk = [&](int i) {
+          const int rr = 8 * ows + i;  // row in the block
+          return *reinterpret_cast<const uint4*>(stg + rr * 1024 + ((ln ^ (rr & 15)) * 16));
+        };
+        if (ro8 + 8 <= s.rows) {  // all 8 rows exist: every read before any store
+          uint4 rowv[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) rowv[i] = row_chunk(i);
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            *reinterpret_cast<uint4*>(obase + (orow0 + ro8 + i) * kDv + 8 * ln) = rowv[i];
+        } else {
+          for (int i = 0; i < 8 && ro8 + i < s.rows; ++i) {
+            const uint4 v = row_chunk(i);
+            *reinterpret_cast<uint4*>(obase + (orow0 + ro8 + i) * kDv + 8 * ln) = v;
           }
         }
       }
     };
-    using True = std::integral_constant<bool, true>;
-    using False = std::integral_constant<bool, false>;
-    if (direct) {
-      if (flushed) store_rows(True{}, True{}); else store_rows(True{}, False{});
-    } else {
-      if (flushed) store_rows(False{}, True{}); else store_rows(False{}, False{});
-    }
+    if (flushed) store_rows(std::integral_constant<bool, true>{});
+    else store_rows(std::integral_constant<bool, false>{});
     if (row_ok && h == 0) {
       const int64_t row = (int64_t)u * s.rows + r;
       if (direct)

@@ -34,14 +34,14 @@ struct DecodeArgs {
   const int32_t* num_splits;
   int32_t num_parts;
   float* ws_lse;  // [slots * R]
-  float* ws_o;    // [slots * R * 512]
+  uint16_t* ws_o;  // [slots * R * 512] bf16, normalised split outputs
   float* ws_flush;  // [num_parts * groups * 256 threads * kFlushFloats]
   uint16_t* out;
   float* lse;
 };
 
-// Workspace layout: split lse block, split output block (both for
-// num_parts + U slots of R rows), then one flush record per decode thread
+// Workspace layout: split lse block (fp32), split output block (bf16; both
+// for num_parts + U slots of R rows), then one flush record per decode thread
 // (num_parts * groups workgroups of 256 threads, kFlushFloats floats each:
 // 256 output values, 4 row maxima, a row sum and its maximum, padding).
 constexpr int kFlushFloats = 264;
@@ -51,7 +51,7 @@ inline size_t ws_lse_bytes(size_t slots, int32_t rows) {
   return align256(slots * (size_t)rows * sizeof(float));
 }
 inline size_t ws_o_bytes(size_t slots, int32_t rows) {
-  return align256(slots * (size_t)rows * kDv * sizeof(float));
+  return align256(slots * (size_t)rows * kDv * sizeof(uint16_t));
 }
 inline size_t ws_flush_bytes(int32_t num_parts, int32_t groups) {
   return (size_t)num_parts * (size_t)groups * 256 * kFlushFloats * sizeof(float);
@@ -65,6 +65,6 @@ hipError_t launch_metadata(const Shape& s, const int32_t* seqlens, int32_t num_p
                            int32_t* sched, int32_t* num_splits, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_combine(const Shape& s, const int32_t* num_splits, const float* ws_lse,
-                          const float* ws_o, uint16_t* out, float* lse, hipStream_t stream);
+                          const uint16_t* ws_o, uint16_t* out, float* lse, hipStream_t stream);
 
 }  // namespace mla
