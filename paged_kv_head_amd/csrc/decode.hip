@@ -400,23 +400,30 @@ __device__ inline void mfma_s_drain(f32x16& acc) {
 
 // S^T for 32 keys (rows of the tile at kb) against this lane's Q row, with
 // hook(integral_constant<st>) emitted after the MFMA of k-step st (independent VALU work that
-// runs while the matrix core is busy).  K operands are read kPrefetch steps
+// runs while the matrix core is busy).  K operands are read kKPrefetch steps
 // ahead of their MFMA so the LDS latency hides behind the chain.
-template <class Hook>
-__device__ inline __attribute__((always_inline)) void score_chain(f32x16& acc, const uint8_t* kb,
-                                                                  const int* k_off,
-                                                                  const bf16x8* qf, Hook&& hook) {
-  auto kload = [&](int st) {
-    return *reinterpret_cast<const bf16x8*>(kb + k_off[st & 3] + 8192 * (st >> 2));
-  };
-  constexpr int kPrefetch = 4;
-  bf16x8 kf[kPrefetch];
+constexpr int kKPrefetch = 4;
+struct KOperands {
+  bf16x8 kf[kKPrefetch];
+};
+__device__ inline bf16x8 k_operand(const uint8_t* kb, const int* k_off, int st) {
+  return *reinterpret_cast<const bf16x8*>(kb + k_off[st & 3] + 8192 * (st >> 2));
+}
+// The first kKPrefetch K operands of a chain (issued early, e.g. right after
+// the barrier that makes the tile visible).
+__device__ inline void score_chain_begin(KOperands& kp, const uint8_t* kb, const int* k_off) {
 #pragma unroll
-  for (int st = 0; st < kPrefetch; ++st) kf[st] = kload(st);
+  for (int st = 0; st < kKPrefetch; ++st) kp.kf[st] = k_operand(kb, k_off, st);
+}
+template <class Hook>
+__device__ inline __attribute__((always_inline)) void score_chain_run(f32x16& acc, KOperands& kp,
+                                                                      const uint8_t* kb,
+                                                                      const int* k_off,
+                                                                      const bf16x8* qf, Hook&& hook) {
   static_for<0, kQSteps>([&](auto st_c) __attribute__((always_inline)) {
     constexpr int st = decltype(st_c)::value;
-    const bf16x8 cur_k = kf[st % kPrefetch];
-    if constexpr (st + kPrefetch < kQSteps) kf[st % kPrefetch] = kload(st + kPrefetch);
+    const bf16x8 cur_k = kp.kf[st % kKPrefetch];
+    if constexpr (st + kKPrefetch < kQSteps) kp.kf[st % kKPrefetch] = k_operand(kb, k_off, st + kKPrefetch);
     if constexpr (st == 0)
       mfma_s_first(acc, cur_k, qf[st]);
     else
@@ -425,6 +432,14 @@ __device__ inline __attribute__((always_inline)) void score_chain(f32x16& acc, c
     __builtin_amdgcn_sched_barrier(0);
   });
   mfma_s_drain(acc);
+}
+template <class Hook>
+__device__ inline __attribute__((always_inline)) void score_chain(f32x16& acc, const uint8_t* kb,
+                                                                  const int* k_off,
+                                                                  const bf16x8* qf, Hook&& hook) {
+  KOperands kp;
+  score_chain_begin(kp, kb, k_off);
+  score_chain_run(acc, kp, kb, k_off, qf, hook);
 }
 
 // Four accumulator values of a lane, copied out through the lane's private
@@ -767,7 +782,12 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
       } else if (u < 29) {
         const int sp = u - 27;
         uint8_t* pb = kb2 == 0 ? pbuf : (FMT == 1 ? pbuf1 : ks + kRopeOffset);
-        *reinterpret_cast<bf16x8*>(pb + 2048 * wave + p_off[sp]) = hs.pf[sp];
+        // the address is recomputed from the thread index, not kept in a
+        // register through the tile loop
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const int pw = tid >> 6, pn = tid & 31, ph = (tid >> 5) & 1;
+        *reinterpret_cast<bf16x8*>(pb + 2048 * pw + p_chunk(pn, 2 * sp + ph)) = hs.pf[sp];
       }
     };
 
@@ -801,14 +821,20 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int g = 0; g < kVAhead; ++g) vf[g] = load_v(vt, kb2, g);
     };
-    auto pv_half = [&](int kb2, const uint8_t* vt, const uint8_t* pb, bf16x8* vf, auto&& pre,
-                       auto&& hook) __attribute__((always_inline)) {
-      auto load_p = [&](int sp, int rb) {
-        return *reinterpret_cast<const bf16x8*>(pb + 2048 * rb + p_off[sp]);
-      };
-      bf16x8 pfr[4];
+    auto load_p = [&](const uint8_t* pb, int sp, int rb) {
+      return *reinterpret_cast<const bf16x8*>(pb + 2048 * rb + p_off[sp]);
+    };
+    // Every first operand of a half: V^T as pv_prefetch, and the P^T blocks
+    // of the first key step (once the half's P^T is visible).
+    constexpr int kPVBeginReads = kVPrefetchReads + 4;
+    auto pv_begin = [&](const uint8_t* vt, int kb2, const uint8_t* pb, bf16x8* vf, bf16x8* pfr)
+        __attribute__((always_inline)) {
+      pv_prefetch(vt, kb2, vf);
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) pfr[rb] = load_p(0, rb);
+      for (int rb = 0; rb < 4; ++rb) pfr[rb] = load_p(pb, 0, rb);
+    };
+    auto pv_run = [&](int kb2, const uint8_t* vt, const uint8_t* pb, bf16x8* vf, bf16x8* pfr,
+                      auto&& pre, auto&& hook) __attribute__((always_inline)) {
       pre();  // runs while the first operands are in flight
       static_for<0, 8>([&](auto g_c) __attribute__((always_inline)) {
         constexpr int g = decltype(g_c)::value;
@@ -818,11 +844,18 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
           constexpr int rb = decltype(rb_c)::value;
           o[cb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[g % kVRegs], pfr[rb], o[cb][rb], 0, 0, 0);
           // the second key step's P^T block rb, right after its last use
-          if constexpr (g == 3) pfr[rb] = load_p(1, rb);
+          if constexpr (g == 3) pfr[rb] = load_p(pb, 1, rb);
           hook(std::integral_constant<int, 4 * g + rb>{});
           __builtin_amdgcn_sched_barrier(0);
         });
       });
+    };
+    auto pv_half = [&](int kb2, const uint8_t* vt, const uint8_t* pb, bf16x8* vf, auto&& pre,
+                       auto&& hook) __attribute__((always_inline)) {
+      bf16x8 pfr[4];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) pfr[rb] = load_p(pb, 0, rb);
+      pv_run(kb2, vt, pb, vf, pfr, pre, hook);
     };
 
     // Dense bf16 tiles run one P*V half behind the scores, so that both
@@ -848,26 +881,34 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
         //    and its maxima are free); softmax 1 of tile kt-1 is published.
         MLA_WAIT_VMCNT(TileCopy<0>::kLateCopies);
         MLA_BARRIER_NO_FENCE();
+        ks = odd ? lds1 : lds0;
+        const uint8_t* kprev = odd ? lds0 : lds1;
+        // the chain's first K reads go out before the copy address arithmetic
+        KOperands kp;
+        score_chain_begin(kp, ks, k_off);
         TileCopy<0> next;
         const uint32_t next_buf = lds_addr(odd ? lds0 : lds1);
         next.prepare_page(a.kv, pg_next, kt + 1, kt + 1 < kend ? L : 0, next_buf, wave, lane);
         pg_next = bt_const[min(kt + 2, nb - 1)];  // for the next tile
-        ks = odd ? lds1 : lds0;
-        const uint8_t* kprev = odd ? lds0 : lds1;
         jlim = min(63, tlim - kt * kPage);
 
         HalfSoftmax hs0, hs1;
         f32x16 sacc0, sacc1;
-        score_chain(sacc0, ks, k_off, qf, [&](auto st_c) __attribute__((always_inline)) {
-          next.template issue_split<0, decltype(st_c)::value>(lane);
+        bf16x8 pfr[4];
+        // P*V 1 of tile kt-1 reads operands published at B1: its first reads
+        // go out during the last MFMAs of the chain (for the first tile of
+        // a segment they read the idle buffer and are not used)
+        score_chain_run(sacc0, kp, ks, k_off, qf, [&](auto st_c) __attribute__((always_inline)) {
+          constexpr int st = decltype(st_c)::value;
+          next.template issue_split<0, st>(lane);
+          if constexpr (st == kQSteps - 3) pv_begin(kprev, 1, kprev + kRopeOffset, vf, pfr);
         });
         if (kt > kfirst) {
-          pv_prefetch(kprev, 1, vf);
-          pv_half(1, kprev, kprev + kRopeOffset, vf, [&] { settle(1, prev_mo, prev_lh); },
-                  [&](auto j_c) __attribute__((always_inline)) {
-                    constexpr int j = decltype(j_c)::value;
-                    if constexpr (j < kSoftmaxSteps) softmax_step(0, sacc0, hs0, j);
-                  });
+          pv_run(1, kprev, kprev + kRopeOffset, vf, pfr, [&] { settle(1, prev_mo, prev_lh); },
+                 [&](auto j_c) __attribute__((always_inline)) {
+                   constexpr int j = decltype(j_c)::value;
+                   if constexpr (j < kSoftmaxSteps) softmax_step(0, sacc0, hs0, j);
+                 });
         } else {
           static_for<0, kSoftmaxSteps>([&](auto u_c) __attribute__((always_inline)) {
             softmax_step(0, sacc0, hs0, decltype(u_c)::value);
@@ -882,10 +923,11 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
           next.template issue_split<1, decltype(st_c)::value>(lane);
         });
         // 3. every wave is past the scores of tile kt: its RoPE chunk group
-        //    takes half 1's P^T
-        pv_prefetch(ks, 0, vf);
-        MLA_BARRIER_NO_FENCE_KEEP(kVPrefetchReads);
-        pv_half(0, ks, pbuf, vf, [&] { settle(0, hs0.mo, hs0.lh); },
+        //    takes half 1's P^T.  (Half 0's P^T is visible since B2, so
+        //    all first operands are read before this barrier.)
+        pv_begin(ks, 0, pbuf, vf, pfr);
+        MLA_BARRIER_NO_FENCE_KEEP(kPVBeginReads);
+        pv_run(0, ks, pbuf, vf, pfr, [&] { settle(0, hs0.mo, hs0.lh); },
                 [&](auto j_c) __attribute__((always_inline)) {
                   constexpr int j = decltype(j_c)::value;
                   if constexpr (j < kSoftmaxSteps) softmax_step(1, sacc1, hs1, j);

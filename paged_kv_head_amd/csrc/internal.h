@@ -10,7 +10,8 @@ constexpr int kDqk = 576;
 constexpr int kDv = 512;
 constexpr int kPage = 64;          // tokens per page == keys per tile
 constexpr int kRowsPerGroup = 128; // query rows one workgroup owns
-constexpr int kSplitPenalty = 2;   // scheduler cost of one segment, in blocks
+constexpr int kSplitPenalty = 3;   // scheduler cost of one segment, in blocks (measured: a
+                                    // segment's prologue + epilogue ~ 3 tiles)
 constexpr int kMaxUnits = 16384;   // metadata kernel keeps per-unit arrays in LDS
 constexpr int kMaxParts = 65536;
 
