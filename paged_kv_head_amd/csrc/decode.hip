@@ -488,9 +488,10 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
   // second P*V half)
   __shared__ __attribute__((aligned(16))) uint8_t pbuf1[FMT == 1 ? kPHalfBytes : 16];
   __shared__ float mold_s[2][kRowsPerGroup];  // per row: running max before each half's update
-  // per half, wave and lane: some row of the wave grew (every lane writes
-  // the wave's value to its own word, so the write needs no branch)
-  __shared__ uint32_t gflag[2][4][64];
+  // per half, lane and wave: some row of the wave grew (every lane writes
+  // the wave's value to its own word, so the write needs no branch; the
+  // four waves' words of lane 0 are read as one 16-byte load)
+  __shared__ __attribute__((aligned(16))) uint32_t gflag[2][64][4];
   __shared__ f32x4 oslots[kThreads];  // per-lane slot for copying accumulators
   f32x4* const oslot = &oslots[threadIdx.x];
 
@@ -763,7 +764,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
         const bool any_grow = __ballot(hs.grow) != 0;
         int tid = threadIdx.x;  // (address recomputed, not kept in a register)
         asm volatile("" : "+v"(tid));
-        gflag[kb2][tid >> 6][tid & 63] = any_grow ? 1u : 0u;
+        gflag[kb2][tid & 63][tid >> 6] = any_grow ? 1u : 0u;
         hs.x = __builtin_fmaf(sc[0], scale, hs.nmuse);
       } else if (u < 27) {
         const int v = u - 10;  // 0..16
@@ -791,11 +792,18 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
       }
     };
 
-    // After the barrier that publishes a half: if any wave saw a row grow,
-    // every wave parks its outputs; then this lane's row sum takes the
-    // half's part.
-    auto settle = [&](int kb2, float mo, float lh) __attribute__((always_inline)) {
-      if ((gflag[kb2][0][0] | gflag[kb2][1][0] | gflag[kb2][2][0] | gflag[kb2][3][0]) != 0) flush(kb2, mo);
+    // Whether some row of the workgroup grew in half kb2 (readable once
+    // the barrier after that half's softmax has passed): the LDS words, and
+    // the wave-uniform answer.  Reading them well before the P*V half that
+    // depends on them keeps the LDS round trip off its start.
+    auto grew_word = [&](int kb2) -> u32x4 { return *reinterpret_cast<const u32x4*>(gflag[kb2][0]); };
+    auto grew_any = [&](u32x4 w) -> bool {
+      return __builtin_amdgcn_readfirstlane(w[0] | w[1] | w[2] | w[3]) != 0;
+    };
+    // Before the P*V of a half: if any wave saw a row grow, every wave
+    // parks its outputs; then this lane's row sum takes the half's part.
+    auto settle = [&](int kb2, float mo, float lh, bool grew) __attribute__((always_inline)) {
+      if (grew) flush(kb2, mo);
       l += lh;
     };
 
@@ -886,11 +894,15 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
         // the chain's first K reads go out before the copy address arithmetic
         KOperands kp;
         score_chain_begin(kp, ks, k_off);
+        __builtin_amdgcn_sched_barrier(0);
+        const u32x4 g1 = grew_word(1);  // softmax 1 of tile kt-1 (published by B1)
+        __builtin_amdgcn_sched_barrier(0);
         TileCopy<0> next;
         const uint32_t next_buf = lds_addr(odd ? lds0 : lds1);
         next.prepare_page(a.kv, pg_next, kt + 1, kt + 1 < kend ? L : 0, next_buf, wave, lane);
         pg_next = bt_const[min(kt + 2, nb - 1)];  // for the next tile
         jlim = min(63, tlim - kt * kPage);
+        const bool grew1 = grew_any(g1);
 
         HalfSoftmax hs0, hs1;
         f32x16 sacc0, sacc1;
@@ -904,7 +916,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
           if constexpr (st == kQSteps - 3) pv_begin(kprev, 1, kprev + kRopeOffset, vf, pfr);
         });
         if (kt > kfirst) {
-          pv_run(1, kprev, kprev + kRopeOffset, vf, pfr, [&] { settle(1, prev_mo, prev_lh); },
+          pv_run(1, kprev, kprev + kRopeOffset, vf, pfr, [&] { settle(1, prev_mo, prev_lh, grew1); },
                  [&](auto j_c) __attribute__((always_inline)) {
                    constexpr int j = decltype(j_c)::value;
                    if constexpr (j < kSoftmaxSteps) softmax_step(0, sacc0, hs0, j);
@@ -919,15 +931,20 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
         //    issued during scores 0 may still be in flight)
         MLA_WAIT_VMCNT(TileCopy<0>::kEarlyCopies);
         MLA_BARRIER_NO_FENCE();
+        const u32x4 g0 = grew_word(0);  // softmax 0 of tile kt (published by B2)
+        __builtin_amdgcn_sched_barrier(0);
+        bool grew0 = false;
         score_chain(sacc1, ks + 32 * 128, k_off, qf, [&](auto st_c) __attribute__((always_inline)) {
-          next.template issue_split<1, decltype(st_c)::value>(lane);
+          constexpr int st = decltype(st_c)::value;
+          next.template issue_split<1, st>(lane);
+          if constexpr (st == 6) grew0 = grew_any(g0);
         });
         // 3. every wave is past the scores of tile kt: its RoPE chunk group
         //    takes half 1's P^T.  (Half 0's P^T is visible since B2, so
         //    all first operands are read before this barrier.)
         pv_begin(ks, 0, pbuf, vf, pfr);
         MLA_BARRIER_NO_FENCE_KEEP(kPVBeginReads);
-        pv_run(0, ks, pbuf, vf, pfr, [&] { settle(0, hs0.mo, hs0.lh); },
+        pv_run(0, ks, pbuf, vf, pfr, [&] { settle(0, hs0.mo, hs0.lh, grew0); },
                 [&](auto j_c) __attribute__((always_inline)) {
                   constexpr int j = decltype(j_c)::value;
                   if constexpr (j < kSoftmaxSteps) softmax_step(1, sacc1, hs1, j);
@@ -938,7 +955,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
       // P*V 1 of the last tile
       pv_prefetch(ks, 1, vf);
       MLA_BARRIER_NO_FENCE_KEEP(kVPrefetchReads);
-      pv_half(1, ks, ks + kRopeOffset, vf, [&] { settle(1, prev_mo, prev_lh); }, [](auto) {});
+      pv_half(1, ks, ks + kRopeOffset, vf, [&] { settle(1, prev_mo, prev_lh, grew_any(grew_word(1))); }, [](auto) {});
     }
 
     // One tile: the copy of tile kt+1 and the row resolution of kt+2/kt+3
@@ -1002,7 +1019,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
       bf16x8 vf[kVRegs];
       pv_prefetch(ks, 0, vf);
       MLA_BARRIER_NO_FENCE_KEEP(kVPrefetchReads);
-      pv_half(0, ks, pbuf, vf, [&] { settle(0, hs0.mo, hs0.lh); }, [&](auto j_c) __attribute__((always_inline)) {
+      pv_half(0, ks, pbuf, vf, [&] { settle(0, hs0.mo, hs0.lh, grew_any(grew_word(0))); }, [&](auto j_c) __attribute__((always_inline)) {
         constexpr int j = decltype(j_c)::value;
         next.template issue_at<2, j>(lane);
         if constexpr (j < kSoftmaxSteps) softmax_step(1, sacc1, hs1, j);
@@ -1030,14 +1047,14 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
       pv_prefetch(ks, 1, vf);
       MLA_BARRIER_NO_FENCE_KEEP(kVPrefetchReads);  // half 1's P^T and maxima visible
       if constexpr (FMT == 0) {
-        pv_half(1, ks, ks + kRopeOffset, vf, [&] { settle(1, hs1.mo, hs1.lh); }, [](auto) {});
+        pv_half(1, ks, ks + kRopeOffset, vf, [&] { settle(1, hs1.mo, hs1.lh, grew_any(grew_word(1))); }, [](auto) {});
       } else {
         // rows 0..31 of tile kt are no longer read (half 0 is done): the
         // staged rows 0..31 of tile kt+1 are dequantised into them between
         // the MFMAs of half 1 (after a unit's last tile they are zero rows
         // written into a tile nothing reads any more)
         HalfDequant dq;
-        pv_half(1, ks, pbuf1, vf, [&] { dq.load(lds1, 0); settle(1, hs1.mo, hs1.lh); },
+        pv_half(1, ks, pbuf1, vf, [&] { dq.load(lds1, 0); settle(1, hs1.mo, hs1.lh, grew_any(grew_word(1))); },
                 [&](auto j_c) __attribute__((always_inline)) {
                   dq.template convert<decltype(j_c)::value>(ks);
                   if constexpr (decltype(j_c)::value == 24) dq.load_rope();
