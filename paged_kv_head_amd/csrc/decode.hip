@@ -220,10 +220,11 @@ struct TileCopy {
   // copies in flight at HBM latency, and a burst stalls instruction issue
   // until the first ones return.  bf16: 7 copies in each score chain (after
   // the MFMAs of steps 2, 7, .., 32) and 4 early in the first P*V half
-  // (after MFMAs 2, 7, 12, 17); FP8 (whose rows are dequantised from the
-  // second P*V half on): 6 in each score chain.  FP8
-  // issues copies 10 and 11 (the RoPE group, which needs the zero-row
-  // source) first, so that source is not held long.
+  // (after MFMAs 2, 7, 12, 17).  FP8: rows 0..31 of the stage (even
+  // copies) in the first score chain, rows 32..63 (odd copies) in the
+  // second, once the dequantisation of the current tile's rows 32..63 has
+  // read them; copies 10 and 11 (the RoPE group, which needs the zero-row
+  // source) go first, so that source is not held long.
   static constexpr int slot(int phase, int step) {
     if (FMT == 0) {
       if (step % 5 != 2) return -1;
@@ -231,7 +232,7 @@ struct TileCopy {
       return step / 5 < 4 ? 14 + step / 5 : -1;
     }
     if (phase == 2 || step % 6 != 2) return -1;
-    return (6 * phase + step / 6 + 10) % kCopies;
+    return (2 * (step / 6) + 10) % kCopies + phase;
   }
   // every copy is issued exactly once (phases: 36, 36 and 32 steps)
   static constexpr bool slots_cover_copies() {
@@ -642,8 +643,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
         MLA_WAIT_VMCNT(0);
         __syncthreads();
         HalfDequant dq;
-        dq.all(lds1, lds0, 0);
-        dq.all(lds1, lds0, 32);
+        dq.all(lds1, lds0, 0);  // rows 32..63 are dequantised during the first score chain
       }
     }
     // Everything loaded so far (Q, rows, the first tile) is needed before the
@@ -963,7 +963,6 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
     // the two buffers, starting with lds0.
     for (int kt = kfirst; kt < kend && !kPipelined; ++kt) {
       const bool odd = ((kt - kfirst) & 1) != 0;
-      const bool has_next = __builtin_amdgcn_readfirstlane(kt + 1 < kend ? 1 : 0) != 0;
       // 1. tile kt has landed (this thread's copies, then everyone's); every
       //    wave is done with tile kt-1, its buffer and both P^T halves
       if constexpr (FMT == 0) MLA_WAIT_VMCNT(kResolveLoads);
@@ -1005,9 +1004,23 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
       // kt+1" resolves to the zero row, so the copies fill the free buffer
       // with zeros, which nothing reads; the next unit starts with a barrier
       // that waits for them.  No branch keeps the chain's registers simple.
+      // FP8: rows 32..63 of tile kt are dequantised from the stage between
+      // the MFMAs of the first chain, which reads rows 0..31 only (they were
+      // dequantised during the previous tile's second P*V half)
+      HalfDequant dqh;
       score_chain(sacc0, ks, k_off, qf, [&](auto st_c) __attribute__((always_inline)) {
-        next.template issue_at<0, decltype(st_c)::value>(lane);
+        constexpr int st = decltype(st_c)::value;
+        next.template issue_at<0, st>(lane);
+        if constexpr (FMT == 1) {
+          if constexpr (st == 0) dqh.load(lds1, 32);
+          if constexpr (st >= 1 && st <= 32) dqh.template convert<st - 1>(ks);
+          if constexpr (st == 20) dqh.load_rope();
+          if constexpr (st == 34) dqh.store_rope(ks);
+        }
       });
+      // FP8: rows 32..63 of tile kt are in place; the stage rows they came
+      // from are free for the next tile's copies
+      if constexpr (FMT == 1) MLA_BARRIER_NO_FENCE();
       score_chain(sacc1, ks + 32 * 128, k_off, qf, [&](auto st_c) __attribute__((always_inline)) {
         constexpr int st = decltype(st_c)::value;
         next.template issue_at<1, st>(lane);
@@ -1067,13 +1080,6 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
         res_off = offset_of(res_t, pg2);
         asm volatile("s_waitcnt vmcnt(0)" : "+v"(t3) :: "memory");
         res_t = t3_ok ? t3 : -1;
-      }
-      if constexpr (FMT == 1) {
-        if (has_next) {
-          __syncthreads();  // rows 32..63 of tile kt consumed
-          HalfDequant dq;
-          dq.all(lds1, lds0, 32);
-        }
       }
     }
 
