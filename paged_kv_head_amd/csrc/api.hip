@@ -85,6 +85,7 @@ mla_status check_problem(const mla_problem* p, mla::Shape* s) {
   s->rows = (int32_t)rows;
   s->groups = (int32_t)((rows + mla::kRowsPerGroup - 1) / mla::kRowsPerGroup);
   s->scale_log2 = s->natural ? (float)((double)p->softmax_scale * 1.4426950408889634) : p->softmax_scale;
+  s->inv_h_q = 1.0f / (float)p->h_q;
   return MLA_OK;
 }
 

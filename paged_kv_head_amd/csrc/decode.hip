@@ -503,13 +503,25 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
   // Workgroup -> (part, row group).  Workgroups are dealt round-robin to
   // the 8 XCDs, so the row groups of one part get ids congruent mod 8 and
   // share that XCD's L2 for the tiles they both read.
+  // Every kernel argument is fetched in one round of scalar loads here,
+  // rather than in a chain of rounds along their first uses.
+  asm volatile("" ::"s"(a.q), "s"(a.kv), "s"(a.block_table), "s"(a.seqlens), "s"(a.indices),
+               "s"(a.sched), "s"(a.num_splits), "s"(a.num_parts), "s"(a.ws_lse), "s"(a.ws_o),
+               "s"(a.ws_flush), "s"(a.out), "s"(a.lse), "s"(s.units), "s"(s.rows), "s"(s.groups),
+               "s"(s.s_q), "s"(s.h_q), "s"(s.topk), "s"(s.max_pages), "s"(s.is_causal),
+               "s"(s.natural), "s"(s.scale_log2));
+  // The schedule, sequence lengths, split counts and (dense) block table
+  // are read-only here: scalar loads through the constant address space.
+  using cint32 = const __attribute__((address_space(4))) int32_t;
   const int wg = blockIdx.x;
   const int span = 8 * s.groups;
   const int part = (wg / span) * 8 + (wg % span) % 8;
   const int grp = (wg % span) / 8;
   if (part >= a.num_parts) return;
-  const int32_t* sc = a.sched + 8 * (size_t)part;
+  cint32* sc = (cint32*)(a.sched + 8 * (size_t)part);
   const int ub = sc[0], kb0 = sc[1], ue = sc[2], ke = sc[3], split0 = sc[4];
+  cint32* seqlens_c = (cint32*)a.seqlens;
+  cint32* splits_c = (cint32*)a.num_splits;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -552,39 +564,73 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
   for (int sp = 0; sp < 2; ++sp) p_off[sp] = p_chunk(n, 2 * sp + h);
 
   for (int u = ub; u < s.units && (u < ue || (u == ue && ke > 0)); ++u) {
+    // The previous segment is fully consumed (tiles, P^T, epilogue staging
+    // in LDS).  No memory fence: Q and the first tile load in parallel below.
+    MLA_BARRIER_NO_FENCE();
     const int b = SPARSE ? u / s.s_q : u;
-    const int L = a.seqlens[b];
-    const int nb = SPARSE ? (s.topk + kPage - 1) / kPage : (max(L, 0) + kPage - 1) / kPage;
+    const int32_t* bt_row = a.block_table + (int64_t)b * s.max_pages;
     const int kfirst = (u == ub) ? kb0 : 0;
-    const int kend = (u == ue) ? ke : nb;
-    if (kfirst >= kend) continue;
-    const int seg = (u == ub) ? split0 : 0;
-    const int nsplit = a.num_splits[u + 1] - a.num_splits[u];
-
-    // Q operand fragments of this lane's score row: dims 16*st + 8*h .. +8
+    // Q operand fragments of this lane's score row: dims 16*st + 8*h .. +8.
+    // Dense: issued first, in flight while the scalar loads below resolve
+    // the segment.  Sparse: issued after the first tile's copies, so that
+    // the waits of the row resolution do not wait for them.  (The row is
+    // recomputed from the thread index: a value kept through the previous
+    // segment would come back as a spill reload, whose wait would also
+    // wait for these loads.)
     bf16x8 qf[kQSteps];
-    {
-      const uint16_t* qrow = a.q + ((int64_t)u * s.rows + (row_ok ? r : 0)) * kDqk + 8 * h;
+    auto load_q = [&]() __attribute__((always_inline)) {
+      int tid = threadIdx.x;
+      asm volatile("" : "+v"(tid));
+      const int qr = grp * kRowsPerGroup + (tid >> 6) * 32 + (tid & 31);
+      const uint16_t* qrow =
+          a.q + ((int64_t)u * s.rows + (qr < s.rows ? qr : 0)) * kDqk + 8 * ((tid >> 5) & 1);
 #pragma unroll
       for (int st = 0; st < kQSteps; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(qrow + 16 * st);
-      // The kernel works with a positive score scale: scale * (q.k) equals
-      // |scale| * ((-q).k) for a negative scale (a sign flip of bf16 is
-      // exact) and 1 * (0.k) = 0 for a zero scale.
-      if (s.scale_log2 <= 0.0f) {
-        const uint32_t flip = s.scale_log2 < 0.0f ? 0x80008000u : 0u;
-        const uint32_t keep = s.scale_log2 < 0.0f ? 0xffffffffu : 0u;
-#pragma unroll
-        for (int st = 0; st < kQSteps; ++st) {
-          u32x4 w = __builtin_bit_cast(u32x4, qf[st]);
-          w = (w & keep) ^ flip;
-          qf[st] = __builtin_bit_cast(bf16x8, w);
-        }
-      }
+    };
+    if constexpr (!SPARSE) load_q();
+    // One round of scalar loads: the sequence length, the split counts and
+    // (dense) the first two pages of the segment, at in-range indices.
+    const int L = seqlens_c[b];
+    const int splits_u = splits_c[u], splits_u1 = splits_c[u + 1];
+    int pg_first = 0, pg_second = 0;
+    if constexpr (!SPARSE) {
+      cint32* btc = (cint32*)bt_row;
+      pg_first = btc[min(kfirst, s.max_pages - 1)];
+      pg_second = btc[min(kfirst + 1, s.max_pages - 1)];
     }
+    // all four waited for together, before the test below
+    asm volatile("" ::"s"(L), "s"(splits_u), "s"(splits_u1), "s"(pg_first), "s"(pg_second));
+    const int nb = SPARSE ? (s.topk + kPage - 1) / kPage : (max(L, 0) + kPage - 1) / kPage;
+    const int kend = (u == ue) ? ke : nb;
+    if (kfirst >= kend) {
+      // (uses the Q loads on this path too, so that they are not moved
+      // below the test, where they would wait for it)
+      if constexpr (!SPARSE) {
+      asm volatile("" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]), "v"(qf[5]),
+                   "v"(qf[6]), "v"(qf[7]), "v"(qf[8]), "v"(qf[9]), "v"(qf[10]), "v"(qf[11]),
+                   "v"(qf[12]), "v"(qf[13]), "v"(qf[14]), "v"(qf[15]), "v"(qf[16]), "v"(qf[17]));
+      asm volatile("" ::"v"(qf[18]), "v"(qf[19]), "v"(qf[20]), "v"(qf[21]), "v"(qf[22]),
+                   "v"(qf[23]), "v"(qf[24]), "v"(qf[25]), "v"(qf[26]), "v"(qf[27]), "v"(qf[28]),
+                   "v"(qf[29]), "v"(qf[30]), "v"(qf[31]), "v"(qf[32]), "v"(qf[33]), "v"(qf[34]),
+                   "v"(qf[35]));
+      }
+      continue;
+    }
+    const int seg = (u == ub) ? split0 : 0;
+    const int nsplit = splits_u1 - splits_u;
     const float scale = s.scale_log2 == 0.0f ? 1.0f : fabsf(s.scale_log2);  // > 0
-    // last visible position for this row (dense causal)
+    // last visible position for this row (dense causal; the row is
+    // recomputed from the thread index, as for Q above)
     int tlim = L - 1;
-    if (!SPARSE && s.is_causal) tlim = L - s.s_q + (r / s.h_q);
+    if (!SPARSE && s.is_causal) {
+      int tid = threadIdx.x;
+      asm volatile("" : "+v"(tid));
+      const int qr = grp * kRowsPerGroup + (tid >> 6) * 32 + (tid & 31);
+      // query position of the row = floor(qr / h_q), through the host's
+      // reciprocal: (qr + 0.5) / h_q lies at least 0.5 / h_q from an
+      // integer, far beyond the float rounding error for these sizes
+      tlim = L - s.s_q + (int)(((float)qr + 0.5f) * s.inv_h_q);
+    }
 
     float m = -INFINITY;  // running (possibly stale) max of the score row, log2 units
     float l = 0.0f;       // running sum of this lane's half of the keys
@@ -601,7 +647,6 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
     //   res_t:   logical position of key `lane` in tile kt+2
     //   res_off: cache byte offset of key `lane` in tile kt+1 (-1: masked)
     const int32_t* idx_row = SPARSE ? a.indices + (int64_t)u * s.topk : nullptr;
-    const int32_t* bt_row = a.block_table + (int64_t)b * s.max_pages;
     auto position = [&](int tile) -> int {  // logical key position, or -1
       const int k = tile * kPage + lane;
       if constexpr (SPARSE) {
@@ -623,7 +668,6 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
     bool t3_ok = false;  // sparse: tile kt+3's slot of this lane holds an index
     int64_t res_off = -1;
     uint64_t vm_cur = 0;  // keys of the current tile that are visible (sparse masking)
-    __syncthreads();  // the previous segment is fully consumed (tiles, P^T, epilogue slots)
     {
       TileCopy<FMT> first;
       if constexpr (SPARSE) {
@@ -635,10 +679,13 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
         vm_cur = __ballot(off0 >= 0);
         first.prepare(a.kv, off0, lds_addr(FMT == 0 ? lds0 : lds1), wave, lane);
       } else {
-        first.prepare_page(a.kv, bt_row[kfirst], kfirst, L, lds_addr(FMT == 0 ? lds0 : lds1), wave, lane);
-        pg_next = bt_row[min(kfirst + 1, nb - 1)];
+        // (past the segment's end the second page is not used: its rows
+        // are copied from the zero row)
+        first.prepare_page(a.kv, pg_first, kfirst, L, lds_addr(FMT == 0 ? lds0 : lds1), wave, lane);
+        pg_next = pg_second;
       }
       first.issue_all(lane);
+      if constexpr (SPARSE) load_q();
       if constexpr (FMT == 1) {
         MLA_WAIT_VMCNT(0);
         __syncthreads();
@@ -651,6 +698,19 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
     // placing its own waits for the Q loads inside the tile loop, where they
     // would stall on the next tile's copies that it cannot see.
     MLA_WAIT_VMCNT(0);
+    // The kernel works with a positive score scale: scale * (q.k) equals
+    // |scale| * ((-q).k) for a negative scale (a sign flip of bf16 is exact)
+    // and 1 * (0.k) = 0 for a zero scale.
+    if (s.scale_log2 <= 0.0f) {
+      const uint32_t flip = s.scale_log2 < 0.0f ? 0x80008000u : 0u;
+      const uint32_t keep = s.scale_log2 < 0.0f ? 0xffffffffu : 0u;
+#pragma unroll
+      for (int st = 0; st < kQSteps; ++st) {
+        u32x4 w = __builtin_bit_cast(u32x4, qf[st]);
+        w = (w & keep) ^ flip;
+        qf[st] = __builtin_bit_cast(bf16x8, w);
+      }
+    }
 
     // Park this lane's outputs (all 16 blocks) and its score row's sum in
     // the flush record and restart them from zero.  Two partial results

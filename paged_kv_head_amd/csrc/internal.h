@@ -22,6 +22,7 @@ struct Shape {
   int32_t rows;   // query rows per unit (R)
   int32_t groups; // ceil(R / 128)
   float scale_log2;  // exponent multiplier: softmax_scale, times log2(e) for base e
+  float inv_h_q;     // 1 / h_q (query position of a row without an integer division)
 };
 
 struct DecodeArgs {
