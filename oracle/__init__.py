@@ -51,6 +51,12 @@ def _load():
         lib.oracle_decode_row.argtypes = [P, I, P]
         lib.oracle_decode_row.restype = None
         lib.oracle_num_threads.restype = I
+        lib.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+        lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+        lib.oracle_quantize_row_fp8.argtypes = [P, P]
+        lib.oracle_quantize_row_fp8.restype = None
+        lib.oracle_kv_append_fp8.argtypes = [I, I, I, I, I, P, P, P, P]
+        lib.oracle_kv_append_fp8.restype = None
         _lib = lib
     return _lib
 
@@ -69,6 +75,36 @@ def e4m3_value(code: int) -> float:
 
 def bf16_round(x: float) -> int:
     return int(_load().oracle_bf16_round(x))
+
+
+def e4m3_encode(v: float) -> int:
+    """Nearest e4m3fn code (ties to even), saturated to +-448."""
+    return int(_load().oracle_e4m3_encode(v))
+
+
+def quantize_row_fp8(row_bf16: np.ndarray) -> np.ndarray:
+    """bf16 bit row [576] -> the 656-byte FP8 row."""
+    x = np.ascontiguousarray(row_bf16, dtype=np.uint16)
+    assert x.shape == (576,)
+    out = np.zeros(656, dtype=np.uint8)
+    _load().oracle_quantize_row_fp8(_ptr(x), _ptr(out))
+    return out
+
+
+def kv_append_fp8(kv_new: np.ndarray, start_pos: np.ndarray, block_table: np.ndarray,
+                  kv_pool: np.ndarray, page_size: int = 64) -> np.ndarray:
+    """Quantise kv_new (bf16 bits [B, n_new, 576]) into a copy of kv_pool
+    ([num_pages, page_size, 656] bytes) at positions start_pos[b] + j
+    through block_table [B, max_pages]; returns the new pool."""
+    kv_new = np.ascontiguousarray(kv_new, dtype=np.uint16)
+    B, n_new, d = kv_new.shape
+    assert d == 576
+    sp = np.ascontiguousarray(start_pos, dtype=np.int32)
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    pool = np.array(kv_pool, dtype=np.uint8, copy=True, order="C")
+    _load().oracle_kv_append_fp8(B, n_new, page_size, pool.shape[0], bt.shape[1], _ptr(kv_new),
+                                 _ptr(sp), _ptr(bt), _ptr(pool))
+    return pool
 
 
 def decode_row(row: np.ndarray, kv_format: int) -> np.ndarray:

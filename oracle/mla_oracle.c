@@ -9,7 +9,8 @@
  *  [FlashMLA] "为什么 FlashMLA 的解码内核能跑到 660 TFLOPS——内核里的 5 个关键设计"
  *      - "设计 2" (FP8 KV cache): 656-byte token = 512 e4m3 NoPE codes quantised per
  *        1x128 tile with four fp32 scales, then 64 bf16 RoPE values; dequantise
- *        to bf16 before any product.
+ *        to bf16 before any product.  The writer side (quantise, append by
+ *        block table) follows the same layout.
  *      - "上手示例" (usage): sparse semantics -- gather rows by index, scores
  *        P = (Q K^T) * sm_scale, lse = log2 of the sum of 2^P, weights
  *        2^(P - lse), output = weights times the gathered rows.
@@ -73,6 +74,69 @@ double oracle_e4m3_value(uint8_t c) {
     else
         v = ldexp(1.0 + (double)m / 8.0, e - 7);
     return sign ? -v : v;
+}
+
+/* Nearest e4m3fn code to v (ties to the code with an even mantissa LSB),
+ * saturated to +-448, sign from v's sign bit: a brute-force search over
+ * the 127 finite magnitudes, every one exact in double, so each distance
+ * is exact.  (FlashMLA page, "设计 2": codes are e4m3; the rounding rule is
+ * this library's reading: round to nearest even, as IEEE conversions do.) */
+uint8_t oracle_e4m3_encode(float v) {
+    const uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    const double a = fabs((double)v);
+    if (a >= 448.0) return sign | 0x7e;
+    int best = 0;
+    double best_d = a;
+    for (int c = 1; c <= 0x7e; ++c) {
+        const double d = fabs(oracle_e4m3_value((uint8_t)c) - a);
+        if (d < best_d || (d == best_d && (c & 1) == 0 && (best & 1) != 0)) {
+            best = c;
+            best_d = d;
+        }
+    }
+    return sign | (uint8_t)best;
+}
+
+/* One bf16 latent row (576 values) -> the 656-byte FP8 layout (FlashMLA
+ * page, "设计 2"): per 1x128 tile k of the 512 NoPE values, amax = max |x|,
+ * scale = amax / 448 as one float division (round to nearest even), code =
+ * e4m3(x / scale) with the quotient also one float division; amax = 0 gives
+ * scale 0 and all codes 0.  Bytes [0, 512) codes, [512, 528) the four
+ * scales (little endian), [528, 656) the 64 RoPE values copied as bf16. */
+void oracle_quantize_row_fp8(const uint16_t* x576, uint8_t* out656) {
+    for (int k = 0; k < 4; ++k) {
+        float amax = 0.0f;
+        for (int d = 128 * k; d < 128 * (k + 1); ++d) {
+            const float x = fabsf(bf16_value(x576[d]));
+            if (x > amax) amax = x;
+        }
+        const float scale = amax / 448.0f;
+        for (int d = 128 * k; d < 128 * (k + 1); ++d)
+            out656[d] = amax == 0.0f ? 0 : oracle_e4m3_encode(bf16_value(x576[d]) / scale);
+        memcpy(out656 + ORACLE_D_NOPE + 4 * k, &scale, 4);
+    }
+    memcpy(out656 + ORACLE_D_NOPE + 16, x576 + ORACLE_D_NOPE, 128);
+}
+
+/* Append n_new tokens per sequence to a paged FP8 cache: token j of
+ * sequence b (bf16 row kv_new[b][j]) goes to logical position
+ * t = start_pos[b] + j, i.e. slot t mod page_size of page
+ * block_table[b][t div page_size] (Modular page, section 四: divmod of the
+ * token index by the page size, then the block table).  Tokens whose page
+ * index or page entry is out of range are skipped; nothing else is
+ * written. */
+void oracle_kv_append_fp8(int batch, int n_new, int page_size, int num_pages, int max_pages,
+                          const uint16_t* kv_new, const int32_t* start_pos,
+                          const int32_t* block_table, uint8_t* kv_pool) {
+    for (int b = 0; b < batch; ++b)
+        for (int j = 0; j < n_new; ++j) {
+            const long t = (long)start_pos[b] + j;
+            if (t < 0 || t / page_size >= max_pages) continue;
+            const int page = block_table[(long)b * max_pages + t / page_size];
+            if (page < 0 || page >= num_pages) continue;
+            uint8_t* row = kv_pool + ((long)page * page_size + t % page_size) * ORACLE_ROW_FP8;
+            oracle_quantize_row_fp8(kv_new + ((long)b * n_new + j) * ORACLE_D_QK, row);
+        }
 }
 
 /* One cached latent row -> 576 values (bf16-exact, stored as float). */

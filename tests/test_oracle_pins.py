@@ -316,3 +316,98 @@ def test_page_figures_pin_layout_and_flop_model():
     with np.errstate(over="ignore"):
         assert np.isfinite(np.exp(np.float32(x - 1e-5), dtype=np.float32))
         assert np.isinf(np.exp(np.float32(x + 1e-4), dtype=np.float32))
+
+
+# ------------------------------------------------ FP8 writer (quantiser) ---
+
+def test_e4m3_encode_exact_codes_round_trip():
+    """Every finite code's value encodes back to that code (both signs)."""
+    for c in range(0x7F):
+        v = oracle.e4m3_value(c)
+        assert oracle.e4m3_encode(v) == c, hex(c)
+        assert oracle.e4m3_encode(-v) == (c | 0x80), hex(c)
+
+
+def test_e4m3_encode_midpoints_go_to_even_and_saturate():
+    """Halfway between neighbouring codes the even code wins; beyond 448 the
+    code saturates (e4m3fn has no infinity and 0x7F is NaN)."""
+    for c in range(0x7E):
+        lo, hi = oracle.e4m3_value(c), oracle.e4m3_value(c + 1)
+        mid = np.float32((lo + hi) / 2)
+        assert float(mid) == (lo + hi) / 2  # the midpoint is exact in float
+        want = c if c % 2 == 0 else c + 1
+        assert oracle.e4m3_encode(float(mid)) == want, hex(c)
+        # just off the midpoint rounds to the nearer code
+        assert oracle.e4m3_encode(float(np.nextafter(mid, np.float32(0)))) == c
+        assert oracle.e4m3_encode(float(np.nextafter(mid, np.float32(1e9)))) == c + 1
+    for v in (448.0, 449.0, 464.0, 500.0, 1e30):
+        assert oracle.e4m3_encode(v) == 0x7E and oracle.e4m3_encode(-v) == 0xFE
+
+
+def test_e4m3_encode_matches_torch_cast():
+    """Library pin: torch's float8_e4m3fn cast (round to nearest even) agrees
+    on random values across the whole range, subnormals included."""
+    rng = np.random.default_rng(7)
+    x = np.concatenate([rng.uniform(-448, 448, 20000), rng.uniform(-0.02, 0.02, 20000),
+                        np.ldexp(rng.uniform(-1, 1, 5000), rng.integers(-12, 9, 5000))]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.e4m3_encode(float(v)) for v in x], dtype=np.uint8)
+    assert np.array_equal(got, ref)
+
+
+def test_quantize_row_closed_form():
+    """Tile maxima 3.5, 0, 448 and 1e-3: scale = amax / 448; with amax = 3.5
+    the scale is exactly 2^-7, so a value x encodes as x * 128."""
+    row = np.zeros(576, dtype=np.float32)
+    row[0:128] = np.linspace(-3.5, 3.5, 128)
+    row[5] = 1.0
+    row[256:384] = np.linspace(-448, 448, 128)
+    row[384:512] = 1e-3
+    row[512:] = np.arange(64) - 32
+    bits = synth.bf16_bits_from_f32(row)
+    out = oracle.quantize_row_fp8(bits)
+    scales = out[512:528].view(np.float32)
+    x = synth.bf16_bits_to_f32(bits)
+    assert scales[0] == np.float32(np.abs(x[0:128]).max()) / np.float32(448.0) == np.float32(2.0 ** -7)
+    assert scales[1] == 0.0 and np.all(out[128:256] == 0)
+    assert scales[2] == np.float32(1.0)
+    assert out[5] == 0x70  # 1.0 * 128 = 2^7: exponent field 14, mantissa 0
+    assert out[256] == 0xFE and out[383] == 0x7E  # -448 and 448
+    assert np.array_equal(out[528:].view(np.uint16), bits[512:])  # RoPE copied
+
+
+def test_quantize_row_matches_input_generator():
+    """The input generator's encoding (numpy float32 divisions + torch's
+    cast) and the oracle's quantiser agree byte for byte."""
+    rng = np.random.default_rng(11)
+    rows = synth.bf16_bits_from_f32((rng.standard_normal((64, 576)) * rng.uniform(0.01, 100, (64, 1))).astype(np.float32))
+    rows[3, 0:128] = 0  # an all-zero tile
+    rows[4, 128:256] = 0x8000  # negative zeros
+    ref = synth.encode_fp8_rows(rows)
+    got = np.stack([oracle.quantize_row_fp8(r) for r in rows])
+    assert np.array_equal(got, ref)
+
+
+def test_kv_append_places_rows_through_block_table():
+    """Appended tokens land at slot t mod 64 of page block_table[b][t div 64];
+    decoding them through the block table gives the dequantised rows; every
+    other byte of the pool is untouched; out-of-range positions are skipped."""
+    rng = np.random.default_rng(3)
+    B, n_new, pages_per_seq = 3, 70, 4
+    num_pages = B * pages_per_seq + 2
+    perm = rng.permutation(num_pages)[:B * pages_per_seq].reshape(B, pages_per_seq).astype(np.int32)
+    start = np.array([0, 60, 250], dtype=np.int32)  # the last sequence runs past its 4 pages
+    new = synth.bf16_bits_from_f32(rng.standard_normal((B, n_new, 576)).astype(np.float32))
+    pool0 = rng.integers(0, 256, (num_pages, 64, 656), dtype=np.uint8)
+    pool = oracle.kv_append_fp8(new, start, perm, pool0)
+    written = np.zeros(pool.shape[:2], dtype=bool)
+    for b in range(B):
+        for j in range(n_new):
+            t = start[b] + j
+            if t // 64 >= pages_per_seq:
+                continue
+            page, slot = perm[b, t // 64], t % 64
+            written[page, slot] = True
+            assert np.array_equal(pool[page, slot], oracle.quantize_row_fp8(new[b, j]))
+    assert np.array_equal(pool[~written], pool0[~written])
+    assert written.sum() == 70 + 70 + (256 - 250)
