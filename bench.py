@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--num-parts", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-units", type=int, default=None)
+    ap.add_argument("--kernel", choices=["decode", "writer"], default="decode",
+                    help="decode: the decode step (default); writer: the FP8 KV writer filling "
+                         "128 sequences x 4096 new tokens")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run three 1 GiB device-to-device copies (reference for the HBM byte "
                          "counters under rocprofv3), print nothing else")
@@ -67,15 +70,15 @@ def copy_calibration():
     torch.cuda.synchronize()
 
 
-def traffic_record(config_name: str):
-    """HBM traffic of the decode kernel from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"decode_{config_name}_traffic.json")
+def traffic_record(config_name: str, source: str = "decode.hip", prefix: str = "decode"):
+    """HBM traffic of a kernel from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{prefix}_{config_name}_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = open(os.path.join(ROOT, "paged_kv_head_amd", "csrc", "decode.hip"), "rb").read()
-    if rec.get("decode_source_sha256") != hashlib.sha256(src).hexdigest():
+    src = open(os.path.join(ROOT, "paged_kv_head_amd", "csrc", source), "rb").read()
+    if rec.get("source_sha256", rec.get("decode_source_sha256")) != hashlib.sha256(src).hexdigest():
         return None
     return rec
 
@@ -109,6 +112,96 @@ def cpu_baseline(w, sample_units, min_seconds=10.0, max_reps=6):
                       f"{reps} pass(es), {secs:.1f} s on the host"}
 
 
+WRITER_WORKLOAD = dict(name="fp8_writer_fill_b128_n4096", batch=128, n_new=4096, seed=2024)
+
+
+def writer_cpu_baseline(w, n_tokens=20000, min_seconds=10.0, max_reps=6):
+    """The oracle's append (one thread) over a bounded sample of the fill's
+    tokens: the first n_tokens of sequence order."""
+    import oracle
+
+    B, n_new, _ = w.kv_new.shape
+    nb = max(1, min(B, n_tokens // n_new)) if n_tokens >= n_new else 1
+    nn = min(n_new, n_tokens)
+    sub_new = np.ascontiguousarray(w.kv_new[:nb, :nn])
+    secs, reps = 0.0, 0
+    while reps < max_reps and (reps == 0 or secs < min_seconds):
+        t = time.perf_counter()
+        oracle.kv_append_fp8(sub_new, w.start_pos[:nb], w.block_table[:nb], w.pool)
+        secs += time.perf_counter() - t
+        reps += 1
+    tok = nb * nn
+    return {"value": tok * 1808 * reps / secs / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{tok} of {B * n_new} tokens ({nb} sequences x {nn}) of {w.name}, "
+                      f"{reps} pass(es), {secs:.1f} s on one host thread (pool copy included)"}
+
+
+def bench_writer(args):
+    """FP8 KV writer: quantise 128 x 4096 new bf16 latent rows into the
+    656-byte paged layout.  Algorithmic bytes per token: 1152 read + 656
+    written, plus the block table (4 bytes per page) and start positions."""
+    import torch
+
+    import paged_kv_head_amd as mla
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    c = WRITER_WORKLOAD
+    t0 = time.time()
+    w = synth.make_append(c["name"], batch=c["batch"], n_new=c["n_new"],
+                          start_pos=[0] * c["batch"], seed=c["seed"])
+    print(f"[bench] workload {w.name}: generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    kv_new = torch.from_numpy(w.kv_new.view(np.int16)).to(dev).view(torch.bfloat16)
+    sp = torch.from_numpy(w.start_pos).to(dev)
+    bt = torch.from_numpy(w.block_table).to(dev)
+    pool = torch.from_numpy(w.pool).to(dev)
+    stream = torch.cuda.current_stream()
+    mla.mla_kv_quantize_fp8(kv_new, sp, bt, pool)  # checked call once
+    lib = mla._load()
+    P = ctypes.c_void_p
+    B, n_new = int(kv_new.shape[0]), int(kv_new.shape[1])
+    call = (B, n_new, 64, int(pool.shape[0]), int(bt.shape[1]), P(kv_new.data_ptr()),
+            P(sp.data_ptr()), P(bt.data_ptr()), P(pool.data_ptr()), P(stream.cuda_stream))
+    for _ in range(args.warmup):
+        lib.mla_kv_quantize_fp8(*call)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        rc = lib.mla_kv_quantize_fp8(*call)
+        evs[i][1].record(stream)
+        if rc:
+            raise RuntimeError(mla.mla_last_error())
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    k_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    ms_per_step = wall * 1e3 / args.steps
+    tokens = w.tokens
+    pages = int((w.block_table >= 0).sum())
+    alg_bytes = tokens * (1152 + 656) + 4 * pages + 4 * B
+    achieved = alg_bytes / (k_ms * 1e-3) / 1e9
+    tr = traffic_record(w.name, "kv_writer.hip", "kv_quantize_fp8")
+    cpu = None if args.no_cpu_baseline else writer_cpu_baseline(w)
+    line = {
+        "metric": "FP8 KV writer GB/s (bf16 576-value rows -> 656-byte paged FP8 rows), % of HBM roofline",
+        "value": alg_bytes / (ms_per_step * 1e-3) / 1e9, "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "n_new": n_new, "tokens": tokens,
+                   "num_pages": int(pool.shape[0]), "algorithmic_bytes_per_step": alg_bytes},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBPS,
+                     "traffic": None if tr is None else tr["hbm_bytes_per_launch"],
+                     "kernel": "kv_quantize_fp8_kernel", "kernel_ms": k_ms},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -119,6 +212,9 @@ def main():
               "the path shards by batch or by query head with no exchange, so N GPUs "
               "would run N independent copies of the one-GPU step.", file=sys.stderr)
         sys.exit(2)
+    if args.kernel == "writer":
+        bench_writer(args)
+        return
 
     import torch
 

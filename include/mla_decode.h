@@ -189,6 +189,33 @@ mla_status mla_decode_combine(const mla_problem* p, int32_t num_parts, const int
                               const void* workspace, size_t workspace_bytes, void* out,
                               float* lse, void* stream);
 
+/* FP8 KV writer: quantises new latent tokens into the 656-byte layout
+ * (MLA_KV_FP8_656) and stores each at its paged slot.
+ *   kv_new       bf16  [batch, n_new, 576]  (16-byte aligned; device)
+ *   start_pos    int32 [batch]  logical position of token 0 of each sequence
+ *   block_table  int32 [batch, max_pages_per_seq]
+ *   kv_pool      bytes [num_pages, 64, 656]  (16-byte aligned; written in place)
+ * Token j of sequence b goes to logical position t = start_pos[b] + j, i.e.
+ * slot t % 64 of page block_table[b][t / 64] ("Modular Platform 设计文档全景
+ * 导读", section 四: divmod of the token index by the page size, then the
+ * block table).  Per 1x128 tile k of the 512 NoPE values: amax = max |x|,
+ * scale_k = amax / 448 (fp32 division), code = e4m3fn(x / scale_k) (fp32
+ * division, nearest code with ties to even, saturated to +-448); a tile with
+ * amax = 0 gets scale 0 and code 0x00 throughout.  The 64 RoPE values are
+ * copied as bf16.  Layout source: the FlashMLA page above, section 设计 2
+ * (1x128-tile fp32 scales, e4m3 codes, bf16 RoPE); the rounding and the
+ * amax/448 scale are this library's reading of it.
+ * Inputs must be finite.  Tokens whose position is negative, whose page
+ * index t / 64 is >= max_pages_per_seq or whose block-table entry lies
+ * outside [0, num_pages) are skipped (not errors; device values are not
+ * checked on the host).  If two tokens map to the same slot, which one is
+ * stored is unspecified.  Only the addressed rows are written; the call
+ * neither allocates nor synchronises.  page_size must be 64. */
+mla_status mla_kv_quantize_fp8(int32_t batch, int32_t n_new, int32_t page_size,
+                               int32_t num_pages, int32_t max_pages_per_seq, const void* kv_new,
+                               const int32_t* start_pos, const int32_t* block_table,
+                               void* kv_pool, void* stream);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* mla_last_error(void);
 

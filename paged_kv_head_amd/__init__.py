@@ -20,7 +20,7 @@ __all__ = [
     "library_path", "mla_decode_num_units", "mla_decode_num_parts", "mla_decode_metadata_size",
     "mla_decode_workspace_bytes", "mla_decode_get_metadata", "mla_decode_paged",
     "mla_decode_paged_fp8", "mla_decode_sparse_fp8", "mla_decode_combine", "mla_last_error",
-    "mla_decode_with_kvcache",
+    "mla_decode_with_kvcache", "mla_kv_quantize_fp8",
 ]
 
 MLA_KV_BF16 = 0
@@ -94,9 +94,10 @@ def _load():
     lib.mla_decode_paged_fp8.argtypes = [PP, P, P, P, P, P, I32, P, P, SZ, P, P, P]
     lib.mla_decode_sparse_fp8.argtypes = [PP, P, P, P, P, P, P, I32, P, P, SZ, P, P, P]
     lib.mla_decode_combine.argtypes = [PP, I32, P, P, SZ, P, P, P]
+    lib.mla_kv_quantize_fp8.argtypes = [I32, I32, I32, I32, I32, P, P, P, P, P]
     for fn in ("mla_decode_num_parts", "mla_decode_metadata_size", "mla_decode_workspace_bytes",
                "mla_decode_get_metadata", "mla_decode_paged", "mla_decode_paged_fp8",
-               "mla_decode_sparse_fp8", "mla_decode_combine"):
+               "mla_decode_sparse_fp8", "mla_decode_combine", "mla_kv_quantize_fp8"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.mla_last_error.argtypes = []
     lib.mla_last_error.restype = ctypes.c_char_p
@@ -236,6 +237,27 @@ def mla_decode_combine(p: Problem, num_parts, num_splits, workspace, out, lse, s
     _check(_load().mla_decode_combine(
         ctypes.byref(p), int(num_parts), _ptr(num_splits), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def mla_kv_quantize_fp8(kv_new, start_pos, block_table, kv_pool, page_size: int = 64,
+                        stream=None):
+    """Quantise kv_new (bf16 [B, n_new, 576]) into the 656-byte FP8 rows of
+    kv_pool (uint8 [num_pages, page_size, 656], written in place) at logical
+    positions start_pos[b] + j through block_table (int32 [B, max_pages])."""
+    if kv_new.dim() != 3 or kv_new.shape[2] != 576:
+        raise ValueError(f"kv_new: shape {tuple(kv_new.shape)}, expected [B, n_new, 576]")
+    B, n_new, _ = kv_new.shape
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError(f"block_table: shape {tuple(block_table.shape)}, expected [{B}, max_pages]")
+    if kv_pool.dim() != 3 or kv_pool.shape[1] != page_size or kv_pool.shape[2] != 656:
+        raise ValueError(f"kv_pool: shape {tuple(kv_pool.shape)}, expected [num_pages, {page_size}, 656]")
+    _expect("kv_new", kv_new, torch.bfloat16, B * n_new * 576)
+    _expect("start_pos", start_pos, torch.int32, B)
+    _expect("block_table", block_table, torch.int32, block_table.numel())
+    _expect("kv_pool", kv_pool, torch.uint8, kv_pool.numel())
+    _check(_load().mla_kv_quantize_fp8(
+        int(B), int(n_new), int(page_size), int(kv_pool.shape[0]), int(block_table.shape[1]),
+        _ptr(kv_new), _ptr(start_pos), _ptr(block_table), _ptr(kv_pool), _stream(stream)))
 
 
 class DecodePlan:

@@ -281,6 +281,33 @@ mla_status mla_decode_combine(const mla_problem* p, int32_t num_parts, const int
                     "combine kernel launch");
 }
 
+mla_status mla_kv_quantize_fp8(int32_t batch, int32_t n_new, int32_t page_size,
+                               int32_t num_pages, int32_t max_pages_per_seq, const void* kv_new,
+                               const int32_t* start_pos, const int32_t* block_table,
+                               void* kv_pool, void* stream) {
+  if (batch < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "batch: must be >= 0 (got %d)", batch);
+  if (n_new < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "n_new: must be >= 0 (got %d)", n_new);
+  if (page_size != mla::kPage)
+    return fail(MLA_ERR_UNSUPPORTED, "page_size: must be 64 (got %d)", page_size);
+  if (num_pages < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "num_pages: must be >= 1 (got %d)", num_pages);
+  if (max_pages_per_seq < 1)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "max_pages_per_seq: must be >= 1 (got %d)", max_pages_per_seq);
+  if ((int64_t)batch * n_new > INT32_MAX)
+    return fail(MLA_ERR_UNSUPPORTED, "n_new: batch * n_new = %lld tokens exceed 2^31 - 1",
+                (long long)batch * n_new);
+  if ((int64_t)batch * max_pages_per_seq >= INT32_MAX)
+    return fail(MLA_ERR_UNSUPPORTED, "block_table: more than 2^31 entries");
+  MLA_CHECK(check_ptr(kv_new, "kv_new", 16));
+  MLA_CHECK(check_ptr(start_pos, "start_pos", 4));
+  MLA_CHECK(check_ptr(block_table, "block_table", 4));
+  MLA_CHECK(check_ptr(kv_pool, "kv_pool", 16));
+  if ((int64_t)batch * n_new == 0) return ok();
+  return hip_status(mla::launch_kv_quantize_fp8(batch, n_new, num_pages, max_pages_per_seq,
+                                                (const uint16_t*)kv_new, start_pos, block_table,
+                                                (uint8_t*)kv_pool, (hipStream_t)stream),
+                    "FP8 KV writer kernel launch");
+}
+
 const char* mla_last_error(void) { return g_err; }
 
 }  // extern "C"

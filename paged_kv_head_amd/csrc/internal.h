@@ -68,5 +68,9 @@ hipError_t launch_metadata(const Shape& s, const int32_t* seqlens, int32_t num_p
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_combine(const Shape& s, const int32_t* num_splits, const float* ws_lse,
                           const uint16_t* ws_o, uint16_t* out, float* lse, hipStream_t stream);
+hipError_t launch_kv_quantize_fp8(int32_t batch, int32_t n_new, int32_t num_pages,
+                                  int32_t max_pages, const uint16_t* kv_new,
+                                  const int32_t* start_pos, const int32_t* block_table,
+                                  uint8_t* kv_pool, hipStream_t stream);
 
 }  // namespace mla

@@ -262,3 +262,61 @@ def config_workload(n: int, batch: Optional[int] = None, seed: Optional[int] = N
     if isinstance(c["seqlens"], int):
         c["seqlens"] = [c["seqlens"]] * b
     return make_workload(seed=1000 + n if seed is None else seed, **c)
+
+
+@dataclasses.dataclass
+class AppendWorkload:
+    """Inputs of one FP8 KV append: new latent rows, their start positions,
+    a block table and the pool they are written into."""
+
+    name: str
+    kv_new: np.ndarray       # uint16 bf16 bits [B, n_new, 576]
+    start_pos: np.ndarray    # int32 [B]
+    block_table: np.ndarray  # int32 [B, max_pages]
+    pool: np.ndarray         # uint8 [num_pages, page_size, 656], initial contents
+
+    @property
+    def tokens(self) -> int:
+        return int(self.kv_new.shape[0] * self.kv_new.shape[1])
+
+
+def make_append(name: str, *, batch: int, n_new: int, start_pos, seed: int,
+                max_pages_per_seq: Optional[int] = None, page_size: int = 64,
+                slack: float = 0.1, value_scale=None, pool_fill: Optional[int] = 0xFF
+                ) -> AppendWorkload:
+    """Seeded append workload.  Draw order from PCG64(seed): start positions
+    (if given as a Uniform), page permutation (pool of ceil((1 + slack) * N)
+    pages for the N pages the appended positions reach, assigned row-major to
+    the block table, unused slots -1), then the new rows: standard normal
+    float32 times ``value_scale`` (a scalar or one factor per row drawn as
+    10^U[-3, 3] when ``value_scale == "mixed"``), rounded to bf16.  The
+    pool starts as ``pool_fill`` bytes (0xFF = NaN everywhere) or, with
+    ``pool_fill=None``, random bytes."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if isinstance(start_pos, Uniform):
+        sp = rng.integers(start_pos.lo, start_pos.hi, size=batch, endpoint=True).astype(np.int32)
+    else:
+        sp = np.asarray(list(start_pos), dtype=np.int32)
+        assert sp.shape == (batch,)
+    end_pages = [_ceil_div(max(0, int(s) + n_new), page_size) for s in sp]
+    width = max_pages_per_seq if max_pages_per_seq is not None else max(1, max(end_pages))
+    n_pages = [min(e, width) for e in end_pages]
+    need = int(sum(n_pages))
+    pool_pages = max(1, int(math.ceil((1.0 + slack) * need)))
+    perm = rng.permutation(pool_pages).astype(np.int32)
+    table = np.full((batch, width), -1, dtype=np.int32)
+    off = 0
+    for b in range(batch):
+        table[b, :n_pages[b]] = perm[off:off + n_pages[b]]
+        off += n_pages[b]
+    x = rng.standard_normal((batch, n_new, D_QK), dtype=np.float32)
+    if isinstance(value_scale, str) and value_scale == "mixed":
+        x *= (10.0 ** rng.uniform(-3, 3, (batch, n_new, 1))).astype(np.float32)
+    elif value_scale is not None:
+        x *= np.float32(value_scale)
+    kv_new = bf16_bits_from_f32(x)
+    if pool_fill is None:
+        pool = rng.integers(0, 256, (pool_pages, page_size, ROW_BYTES_FP8), dtype=np.uint8)
+    else:
+        pool = np.full((pool_pages, page_size, ROW_BYTES_FP8), pool_fill, dtype=np.uint8)
+    return AppendWorkload(name=name, kv_new=kv_new, start_pos=sp, block_table=table, pool=pool)

@@ -31,7 +31,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("mla_decode_get_metadata", "mla_decode_paged", "mla_decode_combine",
-                 "mla_decode_paged_fp8", "mla_decode_sparse_fp8", "mla_last_error"):
+                 "mla_decode_paged_fp8", "mla_decode_sparse_fp8", "mla_kv_quantize_fp8",
+                 "mla_last_error"):
         assert want in names
 
 
@@ -159,3 +160,36 @@ def test_combine_checks():
     assert lib.mla_decode_combine(ctypes.byref(p), 4, None, v, 1 << 40, v, v, None) == mla.MLA_ERR_INVALID_ARGUMENT
     assert "num_splits" in mla.mla_last_error()
     assert lib.mla_decode_combine(ctypes.byref(p), 4, v, v, 16, v, v, None) == mla.MLA_ERR_WORKSPACE_TOO_SMALL
+
+
+def call_writer(batch=2, n_new=3, page_size=64, num_pages=7, max_pages=5, kv_new=FAKE,
+                start_pos=FAKE, bt=FAKE, pool=FAKE):
+    lib = mla._load()
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.mla_kv_quantize_fp8(batch, n_new, page_size, num_pages, max_pages, v(kv_new),
+                                   v(start_pos), v(bt), v(pool), None)
+
+
+@pytest.mark.parametrize("kw, status, word", [
+    (dict(batch=-1), mla.MLA_ERR_INVALID_ARGUMENT, "batch"),
+    (dict(n_new=-2), mla.MLA_ERR_INVALID_ARGUMENT, "n_new"),
+    (dict(page_size=16), mla.MLA_ERR_UNSUPPORTED, "page_size"),
+    (dict(num_pages=0), mla.MLA_ERR_INVALID_ARGUMENT, "num_pages"),
+    (dict(max_pages=0), mla.MLA_ERR_INVALID_ARGUMENT, "max_pages_per_seq"),
+    (dict(batch=1 << 16, n_new=1 << 16), mla.MLA_ERR_UNSUPPORTED, "n_new"),
+    (dict(kv_new=None), mla.MLA_ERR_INVALID_ARGUMENT, "kv_new"),
+    (dict(kv_new=FAKE + 8), mla.MLA_ERR_INVALID_ARGUMENT, "kv_new"),
+    (dict(start_pos=None), mla.MLA_ERR_INVALID_ARGUMENT, "start_pos"),
+    (dict(bt=None), mla.MLA_ERR_INVALID_ARGUMENT, "block_table"),
+    (dict(pool=None), mla.MLA_ERR_INVALID_ARGUMENT, "kv_pool"),
+    (dict(pool=FAKE + 4), mla.MLA_ERR_INVALID_ARGUMENT, "kv_pool"),
+])
+def test_writer_rejects_bad_arguments(kw, status, word):
+    assert call_writer(**kw) == status
+    assert mla.mla_last_error().startswith(word)
+
+
+def test_writer_with_no_tokens_launches_nothing():
+    # zero tokens is a valid no-op: it must succeed without touching the GPU
+    assert call_writer(batch=0) == mla.MLA_OK
+    assert call_writer(n_new=0) == mla.MLA_OK
