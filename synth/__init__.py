@@ -320,3 +320,66 @@ def make_append(name: str, *, batch: int, n_new: int, start_pos, seed: int,
     else:
         pool = np.full((pool_pages, page_size, ROW_BYTES_FP8), pool_fill, dtype=np.uint8)
     return AppendWorkload(name=name, kv_new=kv_new, start_pos=sp, block_table=table, pool=pool)
+
+
+@dataclasses.dataclass
+class PrefillWorkload:
+    """Inputs of one sparse prefill: queries, a flat latent cache (no
+    batch dimension, no block table) and per-query index lists."""
+
+    name: str
+    q: np.ndarray        # uint16 bf16 bits [s_q, h_q, 576]
+    kv: np.ndarray       # uint8 [s_kv, row_bytes]
+    indices: np.ndarray  # int32 [s_q, topk]
+    kv_format: int
+    softmax_scale: float
+
+    @property
+    def s_q(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def h_q(self) -> int:
+        return int(self.q.shape[1])
+
+    @property
+    def s_kv(self) -> int:
+        return int(self.kv.shape[0])
+
+    @property
+    def topk(self) -> int:
+        return int(self.indices.shape[1])
+
+    def flops(self) -> int:
+        return 2 * self.h_q * self.s_q * self.topk * (D_QK + D_V)
+
+    def algorithmic_bytes(self) -> int:
+        row = ROW_BYTES_BF16 if self.kv_format == KV_BF16 else ROW_BYTES_FP8
+        rows = self.s_q * self.h_q
+        return (self.s_q * self.topk * (row + 4) + rows * D_QK * 2 + rows * D_V * 2 + rows * 4)
+
+
+def make_sparse_prefill(name: str, *, s_q: int, h_q: int, s_kv: int, topk: int, seed: int,
+                        kv_format: int = KV_BF16, invalid_frac: float = 0.0,
+                        softmax_scale: Optional[float] = None) -> PrefillWorkload:
+    """Seeded sparse prefill.  Draw order from PCG64(seed): Q [s_q, h_q, 576]
+    standard normal rounded to bf16; KV [s_kv, 576] standard normal rounded
+    to bf16 (FP8: encoded as in the decode workloads); per query token,
+    ``topk`` distinct positions uniform without replacement from
+    [0, s_kv); then, if ``invalid_frac`` > 0, that fraction of all entries
+    (uniform positions) replaced by -1."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = bf16_bits_from_f32(rng.standard_normal((s_q, h_q, D_QK), dtype=np.float32))
+    kv_bits = bf16_bits_from_f32(rng.standard_normal((s_kv, D_QK), dtype=np.float32))
+    kv = kv_bits.view(np.uint8).reshape(s_kv, ROW_BYTES_BF16) if kv_format == KV_BF16 \
+        else encode_fp8_rows(kv_bits)
+    assert topk <= s_kv
+    indices = np.empty((s_q, topk), dtype=np.int32)
+    for i in range(s_q):
+        indices[i] = rng.choice(s_kv, size=topk, replace=False).astype(np.int32)
+    if invalid_frac > 0:
+        hit = rng.random((s_q, topk)) < invalid_frac
+        indices[hit] = -1
+    scale = np.float32(1.0 / math.sqrt(D_QK)) if softmax_scale is None else np.float32(softmax_scale)
+    return PrefillWorkload(name=name, q=q, kv=np.ascontiguousarray(kv), indices=indices,
+                           kv_format=kv_format, softmax_scale=float(scale))
