@@ -45,9 +45,10 @@ def parse():
     ap.add_argument("--num-parts", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-units", type=int, default=None)
-    ap.add_argument("--kernel", choices=["decode", "writer"], default="decode",
+    ap.add_argument("--kernel", choices=["decode", "writer", "prefill"], default="decode",
                     help="decode: the decode step (default); writer: the FP8 KV writer filling "
-                         "128 sequences x 4096 new tokens")
+                         "128 sequences x 4096 new tokens; prefill: sparse prefill, 4096 query "
+                         "tokens x 128 heads over a 32768-row cache, topk 2048")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run three 1 GiB device-to-device copies (reference for the HBM byte "
                          "counters under rocprofv3), print nothing else")
@@ -202,6 +203,100 @@ def bench_writer(args):
     print(json.dumps(line), flush=True)
 
 
+PREFILL_WORKLOAD = dict(name="prefill_s4096_kv32768_topk2048", s_q=4096, h_q=128, s_kv=32768,
+                        topk=2048, seed=77)
+
+
+def prefill_cpu_baseline(w, n_tokens=640, min_seconds=10.0, max_reps=8):
+    """The prefill oracle (numpy fp64) on the first n_tokens query tokens."""
+    from oracle.sparse_prefill import sparse_prefill
+
+    n = min(n_tokens, w.s_q)
+    secs, reps = 0.0, 0
+    while reps < max_reps and (reps == 0 or secs < min_seconds):
+        t = time.perf_counter()
+        sparse_prefill(w.q[:n], w.kv, w.indices[:n], w.softmax_scale, w.kv_format)
+        secs += time.perf_counter() - t
+        reps += 1
+    flops = 2 * w.h_q * n * w.topk * (576 + 512) * reps
+    return {"value": flops / secs / 1e12, "unit": "TFLOPS", "cores": int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count(),
+            "kind": "oracle",
+            "sample": f"{n} of {w.s_q} query tokens (all {w.h_q} heads) of {w.name}, {reps} pass(es), "
+                      f"{secs:.1f} s on the host (numpy fp64; BLAS threads as the host allows)"}
+
+
+def bench_prefill(args):
+    """Sparse prefill: gather-attend of 4096 query tokens (128 heads each)
+    over their own 2048 rows of a flat 32768-row bf16 latent cache."""
+    import torch
+
+    import paged_kv_head_amd as mla
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    c = PREFILL_WORKLOAD
+    t0 = time.time()
+    w = synth.make_sparse_prefill(c["name"], s_q=c["s_q"], h_q=c["h_q"], s_kv=c["s_kv"],
+                                  topk=c["topk"], seed=c["seed"])
+    print(f"[bench] workload {w.name}: generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    q = torch.from_numpy(w.q.view(np.int16)).to(dev).view(torch.bfloat16)
+    kv = torch.from_numpy(w.kv).to(dev).view(torch.bfloat16)
+    idx = torch.from_numpy(w.indices).to(dev)
+    parts = mla.mla_sparse_prefill_num_parts(w.h_q, w.topk, 0, 0)
+    need = mla.mla_sparse_prefill_workspace_bytes(w.s_q, w.h_q, w.s_kv, w.topk, 0, parts)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    out = torch.empty((w.s_q, w.h_q, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.s_q, w.h_q), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    mla.mla_sparse_prefill(q, kv, idx, w.softmax_scale, num_parts=parts, workspace=ws, out=out,
+                           lse=lse)  # checked call once
+    lib = mla._load()
+    P = ctypes.c_void_p
+    call = (w.s_q, w.h_q, w.s_kv, w.topk, 0, 0, ctypes.c_float(w.softmax_scale), P(q.data_ptr()),
+            P(kv.data_ptr()), P(idx.data_ptr()), parts, P(ws.data_ptr()), ctypes.c_size_t(need),
+            P(out.data_ptr()), P(lse.data_ptr()), P(stream.cuda_stream))
+    warm = max(3, args.warmup // 20)
+    steps = max(5, args.steps // 10)
+    for _ in range(warm):
+        lib.mla_sparse_prefill(*call)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    t_start = time.perf_counter()
+    for i in range(steps):
+        evs[i][0].record(stream)
+        rc = lib.mla_sparse_prefill(*call)
+        evs[i][1].record(stream)
+        if rc:
+            raise RuntimeError(mla.mla_last_error())
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    call_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    ms_per_step = wall * 1e3 / steps
+    flops = w.flops()
+    alg_bytes = w.algorithmic_bytes()
+    achieved = flops / (call_ms * 1e-3) / 1e12
+    cpu = None if args.no_cpu_baseline else prefill_cpu_baseline(w)
+    line = {
+        "metric": "sparse MLA prefill TFLOPS (h_q=128, d_qk=576, d_v=512, topk=2048), % of roofline",
+        "value": flops / (ms_per_step * 1e-3) / 1e12, "unit": "TFLOPS", "n_gpus": 1, "steps": steps,
+        "warmup": warm, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "arithmetic_intensity": flops / alg_bytes,
+        "config": {"workload": w.name, "s_q": w.s_q, "h_q": w.h_q, "s_kv": w.s_kv, "topk": w.topk,
+                   "kv_format": "bf16", "num_parts": parts, "flops_per_step": flops,
+                   "algorithmic_bytes_per_step": alg_bytes},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "kernel": "mla_sparse_prefill call (identity table; per 2048-token chunk: "
+                               "metadata, decode_kernel, combine_kernel)",
+                     "kernel_ms": call_ms},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -214,6 +309,9 @@ def main():
         sys.exit(2)
     if args.kernel == "writer":
         bench_writer(args)
+        return
+    if args.kernel == "prefill":
+        bench_prefill(args)
         return
 
     import torch

@@ -216,6 +216,37 @@ mla_status mla_kv_quantize_fp8(int32_t batch, int32_t n_new, int32_t page_size,
                                const int32_t* start_pos, const int32_t* block_table,
                                void* kv_pool, void* stream);
 
+/* Sparse prefill.  Source: the FlashMLA page above, section 上手示例: the
+ * sparse prefill call takes q [s_q, h_q, 576], a flat latent cache
+ * kv [s_kv, 1, 576] (no batch dimension, no block table; one KV head) and
+ * indices [s_q, 1, topk]; per query token i it gathers the rows
+ * kv[indices[i][k]], scores P = scale * q.K, and returns
+ * lse = log2(sum 2^P) and out = sum 2^(P - lse) * K[0:512] (base e with
+ * MLA_FLAG_NATURAL_BASE).  Entries outside [0, s_kv) are skipped;
+ * duplicates count with multiplicity; an empty list gives lse = -inf and
+ * out = 0.
+ *   q        bf16  [s_q, h_q, 576]        (16-byte aligned; device)
+ *   kv       bytes [s_kv, row bytes]      (16-byte aligned; 1152 for
+ *            MLA_KV_BF16, 656 for MLA_KV_FP8_656)
+ *   indices  int32 [s_q, topk]
+ *   workspace >= mla_sparse_prefill_workspace_bytes (256-byte aligned)
+ *   out      bf16  [s_q, h_q, 512]        (16-byte aligned)
+ *   lse      float [s_q, h_q]
+ *   num_parts  split-KV parts per launch, in [1, 65536]; the value
+ *            mla_decode_num_parts gives for a batch-1 sparse problem with
+ *            the same h_q fills the GPU.
+ * It runs the sparse decode kernels (batch 1, one work unit per query
+ * token, chunks of at most 2048 query tokens) with an identity block table
+ * (page p = rows 64p..64p+63) that it writes into the workspace first.  All
+ * work is enqueued on `stream`; nothing is allocated. */
+mla_status mla_sparse_prefill_workspace_bytes(int32_t s_q, int32_t h_q, int32_t s_kv, int32_t topk,
+                                              int32_t kv_format, int32_t num_parts, size_t* bytes);
+mla_status mla_sparse_prefill(int32_t s_q, int32_t h_q, int32_t s_kv, int32_t topk,
+                              int32_t kv_format, int32_t flags, float softmax_scale,
+                              const void* q, const void* kv, const int32_t* indices,
+                              int32_t num_parts, void* workspace, size_t workspace_bytes,
+                              void* out, float* lse, void* stream);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* mla_last_error(void);
 

@@ -20,7 +20,8 @@ __all__ = [
     "library_path", "mla_decode_num_units", "mla_decode_num_parts", "mla_decode_metadata_size",
     "mla_decode_workspace_bytes", "mla_decode_get_metadata", "mla_decode_paged",
     "mla_decode_paged_fp8", "mla_decode_sparse_fp8", "mla_decode_combine", "mla_last_error",
-    "mla_decode_with_kvcache", "mla_kv_quantize_fp8",
+    "mla_decode_with_kvcache", "mla_kv_quantize_fp8", "mla_sparse_prefill_workspace_bytes",
+    "mla_sparse_prefill", "mla_sparse_prefill_num_parts",
 ]
 
 MLA_KV_BF16 = 0
@@ -95,9 +96,13 @@ def _load():
     lib.mla_decode_sparse_fp8.argtypes = [PP, P, P, P, P, P, P, I32, P, P, SZ, P, P, P]
     lib.mla_decode_combine.argtypes = [PP, I32, P, P, SZ, P, P, P]
     lib.mla_kv_quantize_fp8.argtypes = [I32, I32, I32, I32, I32, P, P, P, P, P]
+    lib.mla_sparse_prefill_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32, ctypes.POINTER(SZ)]
+    lib.mla_sparse_prefill.argtypes = [I32, I32, I32, I32, I32, I32, ctypes.c_float, P, P, P, I32, P,
+                                       SZ, P, P, P]
     for fn in ("mla_decode_num_parts", "mla_decode_metadata_size", "mla_decode_workspace_bytes",
                "mla_decode_get_metadata", "mla_decode_paged", "mla_decode_paged_fp8",
-               "mla_decode_sparse_fp8", "mla_decode_combine", "mla_kv_quantize_fp8"):
+               "mla_decode_sparse_fp8", "mla_decode_combine", "mla_kv_quantize_fp8",
+               "mla_sparse_prefill_workspace_bytes", "mla_sparse_prefill"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.mla_last_error.argtypes = []
     lib.mla_last_error.restype = ctypes.c_char_p
@@ -258,6 +263,61 @@ def mla_kv_quantize_fp8(kv_new, start_pos, block_table, kv_pool, page_size: int 
     _check(_load().mla_kv_quantize_fp8(
         int(B), int(n_new), int(page_size), int(kv_pool.shape[0]), int(block_table.shape[1]),
         _ptr(kv_new), _ptr(start_pos), _ptr(block_table), _ptr(kv_pool), _stream(stream)))
+
+
+def mla_sparse_prefill_num_parts(h_q: int, topk: int, kv_format: int = MLA_KV_BF16,
+                                 device: int = 0) -> int:
+    """Parts that fill the GPU for a sparse prefill with h_q heads."""
+    p = Problem.make(batch=1, s_q=1, h_q=h_q, num_pages=1, max_pages_per_seq=1, softmax_scale=1.0,
+                     topk=topk, kv_format=kv_format)
+    return mla_decode_num_parts(p, device)
+
+
+def mla_sparse_prefill_workspace_bytes(s_q, h_q, s_kv, topk, kv_format, num_parts) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_load().mla_sparse_prefill_workspace_bytes(int(s_q), int(h_q), int(s_kv), int(topk),
+                                                      int(kv_format), int(num_parts), ctypes.byref(n)))
+    return int(n.value)
+
+
+def mla_sparse_prefill(q, kv, indices, softmax_scale, *, kv_format=MLA_KV_BF16, natural_base=False,
+                       num_parts=None, workspace=None, out=None, lse=None, stream=None):
+    """Sparse prefill over a flat latent cache.  q bf16 [s_q, h_q, 576];
+    kv [s_kv, 576] bf16 or [s_kv, 656] uint8 (MLA_KV_FP8_656); indices int32
+    [s_q, topk].  Returns (out bf16 [s_q, h_q, 512], lse float32 [s_q, h_q])."""
+    if q.dim() != 3 or q.shape[2] != 576:
+        raise ValueError(f"q: shape {tuple(q.shape)}, expected [s_q, h_q, 576]")
+    s_q, h_q = int(q.shape[0]), int(q.shape[1])
+    if indices.dim() != 2 or indices.shape[0] != s_q:
+        raise ValueError(f"indices: shape {tuple(indices.shape)}, expected [{s_q}, topk]")
+    topk = int(indices.shape[1])
+    row_bytes = 1152 if kv_format == MLA_KV_BF16 else 656
+    kv_bytes = kv.numel() * kv.element_size()
+    if kv.dim() < 1 or kv_bytes % row_bytes or kv.shape[0] * row_bytes != kv_bytes:
+        raise ValueError(f"kv: shape {tuple(kv.shape)} is not [s_kv, {row_bytes} bytes]")
+    s_kv = int(kv.shape[0])
+    _expect("q", q, torch.bfloat16, s_q * h_q * 576)
+    _expect("kv", kv, None, s_kv * row_bytes)
+    _expect("indices", indices, torch.int32, s_q * topk)
+    if num_parts is None:
+        num_parts = mla_sparse_prefill_num_parts(h_q, topk, kv_format, q.device.index or 0)
+    need = mla_sparse_prefill_workspace_bytes(s_q, h_q, s_kv, topk, kv_format, num_parts)
+    if workspace is None:
+        workspace = torch.empty(max(256, need), dtype=torch.uint8, device=q.device)
+    if workspace.numel() and workspace.data_ptr() % 256:
+        raise ValueError("workspace: must be 256-byte aligned")
+    _expect("workspace", workspace, torch.uint8, need, at_least=True)
+    if out is None:
+        out = torch.empty((s_q, h_q, 512), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((s_q, h_q), dtype=torch.float32, device=q.device)
+    _expect("out", out, torch.bfloat16, s_q * h_q * 512)
+    _expect("lse", lse, torch.float32, s_q * h_q)
+    _check(_load().mla_sparse_prefill(
+        s_q, h_q, s_kv, topk, int(kv_format), MLA_FLAG_NATURAL_BASE if natural_base else 0,
+        float(softmax_scale), _ptr(q), _ptr(kv), _ptr(indices), int(num_parts), _ptr(workspace),
+        workspace.numel(), _ptr(out), _ptr(lse), _stream(stream)))
+    return out, lse
 
 
 class DecodePlan:

@@ -308,6 +308,105 @@ mla_status mla_kv_quantize_fp8(int32_t batch, int32_t n_new, int32_t page_size,
                     "FP8 KV writer kernel launch");
 }
 
+}  // extern "C"
+
+namespace {
+
+// Workspace of a sparse prefill: identity block table, the cache length,
+// metadata, then the decode workspace of one chunk (each part 256-aligned).
+struct PrefillLayout {
+  size_t table, seqlen, sched, num_splits, decode, total;
+  size_t decode_bytes;
+};
+
+mla_status prefill_problem(int32_t n, int32_t h_q, int32_t s_kv, int32_t topk, int32_t kv_format,
+                           int32_t flags, float softmax_scale, mla_problem* p) {
+  if (s_kv < 1 || s_kv > INT32_MAX - 63)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "s_kv: must be in [1, 2^31 - 64] (got %d)", s_kv);
+  if (topk < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "topk: must be >= 1 (got %d)", topk);
+  const int32_t pages = (int32_t)(((int64_t)s_kv + 63) / 64);
+  *p = mla_problem{1, n < 1 ? 1 : n, h_q, 1, mla::kDqk, mla::kDv, mla::kPage, pages, pages,
+                   topk, kv_format, 0, flags, softmax_scale};
+  mla::Shape s;
+  return check_problem(p, &s);
+}
+
+mla_status prefill_layout(int32_t s_q, int32_t h_q, int32_t s_kv, int32_t topk, int32_t kv_format,
+                          int32_t flags, float softmax_scale, int32_t num_parts, PrefillLayout* L) {
+  if (s_q < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "s_q: must be >= 0 (got %d)", s_q);
+  const int32_t chunk = s_q < mla::kPrefillChunk ? s_q : mla::kPrefillChunk;
+  mla_problem p;
+  MLA_CHECK(prefill_problem(chunk, h_q, s_kv, topk, kv_format, flags, softmax_scale, &p));
+  MLA_CHECK(check_parts(num_parts));
+  size_t sched_ints = 0, splits_ints = 0, ws = 0;
+  MLA_CHECK(mla_decode_metadata_size(&p, num_parts, &sched_ints, &splits_ints));
+  MLA_CHECK(mla_decode_workspace_bytes(&p, num_parts, &ws));
+  L->table = 0;
+  L->seqlen = mla::align256(L->table + (size_t)p.num_pages * 4);
+  L->sched = L->seqlen + 256;
+  L->num_splits = mla::align256(L->sched + sched_ints * 4);
+  L->decode = mla::align256(L->num_splits + splits_ints * 4);
+  L->decode_bytes = ws;
+  L->total = L->decode + ws;
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status mla_sparse_prefill_workspace_bytes(int32_t s_q, int32_t h_q, int32_t s_kv, int32_t topk,
+                                              int32_t kv_format, int32_t num_parts, size_t* bytes) {
+  if (!bytes) return fail(MLA_ERR_INVALID_ARGUMENT, "bytes: NULL pointer");
+  PrefillLayout L;
+  MLA_CHECK(prefill_layout(s_q, h_q, s_kv, topk, kv_format, 0, 1.0f, num_parts, &L));
+  *bytes = L.total;
+  return ok();
+}
+
+mla_status mla_sparse_prefill(int32_t s_q, int32_t h_q, int32_t s_kv, int32_t topk,
+                              int32_t kv_format, int32_t flags, float softmax_scale,
+                              const void* q, const void* kv, const int32_t* indices,
+                              int32_t num_parts, void* workspace, size_t workspace_bytes,
+                              void* out, float* lse, void* stream) {
+  PrefillLayout L;
+  MLA_CHECK(prefill_layout(s_q, h_q, s_kv, topk, kv_format, flags, softmax_scale, num_parts, &L));
+  if (s_q == 0) return ok();  // nothing to read or write; empty tensors may have NULL data
+  MLA_CHECK(check_ptr(q, "q", 16));
+  MLA_CHECK(check_ptr(kv, "kv", 16));
+  MLA_CHECK(check_ptr(indices, "indices", 4));
+  MLA_CHECK(check_ptr(workspace, "workspace", 256));
+  MLA_CHECK(check_ptr(out, "out", 16));
+  MLA_CHECK(check_ptr(lse, "lse", 4));
+  if (workspace_bytes < L.total)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes: %zu given, %zu needed", workspace_bytes, L.total);
+  char* ws = (char*)workspace;
+  int32_t* table = (int32_t*)(ws + L.table);
+  int32_t* seqlen = (int32_t*)(ws + L.seqlen);
+  int32_t* sched = (int32_t*)(ws + L.sched);
+  int32_t* num_splits = (int32_t*)(ws + L.num_splits);
+  hipStream_t st = (hipStream_t)stream;
+  const int32_t pages = (int32_t)(((int64_t)s_kv + 63) / 64);
+  MLA_CHECK(hip_status(mla::launch_identity_table(table, pages, seqlen, s_kv, st),
+                       "identity table kernel launch"));
+  for (int32_t c0 = 0; c0 < s_q; c0 += mla::kPrefillChunk) {
+    const int32_t n = s_q - c0 < mla::kPrefillChunk ? s_q - c0 : mla::kPrefillChunk;
+    mla_problem p;
+    MLA_CHECK(prefill_problem(n, h_q, s_kv, topk, kv_format, flags, softmax_scale, &p));
+    const int64_t row0 = (int64_t)c0 * h_q;
+    const uint16_t* qc = (const uint16_t*)q + row0 * mla::kDqk;
+    const int32_t* ic = indices + (int64_t)c0 * topk;
+    uint16_t* oc = (uint16_t*)out + row0 * mla::kDv;
+    float* lc = lse + row0;
+    MLA_CHECK(mla_decode_get_metadata(&p, seqlen, num_parts, sched, num_splits, stream));
+    MLA_CHECK(mla_decode_paged(&p, qc, kv, table, seqlen, ic, sched, num_parts, num_splits,
+                               ws + L.decode, L.decode_bytes, oc, lc, stream));
+    MLA_CHECK(mla_decode_combine(&p, num_parts, num_splits, ws + L.decode, L.decode_bytes, oc, lc,
+                                 stream));
+  }
+  return ok();
+}
+
 const char* mla_last_error(void) { return g_err; }
 
 }  // extern "C"

@@ -354,9 +354,15 @@ class PrefillWorkload:
         return 2 * self.h_q * self.s_q * self.topk * (D_QK + D_V)
 
     def algorithmic_bytes(self) -> int:
+        """Bytes the method must move at least once: every distinct cache row
+        some query lists, the index lists, Q, out and lse.  Rows listed by
+        several queries are counted once (they can be served from cache)."""
         row = ROW_BYTES_BF16 if self.kv_format == KV_BF16 else ROW_BYTES_FP8
+        valid = self.indices[(self.indices >= 0) & (self.indices < self.s_kv)]
+        distinct = int(np.unique(valid).size)
         rows = self.s_q * self.h_q
-        return (self.s_q * self.topk * (row + 4) + rows * D_QK * 2 + rows * D_V * 2 + rows * 4)
+        return (distinct * row + self.indices.size * 4 + rows * D_QK * 2 + rows * D_V * 2
+                + rows * 4)
 
 
 def make_sparse_prefill(name: str, *, s_q: int, h_q: int, s_kv: int, topk: int, seed: int,

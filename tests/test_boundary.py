@@ -193,3 +193,41 @@ def test_writer_with_no_tokens_launches_nothing():
     # zero tokens is a valid no-op: it must succeed without touching the GPU
     assert call_writer(batch=0) == mla.MLA_OK
     assert call_writer(n_new=0) == mla.MLA_OK
+
+
+def call_prefill(s_q=4, h_q=16, s_kv=100, topk=8, fmt=0, flags=0, scale=0.5, q=FAKE, kv=FAKE,
+                 idx=FAKE, parts=4, ws=FAKE, ws_bytes=1 << 40, out=FAKE, lse=FAKE):
+    lib = mla._load()
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.mla_sparse_prefill(s_q, h_q, s_kv, topk, fmt, flags, scale, v(q), v(kv), v(idx),
+                                  parts, v(ws), ws_bytes, v(out), v(lse), None)
+
+
+@pytest.mark.parametrize("kw, status, word", [
+    (dict(s_q=-1), mla.MLA_ERR_INVALID_ARGUMENT, "s_q"),
+    (dict(h_q=0), mla.MLA_ERR_INVALID_ARGUMENT, "h_q"),
+    (dict(s_kv=0), mla.MLA_ERR_INVALID_ARGUMENT, "s_kv"),
+    (dict(topk=0), mla.MLA_ERR_INVALID_ARGUMENT, "topk"),
+    (dict(fmt=7), mla.MLA_ERR_INVALID_ARGUMENT, "kv_format"),
+    (dict(flags=4), mla.MLA_ERR_INVALID_ARGUMENT, "flags"),
+    (dict(scale=float("nan")), mla.MLA_ERR_INVALID_ARGUMENT, "softmax_scale"),
+    (dict(parts=0), mla.MLA_ERR_INVALID_ARGUMENT, "num_parts"),
+    (dict(q=None), mla.MLA_ERR_INVALID_ARGUMENT, "q"),
+    (dict(kv=FAKE + 8), mla.MLA_ERR_INVALID_ARGUMENT, "kv"),
+    (dict(idx=None), mla.MLA_ERR_INVALID_ARGUMENT, "indices"),
+    (dict(ws=FAKE + 16), mla.MLA_ERR_INVALID_ARGUMENT, "workspace"),
+    (dict(out=None), mla.MLA_ERR_INVALID_ARGUMENT, "out"),
+    (dict(lse=None), mla.MLA_ERR_INVALID_ARGUMENT, "lse"),
+    (dict(ws_bytes=1024), mla.MLA_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes"),
+])
+def test_prefill_rejects_bad_arguments(kw, status, word):
+    assert call_prefill(**kw) == status
+    assert mla.mla_last_error().startswith(word)
+
+
+def test_prefill_workspace_grows_with_chunk_not_beyond():
+    a = mla.mla_sparse_prefill_workspace_bytes(100, 128, 5000, 64, 0, 256)
+    b = mla.mla_sparse_prefill_workspace_bytes(2048, 128, 5000, 64, 0, 256)
+    c = mla.mla_sparse_prefill_workspace_bytes(100000, 128, 5000, 64, 0, 256)
+    assert a < b == c
+    assert call_prefill(s_q=0, ws_bytes=mla.mla_sparse_prefill_workspace_bytes(0, 16, 100, 8, 0, 4)) == mla.MLA_OK
