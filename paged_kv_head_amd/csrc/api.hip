@@ -230,6 +230,8 @@ mla_status mla_decode_paged(const mla_problem* p, const void* q, const void* kv_
   a.ws_flush = (float*)((char*)workspace + mla::ws_lse_bytes(slots, s.rows) + mla::ws_o_bytes(slots, s.rows));
   a.out = (uint16_t*)out;
   a.lse = lse;
+  if (mla::small_decode_applies(s))
+    return hip_status(mla::launch_decode_small(a, (hipStream_t)stream), "decode kernel launch");
   return hip_status(mla::launch_decode(a, (hipStream_t)stream), "decode kernel launch");
 }
 

@@ -1,0 +1,289 @@
+// Paged MLA decode for units of at most 16 query rows (s_q * h_q <= 16),
+// dense, bf16 latent cache: the shape a GPU holds when the 128 query heads
+// are split across GPUs ("Modular Platform 设计文档全景导读", section 九:
+// for MLA only the query heads can be split, the latent KV is replicated).
+// It computes what the main decode kernel computes (per row: scores
+// P_t = scale * q.K_t, lse = log2 sum 2^P_t, out = sum 2^(P_t - lse)
+// K_t[:512]; "为什么 FlashMLA 的解码内核能跑到 660 TFLOPS", section 上手示例;
+// online softmax and merges as in the Modular guide, sections 六 and 七),
+// and writes the same outputs and split partials.
+//
+// With so few rows the work per key is small and the cache stream from HBM
+// is the bound, so the design keeps loads flowing instead of sharing tiles:
+//   * wave w owns keys 16w .. 16w+15 of every 64-key page of the segment (a
+//     quarter tile) and streams them into its own pair of LDS buffers with
+//     direct global->LDS copies (1 KiB per instruction, no registers): the
+//     next quarter's copies are issued before the current one is computed,
+//     and no barrier is needed inside the loop;
+//   * scores are computed transposed, S^T = K Q^T, with 16x16x32 bf16 MFMAs
+//     (K from LDS, Q in registers); a lane ends up with 4 keys of one row,
+//     which is exactly the B-operand layout of P^T for O^T += V^T P^T
+//     (16x16x16 MFMAs), so the probabilities never leave the registers;
+//   * O^T keeps one row per lane, so the online-softmax rescale is
+//     lane-local; the running max is refreshed lazily (only when it grows
+//     by more than 8 in log2 units);
+//   * each wave keeps its own running max, sum and output over its own keys;
+//     at the end of a segment the four are merged in LDS in a fixed order
+//     (deterministic results) and written like the main kernel's.
+//
+// LDS key row pitch is 1168 bytes (1152 + 16): 16 consecutive rows then
+// start on 16 distinct 4-bank groups, so the 16-byte K operand reads are
+// conflict free; the 2-byte V^T reads of four rows 4 apart land 16 banks
+// apart.
+#include "internal.h"
+
+namespace mla {
+namespace {
+
+typedef __bf16 bf16x8s __attribute__((ext_vector_type(8)));
+typedef float f32x4s __attribute__((ext_vector_type(4)));
+
+constexpr int kSWaves = 4;
+constexpr int kSQuarter = 16;                                 // keys per wave per page
+constexpr int kSPitch = 1168;                                 // LDS bytes per key row
+constexpr int kSRowSlots = kSPitch / 16;                      // 73 16-byte slots
+constexpr int kSCopies = (kSQuarter * kSRowSlots + 63) / 64;  // 19 copies of 1 KiB
+constexpr int kSBuf = kSCopies * 1024;                        // 19456 bytes per buffer
+constexpr int kSSteps = kDqk / 32;                            // 18 k-steps of 32 dims
+constexpr int kSOPitch = 516;                                 // floats per merge-buffer row
+constexpr float kSRefresh = 8.0f;                             // lazy max refresh threshold
+
+// Stands in for the cache bytes of keys that are not visible.
+__device__ __attribute__((aligned(16))) const uint8_t g_zero16[16] = {};
+
+// 16 bytes per lane from global memory into LDS at m0 + 16 * lane.  Issued
+// from inline assembly, so completion is waited for explicitly (vmcnt).
+__device__ inline void dma16_to_lds(const void* g, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(g), "s"(m0) : "memory", "m0");
+}
+
+__device__ inline uint16_t to_bf16_bits(float x) {
+  __bf16 h = (__bf16)x;  // round to nearest even
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+typedef __bf16 bf16x4s __attribute__((ext_vector_type(4)));
+using cint32s = const __attribute__((address_space(4))) int32_t;
+
+// Copies of one quarter tile (keys 16*wave .. +15 of page `page`, logical
+// positions tbase ..) into the LDS buffer at lds: slot 64*c + lane of the
+// buffer is 16-byte chunk `chunk` of key row `key` (73 slots per row, the
+// last one padding); keys at or past L come from the zero row.
+__device__ inline void issue_quarter(const uint8_t* __restrict__ kv, int page, int wave, int tbase,
+                                     int L, uint32_t lds, int lane) {
+  const uint8_t* src0 = kv + ((int64_t)page * kPage + kSQuarter * wave) * (kDqk * 2);
+  int key = 0, chunk = lane;  // stepping by 64 slots wraps the chunk at most once
+#pragma unroll 1
+  for (int c = 0; c < kSCopies; ++c) {
+    const bool ok = key < kSQuarter && chunk < kSRowSlots - 1 && tbase + key < L;
+    const void* src = ok ? (const void*)(src0 + key * (kDqk * 2) + chunk * 16) : (const void*)g_zero16;
+    dma16_to_lds(src, lds + 1024 * c);
+    chunk += 64;
+    if (chunk >= kSRowSlots) {
+      chunk -= kSRowSlots;
+      ++key;
+    }
+  }
+}
+
+__global__ void __launch_bounds__(64 * kSWaves, 1) decode_small_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf[kSWaves * 2 * kSBuf];
+  __shared__ float m_sh[kSWaves][16];
+  __shared__ float l_sh[kSWaves][16];
+
+  const Shape& s = a.s;
+  const int part = blockIdx.x;
+  if (part >= a.num_parts) return;
+  const int32_t* sc = a.sched + 8 * (size_t)part;
+  const int ub = sc[0], kb0 = sc[1], ue = sc[2], ke = sc[3], split0 = sc[4];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int j16 = lane & 15;  // query row (score and output)
+  const int g = lane >> 4;    // lane group: keys 4g .. 4g+3; dims 8g .. of a k-step
+  uint8_t* const buf0 = kbuf + wave * 2 * kSBuf;
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)buf0);
+
+  for (int u = ub; u < s.units && (u < ue || (u == ue && ke > 0)); ++u) {
+    const int L = a.seqlens[u];
+    const int nb = (max(L, 0) + kPage - 1) / kPage;
+    const int kfirst = (u == ub) ? kb0 : 0;
+    const int kend = (u == ue) ? ke : nb;
+    if (kfirst >= kend) continue;
+    const int seg = (u == ub) ? split0 : 0;
+    const int nsplit = a.num_splits[u + 1] - a.num_splits[u];
+    cint32s* btc = (cint32s*)(a.block_table + (int64_t)u * s.max_pages);  // scalar loads
+
+    // Q^T operands of row j16 (dims 32*st + 8*g .. +7; zero for padding rows)
+    // and the row's last visible position.
+    const bool row_ok = j16 < s.rows;
+    const uint16_t* qrow = a.q + ((int64_t)u * s.rows + (row_ok ? j16 : 0)) * kDqk + 8 * g;
+    bf16x8s qf[kSSteps];
+#pragma unroll
+    for (int st = 0; st < kSSteps; ++st)
+      qf[st] = row_ok ? *reinterpret_cast<const bf16x8s*>(qrow + 32 * st) : bf16x8s{};
+    const int tlim = s.is_causal ? L - s.s_q + (row_ok ? j16 : 0) / s.h_q : L - 1;
+    // The first quarter's copies go out while Q is in flight; Q is waited for
+    // here, before the loop, so that no wait for it lands inside the loop
+    // (it would also wait for the copies in flight there).
+    issue_quarter(a.kv, btc[kfirst], wave, kfirst * kPage + kSQuarter * wave, L, lds0, lane);
+    asm volatile("" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]), "v"(qf[5]),
+                 "v"(qf[6]), "v"(qf[7]), "v"(qf[8]));
+    asm volatile("" ::"v"(qf[9]), "v"(qf[10]), "v"(qf[11]), "v"(qf[12]), "v"(qf[13]), "v"(qf[14]),
+                 "v"(qf[15]), "v"(qf[16]), "v"(qf[17]));
+
+    f32x4s o[32];  // O^T: columns 16*cb + 4*g + v of row j16
+#pragma unroll
+    for (int cb = 0; cb < 32; ++cb) o[cb] = f32x4s{0.0f, 0.0f, 0.0f, 0.0f};
+    float m = -INFINITY;  // reference max of the row (log2 units); lags the true max by < 8
+    float l = 0.0f;       // this lane's part of the row sum
+
+    int cur = 0;
+    for (int kt = kfirst; kt < kend; ++kt) {
+      const int tbase = kt * kPage + kSQuarter * wave;  // logical position of key 0
+      if (kt + 1 < kend) {
+        // the other buffer was last read by the previous quarter's products
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        issue_quarter(a.kv, btc[kt + 1], wave, tbase + kPage, L, lds0 + (cur ^ 1) * kSBuf, lane);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kSCopies) : "memory");  // this quarter has landed
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      const uint8_t* qb = buf0 + cur * kSBuf;
+      cur ^= 1;
+
+      // S^T (16 keys x 16 rows); K operands of step st+1 read while step st multiplies.
+      f32x4s acc = f32x4s{0.0f, 0.0f, 0.0f, 0.0f};
+      const uint8_t* krow = qb + j16 * kSPitch + 16 * g;
+      bf16x8s kop = *reinterpret_cast<const bf16x8s*>(krow);
+#pragma unroll
+      for (int st = 0; st < kSSteps; ++st) {
+        bf16x8s knext;
+        if (st + 1 < kSSteps) knext = *reinterpret_cast<const bf16x8s*>(krow + 64 * (st + 1));
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qf[st], acc, 0, 0, 0);
+        if (st + 1 < kSSteps) kop = knext;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+
+      // Online softmax (base 2) of row j16 over keys 4g .. 4g+3 of this quarter.
+      float x[4];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        x[v] = tbase + 4 * g + v <= tlim ? acc[v] * s.scale_log2 : -INFINITY;
+        mx = fmaxf(mx, x[v]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const bool grow = mx > m + kSRefresh || (m == -INFINITY && mx > -INFINITY);
+      if (__builtin_amdgcn_ballot_w64(grow)) {  // rare: the reference max moves up
+        const float f = grow ? (m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - mx)) : 1.0f;
+        if (grow) m = mx;
+        l *= f;
+#pragma unroll
+        for (int cb = 0; cb < 32; ++cb) {  // one block at a time: few registers in flight
+          o[cb] *= f;
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      bf16x4s pf;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float p = x[v] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(x[v] - m);
+        l += p;
+        pf[v] = (__bf16)p;
+      }
+
+      // O^T += V^T P^T: column block cb; V^T[col][key] for keys 4g .. 4g+3 of
+      // column 16*cb + j16, read as 4 bf16.
+      const __bf16* vcol = reinterpret_cast<const __bf16*>(qb) + 4 * g * (kSPitch / 2) + j16;
+      auto v_operand = [&](int cb) {
+        bf16x4s v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = vcol[e * (kSPitch / 2) + 16 * cb];
+        return v;
+      };
+      bf16x4s vop = v_operand(0);
+#pragma unroll
+      for (int cb = 0; cb < 32; ++cb) {
+        bf16x4s vnext;
+        if (cb + 1 < 32) vnext = v_operand(cb + 1);  // read while this block multiplies
+        o[cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, pf, o[cb], 0, 0, 0);
+        if (cb + 1 < 32) vop = vnext;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+
+    // Merge the four waves' partial results of each row: M = max of the
+    // maxima, total = sum of l_w * 2^(m_w - M); each wave's output enters
+    // with weight 2^(m_w - M) / total.
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (g == 0) {
+      m_sh[wave][j16] = m;
+      l_sh[wave][j16] = l;
+    }
+    __syncthreads();  // every wave is past its last quarter; the buffers are free
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kSWaves; ++w) M = fmaxf(M, m_sh[w][j16]);
+    float tot = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kSWaves; ++w) {
+      const float mw = m_sh[w][j16];
+      tot += mw == -INFINITY ? 0.0f : l_sh[w][j16] * __builtin_amdgcn_exp2f(mw - M);
+    }
+    const float wgt = (tot > 0.0f && m != -INFINITY) ? __builtin_amdgcn_exp2f(m - M) / tot : 0.0f;
+    const float lse2 = tot > 0.0f ? M + log2f(tot) : -INFINITY;
+    float* const fbuf = reinterpret_cast<float*>(kbuf);  // [16 rows][kSOPitch]
+#pragma unroll
+    for (int w = 0; w < kSWaves; ++w) {  // fixed order: deterministic sums
+      if (wave == w) {
+#pragma unroll
+        for (int cb = 0; cb < 32; ++cb) {
+          f32x4s* dst = reinterpret_cast<f32x4s*>(fbuf + j16 * kSOPitch + 16 * cb + 4 * g);
+          const f32x4s v = o[cb] * wgt;
+          *dst = w == 0 ? v : *dst + v;
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      __syncthreads();
+    }
+    const bool direct = nsplit == 1;
+    const int64_t orow0 = direct ? (int64_t)u * s.rows : ((int64_t)a.num_splits[u] + seg) * s.rows;
+    uint16_t* const obase = direct ? a.out : a.ws_o;
+    for (int row = wave; row < s.rows; row += kSWaves) {
+      const f32x4s v0 = *reinterpret_cast<const f32x4s*>(fbuf + row * kSOPitch + 8 * lane);
+      const f32x4s v1 = *reinterpret_cast<const f32x4s*>(fbuf + row * kSOPitch + 8 * lane + 4);
+      uint4 pk;
+      pk.x = (uint32_t)to_bf16_bits(v0[0]) | ((uint32_t)to_bf16_bits(v0[1]) << 16);
+      pk.y = (uint32_t)to_bf16_bits(v0[2]) | ((uint32_t)to_bf16_bits(v0[3]) << 16);
+      pk.z = (uint32_t)to_bf16_bits(v1[0]) | ((uint32_t)to_bf16_bits(v1[1]) << 16);
+      pk.w = (uint32_t)to_bf16_bits(v1[2]) | ((uint32_t)to_bf16_bits(v1[3]) << 16);
+      *reinterpret_cast<uint4*>(obase + (orow0 + row) * kDv + 8 * lane) = pk;
+    }
+    if (wave == 0 && g == 0 && row_ok) {
+      if (direct)
+        a.lse[(int64_t)u * s.rows + j16] = s.natural ? lse2 * 0.69314718055994531f : lse2;
+      else
+        a.ws_lse[((int64_t)a.num_splits[u] + seg) * s.rows + j16] = lse2;
+    }
+    __syncthreads();  // the merge buffer is read before the next segment's copies
+  }
+}
+
+}  // namespace
+
+// Units of up to 16 rows (one 16-row MFMA block).
+bool small_decode_applies(const Shape& s) {
+  return s.kv_format == 0 && s.topk == 0 && s.rows <= 16;
+}
+
+hipError_t launch_decode_small(const DecodeArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(decode_small_kernel, dim3(a.num_parts), dim3(64 * kSWaves), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -66,6 +66,10 @@ inline size_t ws_total_bytes(int32_t num_parts, int32_t units, int32_t rows, int
 hipError_t launch_metadata(const Shape& s, const int32_t* seqlens, int32_t num_parts,
                            int32_t* sched, int32_t* num_splits, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+// Units of at most 16 query rows (dense, bf16 cache) run on a kernel built
+// for the HBM-bound small-head shape; same inputs, outputs and workspace.
+bool small_decode_applies(const Shape& s);
+hipError_t launch_decode_small(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_combine(const Shape& s, const int32_t* num_splits, const float* ws_lse,
                           const uint16_t* ws_o, uint16_t* out, float* lse, hipStream_t stream);
 hipError_t launch_kv_quantize_fp8(int32_t batch, int32_t n_new, int32_t num_pages,
