@@ -45,10 +45,12 @@ def parse():
     ap.add_argument("--num-parts", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-units", type=int, default=None)
-    ap.add_argument("--kernel", choices=["decode", "writer", "prefill"], default="decode",
+    ap.add_argument("--kernel", choices=["decode", "small", "writer", "prefill"], default="decode",
                     help="decode: the decode step (default); writer: the FP8 KV writer filling "
                          "128 sequences x 4096 new tokens; prefill: sparse prefill, 4096 query "
-                         "tokens x 128 heads over a 32768-row cache, topk 2048")
+                         "tokens x 128 heads over a 32768-row cache, topk 2048; small: decode with "
+                         "16 query heads (an 8-way head split of the 128), batch 128, lengths "
+                         "U[1024, 8192]")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run three 1 GiB device-to-device copies (reference for the HBM byte "
                          "counters under rocprofv3), print nothing else")
@@ -203,6 +205,8 @@ def bench_writer(args):
     print(json.dumps(line), flush=True)
 
 
+SMALL_WORKLOAD = dict(name="b128_h16_sq1_dense_bf16")
+
 PREFILL_WORKLOAD = dict(name="prefill_s4096_kv32768_topk2048", s_q=4096, h_q=128, s_kv=32768,
                         topk=2048, seed=77)
 
@@ -323,7 +327,11 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     t0 = time.time()
-    w = synth.config_workload(args.config)
+    if args.kernel == "small":
+        w = synth.make_workload(SMALL_WORKLOAD["name"], batch=128, h_q=16, s_q=1,
+                                seqlens=synth.Uniform(1024, 8192), seed=1006, max_pages_per_seq=128)
+    else:
+        w = synth.config_workload(args.config)
     print(f"[bench] workload {w.name}: generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     p = problem(w)
     q, kv, bt, sl, idx = to_device(w, dev)
@@ -395,7 +403,8 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     tr = traffic_record(w.name)
     roof["traffic"] = None if tr is None else tr["hbm_bytes_per_launch"]
-    roof["kernel"] = "decode_kernel"
+    roof["kernel"] = "decode_small_kernel" if w.s_q * w.h_q <= 16 and w.kv_format == 0 and w.topk == 0 \
+        else "decode_kernel"
     roof["kernel_ms"] = dec_ms
 
     cpu = None
@@ -404,7 +413,9 @@ def main():
         cpu = cpu_baseline(w, args.cpu_sample_units)
 
     line = {
-        "metric": "paged MLA decode TFLOPS + HBM GB/s (h_q=128, d_qk=576, d_v=512), % of roofline",
+        "metric": ("paged MLA decode TFLOPS + HBM GB/s (h_q=128, d_qk=576, d_v=512), % of roofline"
+                   if args.kernel == "decode" else
+                   f"paged MLA decode TFLOPS + HBM GB/s (h_q={w.h_q}, d_qk=576, d_v=512), % of roofline"),
         "value": tflops, "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",

@@ -1,0 +1,93 @@
+"""GPU parity of decode for units of at most 16 query rows (h_q * s_q <= 16,
+dense bf16), which run on their own kernel: row counts below one MFMA block,
+causal rows, the lazy rescale, forced split counts, bit identity under page
+permutation and across runs, and a seeded sample at the benchmark's size."""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.harness import assert_close, run, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("h_q,s_q,causal", [(1, 1, 0), (3, 1, 0), (4, 3, 1), (8, 2, 1), (16, 1, 0),
+                                            (5, 3, 1), (16, 1, 1)])
+def test_small_head_shapes(h_q, s_q, causal):
+    w = synth.make_workload("small", batch=5, h_q=h_q, s_q=s_q, seqlens=[1, 2, 64, 300, 1000],
+                            seed=60 + h_q * 4 + s_q, is_causal=causal)
+    print(f"h_q {h_q} s_q {s_q} causal {causal}", flush=True)
+    out, lse = run(w)
+    ref_out, ref_lse = oracle.mla_decode(w)
+    assert_close(out, lse, ref_out, ref_lse, what=f"h_q={h_q} s_q={s_q} causal={causal}")
+
+
+@pytest.mark.parametrize("parts", [1, 2, 5, 64, 700])
+def test_small_heads_forced_splits(parts):
+    w = synth.make_workload("small_split", batch=6, h_q=16, s_q=1, seqlens=synth.Uniform(1, 3000),
+                            seed=71)
+    out, lse = run(w, num_parts=parts)
+    ref_out, ref_lse = oracle.mla_decode(w)
+    assert_close(out, lse, ref_out, ref_lse, what=f"parts={parts}")
+
+
+@pytest.mark.parametrize("natural, scale", [(True, None), (False, -0.05), (False, 0.0)])
+def test_small_heads_base_and_scale(natural, scale):
+    w = synth.make_workload("small_scale", batch=3, h_q=16, s_q=1, seqlens=[100, 700, 65], seed=72)
+    out, lse = run(w, natural=natural, softmax_scale=scale)
+    ref_out, ref_lse = oracle.mla_decode(w, natural=natural, softmax_scale=scale)
+    assert_close(out, lse, ref_out, ref_lse, what=f"natural={natural} scale={scale}")
+
+
+def test_small_heads_growing_scores_rescale():
+    """Scores that climb by far more than the refresh threshold force the
+    lazy rescale of the running output many times."""
+    w = synth.make_workload("small_grow", batch=2, h_q=16, s_q=1, seqlens=[900, 300], seed=73,
+                            slack=0)
+    kv = w.kv.copy()
+    for b in range(2):
+        for t in range(int(w.cache_seqlens[b])):
+            page, slot = w.block_table[b, t // 64], t % 64
+            x = np.full(576, 0.05 * t, dtype=np.float32)
+            x[:512] += np.float32(np.sin(t))
+            kv[page, slot] = synth.bf16_bits_from_f32(x).view(np.uint8)
+    w.kv = kv
+    w.q = np.full(w.q.shape, 0x3F80, dtype=np.uint16)
+    for parts in (None, 3):
+        out, lse = run(w, num_parts=parts, softmax_scale=0.02)
+        ref_out, ref_lse = oracle.mla_decode(w, softmax_scale=0.02)
+        assert_close(out, lse, ref_out, ref_lse, what=f"growing parts={parts}")
+
+
+def test_small_heads_bit_identity():
+    """Same results bit for bit across runs and after permuting the physical
+    pages (the block table rewritten to match)."""
+    w = synth.make_workload("small_bits", batch=4, h_q=16, s_q=1, seqlens=[700, 64, 129, 2000],
+                            seed=74)
+    t = to_device(w)
+    out1, lse1 = run(w, tensors=t)
+    out2, lse2 = run(w, tensors=t)
+    assert np.array_equal(out1, out2) and np.array_equal(lse1, lse2)
+    perm = np.random.default_rng(6).permutation(w.num_pages)
+    kv2 = np.empty_like(w.kv)
+    kv2[perm] = w.kv
+    w.block_table = np.where(w.block_table >= 0, perm[np.maximum(w.block_table, 0)], -1).astype(np.int32)
+    w.kv = kv2
+    out3, lse3 = run(w)
+    assert np.array_equal(out1, out3) and np.array_equal(lse1, lse3)
+
+
+def test_small_heads_full_size_sampled():
+    """The small-head benchmark's shape (batch 128, h_q 16, s_q 1, lengths
+    U[1024, 8192]) in its default launch configuration; a seeded sample of
+    sequences is checked against the oracle."""
+    w = synth.make_workload("b128_h16_sq1", batch=128, h_q=16, s_q=1,
+                            seqlens=synth.Uniform(1024, 8192), seed=1006, max_pages_per_seq=128)
+    out, lse = run(w)
+    mask = np.zeros((w.batch, w.s_q), dtype=bool)
+    mask[np.random.default_rng(0).choice(w.batch, size=10, replace=False)] = True
+    ref_out, ref_lse = oracle.mla_decode(w, unit_mask=mask[:, 0].astype(np.uint8))
+    assert_close(out, lse, ref_out, ref_lse, mask=mask, what="b128 h16 sample")
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
