@@ -1,4 +1,4 @@
-// Paged MLA decode for units of at most 16 query rows (s_q * h_q <= 16),
+// Paged MLA decode for units of few query rows (s_q * h_q <= kSmallMaxRows),
 // dense, bf16 latent cache: the shape a GPU holds when the 128 query heads
 // are split across GPUs ("Modular Platform 设计文档全景导读", section 九:
 // for MLA only the query heads can be split, the latent KV is replicated).
@@ -9,7 +9,11 @@
 // and writes the same outputs and split partials.
 //
 // With so few rows the work per key is small and the cache stream from HBM
-// is the bound, so the design keeps loads flowing instead of sharing tiles:
+// is the bound, so the design keeps loads flowing instead of sharing tiles.
+// A workgroup owns 16 rows of a unit (one MFMA block); the row groups of a
+// split-KV part get workgroup ids congruent mod 8, so they run on the same
+// XCD and the second read of each page comes from its L2.  Inside a
+// workgroup:
 //   * wave w owns keys 16w .. 16w+15 of every 64-key page of the segment (a
 //     quarter tile) and streams them into its own pair of LDS buffers with
 //     direct global->LDS copies (1 KiB per instruction, no registers): the
@@ -47,6 +51,10 @@ constexpr int kSBuf = kSCopies * 1024;                        // 19456 bytes per
 constexpr int kSSteps = kDqk / 32;                            // 18 k-steps of 32 dims
 constexpr int kSOPitch = 516;                                 // floats per merge-buffer row
 constexpr float kSRefresh = 8.0f;                             // lazy max refresh threshold
+// LDS operand reads in flight ahead of their MFMA (at most 15 LDS reads may
+// be outstanding: 2 K reads per step, 4 V reads per column block)
+constexpr int kSKAhead = 4;
+constexpr int kSVAhead = 3;
 
 // Stands in for the cache bytes of keys that are not visible.
 __device__ __attribute__((aligned(16))) const uint8_t g_zero16[16] = {};
@@ -93,8 +101,14 @@ __global__ void __launch_bounds__(64 * kSWaves, 1) decode_small_kernel(DecodeArg
   __shared__ float l_sh[kSWaves][16];
 
   const Shape& s = a.s;
-  const int part = blockIdx.x;
+  // Workgroup -> (part, row group); workgroups go round-robin to the 8 XCDs.
+  const int wg = blockIdx.x;
+  const int span = 8 * s.groups;
+  const int part = (wg / span) * 8 + (wg % span) % 8;
+  const int grp = (wg % span) / 8;
   if (part >= a.num_parts) return;
+  const int row0 = kSmallRowsPerGroup * grp;           // first unit row of this workgroup
+  const int nrows = min(kSmallRowsPerGroup, s.rows - row0);  // rows of this workgroup (>= 1)
   const int32_t* sc = a.sched + 8 * (size_t)part;
   const int ub = sc[0], kb0 = sc[1], ue = sc[2], ke = sc[3], split0 = sc[4];
 
@@ -118,13 +132,14 @@ __global__ void __launch_bounds__(64 * kSWaves, 1) decode_small_kernel(DecodeArg
 
     // Q^T operands of row j16 (dims 32*st + 8*g .. +7; zero for padding rows)
     // and the row's last visible position.
-    const bool row_ok = j16 < s.rows;
-    const uint16_t* qrow = a.q + ((int64_t)u * s.rows + (row_ok ? j16 : 0)) * kDqk + 8 * g;
+    const bool row_ok = j16 < nrows;
+    const int urow = row0 + (row_ok ? j16 : 0);  // row in the unit
+    const uint16_t* qrow = a.q + ((int64_t)u * s.rows + urow) * kDqk + 8 * g;
     bf16x8s qf[kSSteps];
 #pragma unroll
     for (int st = 0; st < kSSteps; ++st)
       qf[st] = row_ok ? *reinterpret_cast<const bf16x8s*>(qrow + 32 * st) : bf16x8s{};
-    const int tlim = s.is_causal ? L - s.s_q + (row_ok ? j16 : 0) / s.h_q : L - 1;
+    const int tlim = s.is_causal ? L - s.s_q + urow / s.h_q : L - 1;
     // The first quarter's copies go out while Q is in flight; Q is waited for
     // here, before the loop, so that no wait for it lands inside the loop
     // (it would also wait for the copies in flight there).
@@ -154,16 +169,19 @@ __global__ void __launch_bounds__(64 * kSWaves, 1) decode_small_kernel(DecodeArg
       const uint8_t* qb = buf0 + cur * kSBuf;
       cur ^= 1;
 
-      // S^T (16 keys x 16 rows); K operands of step st+1 read while step st multiplies.
+      // S^T (16 keys x 16 rows); K operands are read kSKAhead steps before
+      // their MFMA, so the LDS latency hides behind the chain.
       f32x4s acc = f32x4s{0.0f, 0.0f, 0.0f, 0.0f};
       const uint8_t* krow = qb + j16 * kSPitch + 16 * g;
-      bf16x8s kop = *reinterpret_cast<const bf16x8s*>(krow);
+      bf16x8s kop[kSKAhead];
+#pragma unroll
+      for (int i = 0; i < kSKAhead; ++i) kop[i] = *reinterpret_cast<const bf16x8s*>(krow + 64 * i);
 #pragma unroll
       for (int st = 0; st < kSSteps; ++st) {
-        bf16x8s knext;
-        if (st + 1 < kSSteps) knext = *reinterpret_cast<const bf16x8s*>(krow + 64 * (st + 1));
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qf[st], acc, 0, 0, 0);
-        if (st + 1 < kSSteps) kop = knext;
+        const bf16x8s cur = kop[st % kSKAhead];
+        if (st + kSKAhead < kSSteps)
+          kop[st % kSKAhead] = *reinterpret_cast<const bf16x8s*>(krow + 64 * (st + kSKAhead));
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, qf[st], acc, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
 
@@ -205,13 +223,14 @@ __global__ void __launch_bounds__(64 * kSWaves, 1) decode_small_kernel(DecodeArg
         for (int e = 0; e < 4; ++e) v[e] = vcol[e * (kSPitch / 2) + 16 * cb];
         return v;
       };
-      bf16x4s vop = v_operand(0);
+      bf16x4s vop[kSVAhead];  // V^T operands read kSVAhead column blocks ahead
+#pragma unroll
+      for (int i = 0; i < kSVAhead; ++i) vop[i] = v_operand(i);
 #pragma unroll
       for (int cb = 0; cb < 32; ++cb) {
-        bf16x4s vnext;
-        if (cb + 1 < 32) vnext = v_operand(cb + 1);  // read while this block multiplies
-        o[cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, pf, o[cb], 0, 0, 0);
-        if (cb + 1 < 32) vop = vnext;
+        const bf16x4s cur = vop[cb % kSVAhead];
+        if (cb + kSVAhead < 32) vop[cb % kSVAhead] = v_operand(cb + kSVAhead);
+        o[cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(cur, pf, o[cb], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -254,7 +273,7 @@ __global__ void __launch_bounds__(64 * kSWaves, 1) decode_small_kernel(DecodeArg
     const bool direct = nsplit == 1;
     const int64_t orow0 = direct ? (int64_t)u * s.rows : ((int64_t)a.num_splits[u] + seg) * s.rows;
     uint16_t* const obase = direct ? a.out : a.ws_o;
-    for (int row = wave; row < s.rows; row += kSWaves) {
+    for (int row = wave; row < nrows; row += kSWaves) {
       const f32x4s v0 = *reinterpret_cast<const f32x4s*>(fbuf + row * kSOPitch + 8 * lane);
       const f32x4s v1 = *reinterpret_cast<const f32x4s*>(fbuf + row * kSOPitch + 8 * lane + 4);
       uint4 pk;
@@ -262,13 +281,13 @@ __global__ void __launch_bounds__(64 * kSWaves, 1) decode_small_kernel(DecodeArg
       pk.y = (uint32_t)to_bf16_bits(v0[2]) | ((uint32_t)to_bf16_bits(v0[3]) << 16);
       pk.z = (uint32_t)to_bf16_bits(v1[0]) | ((uint32_t)to_bf16_bits(v1[1]) << 16);
       pk.w = (uint32_t)to_bf16_bits(v1[2]) | ((uint32_t)to_bf16_bits(v1[3]) << 16);
-      *reinterpret_cast<uint4*>(obase + (orow0 + row) * kDv + 8 * lane) = pk;
+      *reinterpret_cast<uint4*>(obase + (orow0 + row0 + row) * kDv + 8 * lane) = pk;
     }
     if (wave == 0 && g == 0 && row_ok) {
       if (direct)
-        a.lse[(int64_t)u * s.rows + j16] = s.natural ? lse2 * 0.69314718055994531f : lse2;
+        a.lse[(int64_t)u * s.rows + row0 + j16] = s.natural ? lse2 * 0.69314718055994531f : lse2;
       else
-        a.ws_lse[((int64_t)a.num_splits[u] + seg) * s.rows + j16] = lse2;
+        a.ws_lse[((int64_t)a.num_splits[u] + seg) * s.rows + row0 + j16] = lse2;
     }
     __syncthreads();  // the merge buffer is read before the next segment's copies
   }
@@ -276,13 +295,14 @@ __global__ void __launch_bounds__(64 * kSWaves, 1) decode_small_kernel(DecodeArg
 
 }  // namespace
 
-// Units of up to 16 rows (one 16-row MFMA block).
 bool small_decode_applies(const Shape& s) {
-  return s.kv_format == 0 && s.topk == 0 && s.rows <= 16;
+  return s.kv_format == 0 && s.topk == 0 && s.rows <= kSmallMaxRows;
 }
 
 hipError_t launch_decode_small(const DecodeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(decode_small_kernel, dim3(a.num_parts), dim3(64 * kSWaves), 0, stream, a);
+  const int span = 8 * a.s.groups;
+  const int grid = ((a.num_parts + 7) / 8) * span;
+  hipLaunchKernelGGL(decode_small_kernel, dim3(grid), dim3(64 * kSWaves), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -10,6 +10,12 @@ constexpr int kDqk = 576;
 constexpr int kDv = 512;
 constexpr int kPage = 64;          // tokens per page == keys per tile
 constexpr int kRowsPerGroup = 128; // query rows one workgroup owns
+// Dense bf16 units of at most kSmallMaxRows rows run on the small-head
+// kernel, whose workgroups own kSmallRowsPerGroup rows each.  Measured: it
+// is faster than the main kernel for one row group (h_q * s_q <= 16) and
+// slower from two on (the main kernel reads each page once per 128 rows).
+constexpr int kSmallRowsPerGroup = 16;
+constexpr int kSmallMaxRows = 16;
 constexpr int kSplitPenalty = 3;   // scheduler cost of one segment, in blocks (measured: a
                                     // segment's prologue + epilogue ~ 3 tiles)
 constexpr int kMaxUnits = 16384;   // metadata kernel keeps per-unit arrays in LDS
@@ -20,7 +26,7 @@ struct Shape {
   int32_t num_pages, max_pages;
   int32_t units;  // U
   int32_t rows;   // query rows per unit (R)
-  int32_t groups; // ceil(R / 128)
+  int32_t groups; // row groups per unit: ceil(R / rows per workgroup of the kernel that runs it)
   float scale_log2;  // exponent multiplier: softmax_scale, times log2(e) for base e
   float inv_h_q;     // 1 / h_q (query position of a row without an integer division)
 };
@@ -66,7 +72,7 @@ inline size_t ws_total_bytes(int32_t num_parts, int32_t units, int32_t rows, int
 hipError_t launch_metadata(const Shape& s, const int32_t* seqlens, int32_t num_parts,
                            int32_t* sched, int32_t* num_splits, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
-// Units of at most 16 query rows (dense, bf16 cache) run on a kernel built
+// Units of at most kSmallMaxRows query rows (dense, bf16 cache) run on a kernel built
 // for the HBM-bound small-head shape; same inputs, outputs and workspace.
 bool small_decode_applies(const Shape& s);
 hipError_t launch_decode_small(const DecodeArgs& a, hipStream_t stream);

@@ -1,6 +1,6 @@
-"""GPU parity of decode for units of at most 16 query rows (h_q * s_q <= 16,
-dense bf16), which run on their own kernel: row counts below one MFMA block,
-causal rows, the lazy rescale, forced split counts, bit identity under page
+"""GPU parity of decode at small head counts (h_q * s_q <= 64, dense bf16):
+units of at most 16 rows run on their own kernel, larger ones on the main
+kernel; row counts below and between 16-row blocks, causal rows, the lazy rescale, forced split counts, bit identity under page
 permutation and across runs, and a seeded sample at the benchmark's size."""
 
 import numpy as np
@@ -14,7 +14,8 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("h_q,s_q,causal", [(1, 1, 0), (3, 1, 0), (4, 3, 1), (8, 2, 1), (16, 1, 0),
-                                            (5, 3, 1), (16, 1, 1)])
+                                            (5, 3, 1), (16, 1, 1), (17, 1, 0), (16, 2, 1), (32, 1, 0),
+                                            (11, 3, 1), (48, 1, 0), (16, 4, 1), (64, 1, 0), (21, 3, 1)])
 def test_small_head_shapes(h_q, s_q, causal):
     w = synth.make_workload("small", batch=5, h_q=h_q, s_q=s_q, seqlens=[1, 2, 64, 300, 1000],
                             seed=60 + h_q * 4 + s_q, is_causal=causal)
@@ -24,9 +25,10 @@ def test_small_head_shapes(h_q, s_q, causal):
     assert_close(out, lse, ref_out, ref_lse, what=f"h_q={h_q} s_q={s_q} causal={causal}")
 
 
+@pytest.mark.parametrize("h_q", [16, 40])
 @pytest.mark.parametrize("parts", [1, 2, 5, 64, 700])
-def test_small_heads_forced_splits(parts):
-    w = synth.make_workload("small_split", batch=6, h_q=16, s_q=1, seqlens=synth.Uniform(1, 3000),
+def test_small_heads_forced_splits(parts, h_q):
+    w = synth.make_workload("small_split", batch=6, h_q=h_q, s_q=1, seqlens=synth.Uniform(1, 3000),
                             seed=71)
     out, lse = run(w, num_parts=parts)
     ref_out, ref_lse = oracle.mla_decode(w)
@@ -44,7 +46,7 @@ def test_small_heads_base_and_scale(natural, scale):
 def test_small_heads_growing_scores_rescale():
     """Scores that climb by far more than the refresh threshold force the
     lazy rescale of the running output many times."""
-    w = synth.make_workload("small_grow", batch=2, h_q=16, s_q=1, seqlens=[900, 300], seed=73,
+    w = synth.make_workload("small_grow", batch=2, h_q=32, s_q=1, seqlens=[900, 300], seed=73,
                             slack=0)
     kv = w.kv.copy()
     for b in range(2):
@@ -64,8 +66,8 @@ def test_small_heads_growing_scores_rescale():
 def test_small_heads_bit_identity():
     """Same results bit for bit across runs and after permuting the physical
     pages (the block table rewritten to match)."""
-    w = synth.make_workload("small_bits", batch=4, h_q=16, s_q=1, seqlens=[700, 64, 129, 2000],
-                            seed=74)
+    w = synth.make_workload("small_bits", batch=4, h_q=24, s_q=2, seqlens=[700, 64, 129, 2000],
+                            seed=74, is_causal=1)
     t = to_device(w)
     out1, lse1 = run(w, tensors=t)
     out2, lse2 = run(w, tensors=t)
