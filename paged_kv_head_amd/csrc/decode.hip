@@ -501,8 +501,10 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
   constexpr bool kPipelined = FMT == 0 && !SPARSE;  // tile loop order, below
 
   // Workgroup -> (part, row group).  Workgroups are dealt round-robin to
-  // the 8 XCDs, so the row groups of one part get ids congruent mod 8 and
-  // share that XCD's L2 for the tiles they both read.
+  // the 8 XCDs (XCD = id % 8).  XCD x takes the parts
+  // [x * per, (x + 1) * per) with all their row groups: the row groups of a
+  // part share that XCD's L2 for the tiles they all read, and consecutive
+  // parts (the pieces of a split sequence) share it for the sequence's Q.
   // Every kernel argument is fetched in one round of scalar loads here,
   // rather than in a chain of rounds along their first uses.
   asm volatile("" ::"s"(a.q), "s"(a.kv), "s"(a.block_table), "s"(a.seqlens), "s"(a.indices),
@@ -514,9 +516,9 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
   // are read-only here: scalar loads through the constant address space.
   using cint32 = const __attribute__((address_space(4))) int32_t;
   const int wg = blockIdx.x;
-  const int span = 8 * s.groups;
-  const int part = (wg / span) * 8 + (wg % span) % 8;
-  const int grp = (wg % span) / 8;
+  const int per = (a.num_parts + 7) / 8;
+  const int part = (wg % 8) * per + (wg / 8) / s.groups;
+  const int grp = (wg / 8) % s.groups;
   if (part >= a.num_parts) return;
   cint32* sc = (cint32*)(a.sched + 8 * (size_t)part);
   const int ub = sc[0], kb0 = sc[1], ue = sc[2], ke = sc[3], split0 = sc[4];
