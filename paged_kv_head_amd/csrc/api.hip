@@ -83,8 +83,9 @@ mla_status check_problem(const mla_problem* p, mla::Shape* s) {
   s->max_pages = p->max_pages_per_seq;
   s->units = (int32_t)units;
   s->rows = (int32_t)rows;
-  const int32_t per_group = mla::small_decode_applies(*s) ? mla::kSmallRowsPerGroup : mla::kRowsPerGroup;
-  s->groups = (int32_t)((rows + per_group - 1) / per_group);
+  s->groups = mla::small_decode_applies(*s)
+                  ? 1
+                  : (int32_t)((rows + mla::kRowsPerGroup - 1) / mla::kRowsPerGroup);
   s->scale_log2 = s->natural ? (float)((double)p->softmax_scale * 1.4426950408889634) : p->softmax_scale;
   s->inv_h_q = 1.0f / (float)p->h_q;
   return MLA_OK;

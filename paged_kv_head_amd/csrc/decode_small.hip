@@ -10,10 +10,8 @@
 //
 // With so few rows the work per key is small and the cache stream from HBM
 // is the bound, so the design keeps loads flowing instead of sharing tiles.
-// A workgroup owns 16 rows of a unit (one MFMA block); the row groups of a
-// split-KV part get workgroup ids congruent mod 8, so they run on the same
-// XCD and the second read of each page comes from its L2.  Inside a
-// workgroup:
+// A workgroup owns all rows of its unit (one or two 16-row MFMA blocks).
+// Inside a workgroup:
 //   * wave w owns keys 16w .. 16w+15 of every 64-key page of the segment (a
 //     quarter tile) and streams them into its own pair of LDS buffers with
 //     direct global->LDS copies (1 KiB per instruction, no registers): the
@@ -23,9 +21,11 @@
 //     (K from LDS, Q in registers); a lane ends up with 4 keys of one row,
 //     which is exactly the B-operand layout of P^T for O^T += V^T P^T
 //     (16x16x16 MFMAs), so the probabilities never leave the registers;
-//   * O^T keeps one row per lane, so the online-softmax rescale is
-//     lane-local; the running max is refreshed lazily (only when it grows
-//     by more than 8 in log2 units);
+//   * O^T keeps one row per lane; the probabilities are taken against the
+//     first max a row sees, which may lag the true max by up to 2^64 (far
+//     inside the fp32 range), so the output is never rescaled in the loop;
+//     a row whose scores climb further makes the wave run its segment again
+//     against the exact max it found;
 //   * each wave keeps its own running max, sum and output over its own keys;
 //     at the end of a segment the four are merged in LDS in a fixed order
 //     (deterministic results) and written like the main kernel's.
@@ -50,7 +50,10 @@ constexpr int kSCopies = (kSQuarter * kSRowSlots + 63) / 64;  // 19 copies of 1 
 constexpr int kSBuf = kSCopies * 1024;                        // 19456 bytes per buffer
 constexpr int kSSteps = kDqk / 32;                            // 18 k-steps of 32 dims
 constexpr int kSOPitch = 516;                                 // floats per merge-buffer row
-constexpr float kSRefresh = 8.0f;                             // lazy max refresh threshold
+// The running max a row's probabilities are taken against may lag the true
+// max by up to this much (log2 units): probabilities stay <= 2^64, sums far
+// inside the fp32 range.  A larger climb restarts the wave's segment.
+constexpr float kSLag = 64.0f;
 // LDS operand reads in flight ahead of their MFMA (at most 15 LDS reads may
 // be outstanding: 2 K reads per step, 4 V reads per column block)
 constexpr int kSKAhead = 4;
@@ -95,26 +98,24 @@ __device__ inline void issue_quarter(const uint8_t* __restrict__ kv, int page, i
   }
 }
 
+// RB 16-row MFMA blocks per workgroup (the whole unit: RB = 1 for up to 16
+// rows, 2 for up to 32).  K and V operands read from LDS feed all RB blocks.
+template <int RB>
 __global__ void __launch_bounds__(64 * kSWaves, 1) decode_small_kernel(DecodeArgs a) {
+  constexpr int kRows = 16 * RB;
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[kSWaves * 2 * kSBuf];
-  __shared__ float m_sh[kSWaves][16];
-  __shared__ float l_sh[kSWaves][16];
+  __shared__ float m_sh[kSWaves][kRows];
+  __shared__ float l_sh[kSWaves][kRows];
 
   const Shape& s = a.s;
-  // Workgroup -> (part, row group); workgroups go round-robin to the 8 XCDs.
-  const int wg = blockIdx.x;
-  const int span = 8 * s.groups;
-  const int part = (wg / span) * 8 + (wg % span) % 8;
-  const int grp = (wg % span) / 8;
+  const int part = blockIdx.x;
   if (part >= a.num_parts) return;
-  const int row0 = kSmallRowsPerGroup * grp;           // first unit row of this workgroup
-  const int nrows = min(kSmallRowsPerGroup, s.rows - row0);  // rows of this workgroup (>= 1)
   const int32_t* sc = a.sched + 8 * (size_t)part;
   const int ub = sc[0], kb0 = sc[1], ue = sc[2], ke = sc[3], split0 = sc[4];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int j16 = lane & 15;  // query row (score and output)
+  const int j16 = lane & 15;  // row within a 16-row block (score and output)
   const int g = lane >> 4;    // lane group: keys 4g .. 4g+3; dims 8g .. of a k-step
   uint8_t* const buf0 = kbuf + wave * 2 * kSBuf;
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
@@ -130,30 +131,51 @@ __global__ void __launch_bounds__(64 * kSWaves, 1) decode_small_kernel(DecodeArg
     const int nsplit = a.num_splits[u + 1] - a.num_splits[u];
     cint32s* btc = (cint32s*)(a.block_table + (int64_t)u * s.max_pages);  // scalar loads
 
-    // Q^T operands of row j16 (dims 32*st + 8*g .. +7; zero for padding rows)
-    // and the row's last visible position.
-    const bool row_ok = j16 < nrows;
-    const int urow = row0 + (row_ok ? j16 : 0);  // row in the unit
-    const uint16_t* qrow = a.q + ((int64_t)u * s.rows + urow) * kDqk + 8 * g;
-    bf16x8s qf[kSSteps];
+    // Q^T operands of rows 16*rb + j16 (dims 32*st + 8*g .. +7; zero for
+    // padding rows) and each row's last visible position.
+    bf16x8s qf[RB][kSSteps];
+    int tlim[RB];
 #pragma unroll
-    for (int st = 0; st < kSSteps; ++st)
-      qf[st] = row_ok ? *reinterpret_cast<const bf16x8s*>(qrow + 32 * st) : bf16x8s{};
-    const int tlim = s.is_causal ? L - s.s_q + urow / s.h_q : L - 1;
+    for (int rb = 0; rb < RB; ++rb) {
+      const int r = 16 * rb + j16;
+      const bool ok = r < s.rows;
+      const uint16_t* qrow = a.q + ((int64_t)u * s.rows + (ok ? r : 0)) * kDqk + 8 * g;
+#pragma unroll
+      for (int st = 0; st < kSSteps; ++st)
+        qf[rb][st] = ok ? *reinterpret_cast<const bf16x8s*>(qrow + 32 * st) : bf16x8s{};
+      tlim[rb] = s.is_causal ? L - s.s_q + (ok ? r : 0) / s.h_q : L - 1;
+    }
+    f32x4s o[RB][32];  // O^T: columns 16*cb + 4*g + v of row 16*rb + j16
+    float m[RB], l[RB];
+    // Pass 0 takes the probabilities against the first max a row sees.  If a
+    // row's scores later climb more than kSLag above it, the wave runs its
+    // segment again (pass 1) against the exact maximum found in pass 0, so
+    // the output never needs rescaling inside the loop.
+    float mstart[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) mstart[rb] = -INFINITY;
+    for (int pass = 0; pass < 2; ++pass) {
     // The first quarter's copies go out while Q is in flight; Q is waited for
     // here, before the loop, so that no wait for it lands inside the loop
     // (it would also wait for the copies in flight there).
     issue_quarter(a.kv, btc[kfirst], wave, kfirst * kPage + kSQuarter * wave, L, lds0, lane);
-    asm volatile("" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]), "v"(qf[5]),
-                 "v"(qf[6]), "v"(qf[7]), "v"(qf[8]));
-    asm volatile("" ::"v"(qf[9]), "v"(qf[10]), "v"(qf[11]), "v"(qf[12]), "v"(qf[13]), "v"(qf[14]),
-                 "v"(qf[15]), "v"(qf[16]), "v"(qf[17]));
-
-    f32x4s o[32];  // O^T: columns 16*cb + 4*g + v of row j16
 #pragma unroll
-    for (int cb = 0; cb < 32; ++cb) o[cb] = f32x4s{0.0f, 0.0f, 0.0f, 0.0f};
-    float m = -INFINITY;  // reference max of the row (log2 units); lags the true max by < 8
-    float l = 0.0f;       // this lane's part of the row sum
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int st = 0; st < kSSteps; ++st) asm volatile("" ::"v"(qf[rb][st]));
+
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 32; ++cb) o[rb][cb] = f32x4s{0.0f, 0.0f, 0.0f, 0.0f};
+    float mseen[RB];
+    bool restart = false;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      m[rb] = mstart[rb];   // reference max of the row (log2 units)
+      l[rb] = 0.0f;         // this lane's part of the row sum
+      mseen[rb] = -INFINITY;
+    }
 
     int cur = 0;
     for (int kt = kfirst; kt < kend; ++kt) {
@@ -169,49 +191,48 @@ __global__ void __launch_bounds__(64 * kSWaves, 1) decode_small_kernel(DecodeArg
       const uint8_t* qb = buf0 + cur * kSBuf;
       cur ^= 1;
 
-      // S^T (16 keys x 16 rows); K operands are read kSKAhead steps before
-      // their MFMA, so the LDS latency hides behind the chain.
-      f32x4s acc = f32x4s{0.0f, 0.0f, 0.0f, 0.0f};
+      // S^T (16 keys x 16 rows per block); K operands are read kSKAhead
+      // steps before their MFMAs, so the LDS latency hides behind the chain.
+      f32x4s acc[RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) acc[rb] = f32x4s{0.0f, 0.0f, 0.0f, 0.0f};
       const uint8_t* krow = qb + j16 * kSPitch + 16 * g;
       bf16x8s kop[kSKAhead];
 #pragma unroll
       for (int i = 0; i < kSKAhead; ++i) kop[i] = *reinterpret_cast<const bf16x8s*>(krow + 64 * i);
 #pragma unroll
       for (int st = 0; st < kSSteps; ++st) {
-        const bf16x8s cur = kop[st % kSKAhead];
+        const bf16x8s kcur = kop[st % kSKAhead];
         if (st + kSKAhead < kSSteps)
           kop[st % kSKAhead] = *reinterpret_cast<const bf16x8s*>(krow + 64 * (st + kSKAhead));
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, qf[st], acc, 0, 0, 0);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kcur, qf[rb][st], acc[rb], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
 
-      // Online softmax (base 2) of row j16 over keys 4g .. 4g+3 of this quarter.
-      float x[4];
-      float mx = -INFINITY;
+      // Online softmax (base 2) of each row over keys 4g .. 4g+3 of this quarter.
+      bf16x4s pf[RB];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        x[v] = tbase + 4 * g + v <= tlim ? acc[v] * s.scale_log2 : -INFINITY;
-        mx = fmaxf(mx, x[v]);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const bool grow = mx > m + kSRefresh || (m == -INFINITY && mx > -INFINITY);
-      if (__builtin_amdgcn_ballot_w64(grow)) {  // rare: the reference max moves up
-        const float f = grow ? (m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - mx)) : 1.0f;
-        if (grow) m = mx;
-        l *= f;
+      for (int rb = 0; rb < RB; ++rb) {
+        float x[4];
+        float mx = -INFINITY;
 #pragma unroll
-        for (int cb = 0; cb < 32; ++cb) {  // one block at a time: few registers in flight
-          o[cb] *= f;
-          __builtin_amdgcn_sched_barrier(0);
+        for (int v = 0; v < 4; ++v) {
+          x[v] = tbase + 4 * g + v <= tlim[rb] ? acc[rb][v] * s.scale_log2 : -INFINITY;
+          mx = fmaxf(mx, x[v]);
         }
-      }
-      bf16x4s pf;
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mseen[rb] = fmaxf(mseen[rb], mx);
+        if (m[rb] == -INFINITY) m[rb] = mx;  // first visible keys: output and sum still zero
+        restart |= mx > m[rb] + kSLag;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float p = x[v] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(x[v] - m);
-        l += p;
-        pf[v] = (__bf16)p;
+        for (int v = 0; v < 4; ++v) {
+          const float p = x[v] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(x[v] - m[rb]);
+          l[rb] += p;
+          pf[rb][v] = (__bf16)p;
+        }
       }
 
       // O^T += V^T P^T: column block cb; V^T[col][key] for keys 4g .. 4g+3 of
@@ -228,52 +249,70 @@ __global__ void __launch_bounds__(64 * kSWaves, 1) decode_small_kernel(DecodeArg
       for (int i = 0; i < kSVAhead; ++i) vop[i] = v_operand(i);
 #pragma unroll
       for (int cb = 0; cb < 32; ++cb) {
-        const bf16x4s cur = vop[cb % kSVAhead];
+        const bf16x4s vcur = vop[cb % kSVAhead];
         if (cb + kSVAhead < 32) vop[cb % kSVAhead] = v_operand(cb + kSVAhead);
-        o[cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(cur, pf, o[cb], 0, 0, 0);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          o[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vcur, pf[rb], o[rb][cb], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
+    }
+    if (!__builtin_amdgcn_ballot_w64(restart)) break;  // wave-uniform
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) mstart[rb] = mseen[rb];
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // buffer 0 is rewritten by the next pass
     }
 
     // Merge the four waves' partial results of each row: M = max of the
     // maxima, total = sum of l_w * 2^(m_w - M); each wave's output enters
     // with weight 2^(m_w - M) / total.
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    if (g == 0) {
-      m_sh[wave][j16] = m;
-      l_sh[wave][j16] = l;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      l[rb] += __shfl_xor(l[rb], 16);
+      l[rb] += __shfl_xor(l[rb], 32);
+      if (g == 0) {
+        m_sh[wave][16 * rb + j16] = m[rb];
+        l_sh[wave][16 * rb + j16] = l[rb];
+      }
     }
     __syncthreads();  // every wave is past its last quarter; the buffers are free
-    float M = -INFINITY;
+    float wgt[RB], lse2[RB];
 #pragma unroll
-    for (int w = 0; w < kSWaves; ++w) M = fmaxf(M, m_sh[w][j16]);
-    float tot = 0.0f;
+    for (int rb = 0; rb < RB; ++rb) {
+      const int r = 16 * rb + j16;
+      float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kSWaves; ++w) {
-      const float mw = m_sh[w][j16];
-      tot += mw == -INFINITY ? 0.0f : l_sh[w][j16] * __builtin_amdgcn_exp2f(mw - M);
+      for (int w = 0; w < kSWaves; ++w) M = fmaxf(M, m_sh[w][r]);
+      float tot = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kSWaves; ++w) {
+        const float mw = m_sh[w][r];
+        tot += mw == -INFINITY ? 0.0f : l_sh[w][r] * __builtin_amdgcn_exp2f(mw - M);
+      }
+      wgt[rb] = (tot > 0.0f && m[rb] != -INFINITY) ? __builtin_amdgcn_exp2f(m[rb] - M) / tot : 0.0f;
+      lse2[rb] = tot > 0.0f ? M + log2f(tot) : -INFINITY;
     }
-    const float wgt = (tot > 0.0f && m != -INFINITY) ? __builtin_amdgcn_exp2f(m - M) / tot : 0.0f;
-    const float lse2 = tot > 0.0f ? M + log2f(tot) : -INFINITY;
-    float* const fbuf = reinterpret_cast<float*>(kbuf);  // [16 rows][kSOPitch]
+    float* const fbuf = reinterpret_cast<float*>(kbuf);  // [kRows rows][kSOPitch]
 #pragma unroll
     for (int w = 0; w < kSWaves; ++w) {  // fixed order: deterministic sums
       if (wave == w) {
 #pragma unroll
-        for (int cb = 0; cb < 32; ++cb) {
-          f32x4s* dst = reinterpret_cast<f32x4s*>(fbuf + j16 * kSOPitch + 16 * cb + 4 * g);
-          const f32x4s v = o[cb] * wgt;
-          *dst = w == 0 ? v : *dst + v;
-          __builtin_amdgcn_sched_barrier(0);
-        }
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int cb = 0; cb < 32; ++cb) {
+            f32x4s* dst =
+                reinterpret_cast<f32x4s*>(fbuf + (16 * rb + j16) * kSOPitch + 16 * cb + 4 * g);
+            const f32x4s v = o[rb][cb] * wgt[rb];
+            *dst = w == 0 ? v : *dst + v;
+            __builtin_amdgcn_sched_barrier(0);
+          }
       }
       __syncthreads();
     }
     const bool direct = nsplit == 1;
     const int64_t orow0 = direct ? (int64_t)u * s.rows : ((int64_t)a.num_splits[u] + seg) * s.rows;
     uint16_t* const obase = direct ? a.out : a.ws_o;
-    for (int row = wave; row < nrows; row += kSWaves) {
+    for (int row = wave; row < s.rows; row += kSWaves) {
       const f32x4s v0 = *reinterpret_cast<const f32x4s*>(fbuf + row * kSOPitch + 8 * lane);
       const f32x4s v1 = *reinterpret_cast<const f32x4s*>(fbuf + row * kSOPitch + 8 * lane + 4);
       uint4 pk;
@@ -281,13 +320,19 @@ __global__ void __launch_bounds__(64 * kSWaves, 1) decode_small_kernel(DecodeArg
       pk.y = (uint32_t)to_bf16_bits(v0[2]) | ((uint32_t)to_bf16_bits(v0[3]) << 16);
       pk.z = (uint32_t)to_bf16_bits(v1[0]) | ((uint32_t)to_bf16_bits(v1[1]) << 16);
       pk.w = (uint32_t)to_bf16_bits(v1[2]) | ((uint32_t)to_bf16_bits(v1[3]) << 16);
-      *reinterpret_cast<uint4*>(obase + (orow0 + row0 + row) * kDv + 8 * lane) = pk;
+      *reinterpret_cast<uint4*>(obase + (orow0 + row) * kDv + 8 * lane) = pk;
     }
-    if (wave == 0 && g == 0 && row_ok) {
-      if (direct)
-        a.lse[(int64_t)u * s.rows + row0 + j16] = s.natural ? lse2 * 0.69314718055994531f : lse2;
-      else
-        a.ws_lse[((int64_t)a.num_splits[u] + seg) * s.rows + row0 + j16] = lse2;
+    if (wave == 0 && g == 0) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const int r = 16 * rb + j16;
+        if (r < s.rows) {
+          if (direct)
+            a.lse[(int64_t)u * s.rows + r] = s.natural ? lse2[rb] * 0.69314718055994531f : lse2[rb];
+          else
+            a.ws_lse[((int64_t)a.num_splits[u] + seg) * s.rows + r] = lse2[rb];
+        }
+      }
     }
     __syncthreads();  // the merge buffer is read before the next segment's copies
   }
@@ -300,9 +345,10 @@ bool small_decode_applies(const Shape& s) {
 }
 
 hipError_t launch_decode_small(const DecodeArgs& a, hipStream_t stream) {
-  const int span = 8 * a.s.groups;
-  const int grid = ((a.num_parts + 7) / 8) * span;
-  hipLaunchKernelGGL(decode_small_kernel, dim3(grid), dim3(64 * kSWaves), 0, stream, a);
+  if (a.s.rows <= 16)
+    hipLaunchKernelGGL(decode_small_kernel<1>, dim3(a.num_parts), dim3(64 * kSWaves), 0, stream, a);
+  else
+    hipLaunchKernelGGL(decode_small_kernel<2>, dim3(a.num_parts), dim3(64 * kSWaves), 0, stream, a);
   return hipGetLastError();
 }
 

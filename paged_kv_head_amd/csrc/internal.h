@@ -11,11 +11,8 @@ constexpr int kDv = 512;
 constexpr int kPage = 64;          // tokens per page == keys per tile
 constexpr int kRowsPerGroup = 128; // query rows one workgroup owns
 // Dense bf16 units of at most kSmallMaxRows rows run on the small-head
-// kernel, whose workgroups own kSmallRowsPerGroup rows each.  Measured: it
-// is faster than the main kernel for one row group (h_q * s_q <= 16) and
-// slower from two on (the main kernel reads each page once per 128 rows).
-constexpr int kSmallRowsPerGroup = 16;
-constexpr int kSmallMaxRows = 16;
+// kernel (one workgroup per part, all rows of the unit in it).
+constexpr int kSmallMaxRows = 32;
 constexpr int kSplitPenalty = 3;   // scheduler cost of one segment, in blocks (measured: a
                                     // segment's prologue + epilogue ~ 3 tiles)
 constexpr int kMaxUnits = 16384;   // metadata kernel keeps per-unit arrays in LDS
