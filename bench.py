@@ -186,7 +186,7 @@ def bench_writer(args):
     pages = int((w.block_table >= 0).sum())
     alg_bytes = tokens * (1152 + 656) + 4 * pages + 4 * B
     achieved = alg_bytes / (k_ms * 1e-3) / 1e9
-    tr = traffic_record(w.name, "kv_writer.hip", "kv_quantize_fp8")
+    tr = traffic_record(w.name, "kv_writer.hip", "kv_writer")
     cpu = None if args.no_cpu_baseline else writer_cpu_baseline(w)
     line = {
         "metric": "FP8 KV writer GB/s (bf16 576-value rows -> 656-byte paged FP8 rows), % of HBM roofline",

@@ -43,10 +43,13 @@ def test_small_heads_base_and_scale(natural, scale):
     assert_close(out, lse, ref_out, ref_lse, what=f"natural={natural} scale={scale}")
 
 
-def test_small_heads_growing_scores_rescale():
-    """Scores that climb by far more than the refresh threshold force the
-    lazy rescale of the running output many times."""
-    w = synth.make_workload("small_grow", batch=2, h_q=32, s_q=1, seqlens=[900, 300], seed=73,
+@pytest.mark.parametrize("h_q", [16, 32, 128])
+def test_small_heads_growing_scores_rescale(h_q):
+    """Scores that climb by far more than any lag the running max may have
+    (here by ~500 in log2 units over the sequence) force the recovery path:
+    a second pass of the segment on the small-head kernel (h_q 16, 32), the
+    flush path on the main kernel (h_q 128)."""
+    w = synth.make_workload("small_grow", batch=2, h_q=h_q, s_q=1, seqlens=[900, 300], seed=73,
                             slack=0)
     kv = w.kv.copy()
     for b in range(2):
