@@ -145,3 +145,33 @@ def test_writer_full_size_fill_sampled():
     # every written row has finite scales (no poison left in a referenced row)
     scales = got[used][:, :, 512:528].copy().view(np.float32)
     assert np.isfinite(scales).all()
+
+
+def test_writer_then_fp8_decode_end_to_end():
+    """Decode over a cache the GPU writer filled equals the oracle's decode
+    over the cache the oracle's writer filled (the two caches are
+    byte-identical, and the FP8 decode reads them the same way)."""
+    import math
+
+    from tests.harness import assert_close, run
+
+    rng = np.random.default_rng(31)
+    B, s_q, h_q = 3, 2, 128
+    lens = np.array([300, 1, 777], dtype=np.int32)
+    w = synth.make_workload("writer_e2e", batch=B, h_q=h_q, s_q=s_q, seqlens=lens, seed=32,
+                            kv_format=synth.KV_FP8_656, is_causal=1)
+    n_new = int(lens.max())
+    rows = synth.bf16_bits_from_f32(rng.standard_normal((B, n_new, 576)).astype(np.float32))
+    app = synth.AppendWorkload(name="e2e", kv_new=rows, start_pos=np.zeros(B, np.int32),
+                               block_table=w.block_table, pool=w.kv.copy())
+    # positions past a sequence's length fill its last page's tail (masked by the decode)
+    # or have no page (-1 in the table): skipped
+    gpu_pool = gpu_append(app)
+    ref_pool = oracle_append(app)
+    assert_pools_equal(gpu_pool, ref_pool)
+    w.kv = gpu_pool
+    out, lse = run(w)
+    w.kv = ref_pool
+    ref_out, ref_lse = oracle.mla_decode(w)
+    assert_close(out, lse, ref_out, ref_lse, what="writer -> fp8 decode")
+    assert math.isfinite(float(np.abs(out).max()))
