@@ -189,6 +189,20 @@ mla_status mla_decode_combine(const mla_problem* p, int32_t num_parts, const int
                               const void* workspace, size_t workspace_bytes, void* out,
                               float* lse, void* stream);
 
+/* Device-side check of the preconditions the decode calls leave unchecked
+ * (they read device memory): every cache_seqlens[b] in
+ * [0, max_pages_per_seq * 64], and every block-table entry a visible
+ * position can reach (block_table[b][j] for j < ceil(L_b / 64)) in
+ * [0, num_pages).  For sparse problems the same pages bound what listed
+ * indices can reach.  Writes result[0] = number of sequences that violate
+ * either, result[1] = the first such sequence (-1 if none); result is a
+ * device int32[2].  Meant for debugging and input validation outside the
+ * hot loop (one workgroup; cost grows with batch * pages).  Source: the
+ * MAX kernels guide, "max.nn.kernels 内核封装模块全解析", section 输入校验
+ * (inputs are validated and the offending argument reported). */
+mla_status mla_decode_check_inputs(const mla_problem* p, const int32_t* block_table,
+                                   const int32_t* cache_seqlens, int32_t* result, void* stream);
+
 /* FP8 KV writer: quantises new latent tokens into the 656-byte layout
  * (MLA_KV_FP8_656) and stores each at its paged slot.
  *   kv_new       bf16  [batch, n_new, 576]  (16-byte aligned; device)

@@ -21,7 +21,7 @@ __all__ = [
     "mla_decode_workspace_bytes", "mla_decode_get_metadata", "mla_decode_paged",
     "mla_decode_paged_fp8", "mla_decode_sparse_fp8", "mla_decode_combine", "mla_last_error",
     "mla_decode_with_kvcache", "mla_kv_quantize_fp8", "mla_sparse_prefill_workspace_bytes",
-    "mla_sparse_prefill", "mla_sparse_prefill_num_parts",
+    "mla_sparse_prefill", "mla_sparse_prefill_num_parts", "mla_decode_check_inputs",
 ]
 
 MLA_KV_BF16 = 0
@@ -96,13 +96,15 @@ def _load():
     lib.mla_decode_sparse_fp8.argtypes = [PP, P, P, P, P, P, P, I32, P, P, SZ, P, P, P]
     lib.mla_decode_combine.argtypes = [PP, I32, P, P, SZ, P, P, P]
     lib.mla_kv_quantize_fp8.argtypes = [I32, I32, I32, I32, I32, P, P, P, P, P]
+    lib.mla_decode_check_inputs.argtypes = [PP, P, P, P, P]
     lib.mla_sparse_prefill_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32, ctypes.POINTER(SZ)]
     lib.mla_sparse_prefill.argtypes = [I32, I32, I32, I32, I32, I32, ctypes.c_float, P, P, P, I32, P,
                                        SZ, P, P, P]
     for fn in ("mla_decode_num_parts", "mla_decode_metadata_size", "mla_decode_workspace_bytes",
                "mla_decode_get_metadata", "mla_decode_paged", "mla_decode_paged_fp8",
                "mla_decode_sparse_fp8", "mla_decode_combine", "mla_kv_quantize_fp8",
-               "mla_sparse_prefill_workspace_bytes", "mla_sparse_prefill"):
+               "mla_sparse_prefill_workspace_bytes", "mla_sparse_prefill",
+               "mla_decode_check_inputs"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.mla_last_error.argtypes = []
     lib.mla_last_error.restype = ctypes.c_char_p
@@ -242,6 +244,19 @@ def mla_decode_combine(p: Problem, num_parts, num_splits, workspace, out, lse, s
     _check(_load().mla_decode_combine(
         ctypes.byref(p), int(num_parts), _ptr(num_splits), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def mla_decode_check_inputs(p: Problem, block_table, cache_seqlens, stream=None) -> Tuple[int, int]:
+    """Checks cache lengths and the reachable block-table entries on the
+    device; returns (number of bad sequences, first bad sequence or -1).
+    Synchronises the stream to read the answer."""
+    _expect("block_table", block_table, torch.int32, p.batch * p.max_pages_per_seq)
+    _expect("cache_seqlens", cache_seqlens, torch.int32, p.batch)
+    res = torch.empty(2, dtype=torch.int32, device=cache_seqlens.device)
+    _check(_load().mla_decode_check_inputs(ctypes.byref(p), _ptr(block_table), _ptr(cache_seqlens),
+                                           _ptr(res), _stream(stream)))
+    r = res.cpu()
+    return int(r[0]), int(r[1])
 
 
 def mla_kv_quantize_fp8(kv_new, start_pos, block_table, kv_pool, page_size: int = 64,

@@ -285,6 +285,19 @@ mla_status mla_decode_combine(const mla_problem* p, int32_t num_parts, const int
                     "combine kernel launch");
 }
 
+mla_status mla_decode_check_inputs(const mla_problem* p, const int32_t* block_table,
+                                   const int32_t* cache_seqlens, int32_t* result, void* stream) {
+  mla::Shape s;
+  MLA_CHECK(check_problem(p, &s));
+  MLA_CHECK(check_ptr(result, "result", 4));
+  if (s.batch > 0) {
+    MLA_CHECK(check_ptr(block_table, "block_table", 4));
+    MLA_CHECK(check_ptr(cache_seqlens, "cache_seqlens", 4));
+  }
+  return hip_status(mla::launch_check_inputs(s, block_table, cache_seqlens, result, (hipStream_t)stream),
+                    "input check kernel launch");
+}
+
 mla_status mla_kv_quantize_fp8(int32_t batch, int32_t n_new, int32_t page_size,
                                int32_t num_pages, int32_t max_pages_per_seq, const void* kv_new,
                                const int32_t* start_pos, const int32_t* block_table,

@@ -79,6 +79,8 @@ hipError_t launch_kv_quantize_fp8(int32_t batch, int32_t n_new, int32_t num_page
                                   int32_t max_pages, const uint16_t* kv_new,
                                   const int32_t* start_pos, const int32_t* block_table,
                                   uint8_t* kv_pool, hipStream_t stream);
+hipError_t launch_check_inputs(const Shape& s, const int32_t* block_table, const int32_t* seqlens,
+                               int32_t* result, hipStream_t stream);
 hipError_t launch_identity_table(int32_t* table, int32_t pages, int32_t* seqlen, int32_t s_kv,
                                  hipStream_t stream);
 

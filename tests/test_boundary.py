@@ -231,3 +231,16 @@ def test_prefill_workspace_grows_with_chunk_not_beyond():
     c = mla.mla_sparse_prefill_workspace_bytes(100000, 128, 5000, 64, 0, 256)
     assert a < b == c
     assert call_prefill(s_q=0, ws_bytes=mla.mla_sparse_prefill_workspace_bytes(0, 16, 100, 8, 0, 4)) == mla.MLA_OK
+
+
+def test_check_inputs_rejects_bad_arguments():
+    lib = mla._load()
+    p = good()
+    assert lib.mla_decode_check_inputs(None, ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE),
+                                       ctypes.c_void_p(FAKE), None) == mla.MLA_ERR_INVALID_ARGUMENT
+    assert lib.mla_decode_check_inputs(ctypes.byref(p), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE),
+                                       None, None) == mla.MLA_ERR_INVALID_ARGUMENT
+    assert mla.mla_last_error().startswith("result")
+    assert lib.mla_decode_check_inputs(ctypes.byref(p), None, ctypes.c_void_p(FAKE),
+                                       ctypes.c_void_p(FAKE), None) == mla.MLA_ERR_INVALID_ARGUMENT
+    assert mla.mla_last_error().startswith("block_table")

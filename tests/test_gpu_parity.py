@@ -233,3 +233,23 @@ def test_flush_path_growing_scores():
         out, lse = run(w, num_parts=parts, softmax_scale=0.02)
         ref_out, ref_lse = oracle.mla_decode(w, softmax_scale=0.02)
         assert_close(out, lse, ref_out, ref_lse, what=f"flush parts={parts}")
+
+
+def test_check_inputs_finds_bad_lengths_and_pages():
+    """The device-side check flags lengths outside [0, max_pages * 64] and
+    reachable block-table entries outside the pool, and nothing else."""
+    w = synth.make_workload("t", batch=6, h_q=16, s_q=1, seqlens=[100, 0, 64, 300, 1, 129], seed=45,
+                            max_pages_per_seq=6)
+    p = mla.Problem.make(batch=w.batch, s_q=1, h_q=16, num_pages=w.num_pages,
+                         max_pages_per_seq=w.max_pages_per_seq, softmax_scale=w.softmax_scale)
+    _, _, bt, sl, _ = to_device(w)
+    assert mla.mla_decode_check_inputs(p, bt, sl) == (0, -1)
+    bt_bad = w.block_table.copy()
+    bt_bad[3, 4] = w.num_pages         # reachable page (L = 300 uses pages 0..4): bad
+    bt_bad[0, 5] = -7                  # unreachable slot (L = 100 uses pages 0..1): ignored
+    sl_bad = w.cache_seqlens.copy()
+    sl_bad[5] = 6 * 64 + 1             # longer than the table row allows
+    sl_bad[1] = -1
+    n, first = mla.mla_decode_check_inputs(p, torch.from_numpy(bt_bad).cuda(),
+                                           torch.from_numpy(sl_bad).cuda())
+    assert (n, first) == (3, 1)
