@@ -21,6 +21,13 @@ __device__ inline uint16_t bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, h);
 }
 
+// Splits are merged online, in order, kAhead at a time: the loads of a
+// group (each split's lse and this lane's 8 output values) are issued
+// together, so a row costs about n / kAhead memory round trips instead of
+// two per split.  With M the running max of the lse values seen, the
+// running sum tot and output acc are kept relative to 2^M.
+constexpr int kAhead = 4;
+
 __global__ void __launch_bounds__(64 * kRowsPerBlock)
 combine_kernel(Shape s, const int32_t* __restrict__ num_splits, const float* __restrict__ ws_lse,
                const uint16_t* __restrict__ ws_o, uint16_t* __restrict__ out,
@@ -36,23 +43,35 @@ combine_kernel(Shape s, const int32_t* __restrict__ num_splits, const float* __r
   float acc[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
-  float M = -INFINITY;
-  for (int sp = 0; sp < n; ++sp) M = fmaxf(M, ws_lse[(int64_t)(first + sp) * s.rows + r]);
-  float lse2 = -INFINITY;
-  if (M != -INFINITY) {
-    float tot = 0.0f;
-    for (int sp = 0; sp < n; ++sp) {
+  float M = -INFINITY, tot = 0.0f;
+  for (int s0 = 0; s0 < n; s0 += kAhead) {
+    float ls[kAhead];
+    uint4 src[kAhead];
+#pragma unroll
+    for (int k = 0; k < kAhead; ++k) {  // all loads of the group first
+      const int sp = s0 + k < n ? s0 + k : n - 1;  // in range; a repeated split is given weight 0
       const int64_t wrow = (int64_t)(first + sp) * s.rows + r;
-      const float w = __builtin_amdgcn_exp2f(ws_lse[wrow] - M);
-      tot += w;
-      const uint4 src = *reinterpret_cast<const uint4*>(ws_o + wrow * kDv + lane * 8);
-      const uint32_t words[4] = {src.x, src.y, src.z, src.w};
+      ls[k] = s0 + k < n ? ws_lse[wrow] : -INFINITY;
+      src[k] = *reinterpret_cast<const uint4*>(ws_o + wrow * kDv + lane * 8);
+    }
+#pragma unroll
+    for (int k = 0; k < kAhead; ++k) {
+      if (ls[k] == -INFINITY) continue;  // an empty split (or past the end) adds nothing
+      const float Mn = fmaxf(M, ls[k]);
+      const float fo = __builtin_amdgcn_exp2f(M - Mn);  // 0 while M is -inf
+      const float w = __builtin_amdgcn_exp2f(ls[k] - Mn);
+      tot = tot * fo + w;
+      const uint32_t words[4] = {src[k].x, src[k].y, src[k].z, src[k].w};
 #pragma unroll
       for (int c = 0; c < 4; ++c) {  // bf16 -> fp32 is exact: the high half of the word
-        acc[2 * c] += w * __uint_as_float(words[c] << 16);
-        acc[2 * c + 1] += w * __uint_as_float(words[c] & 0xffff0000u);
+        acc[2 * c] = acc[2 * c] * fo + w * __uint_as_float(words[c] << 16);
+        acc[2 * c + 1] = acc[2 * c + 1] * fo + w * __uint_as_float(words[c] & 0xffff0000u);
       }
+      M = Mn;
     }
+  }
+  float lse2 = -INFINITY;
+  if (M != -INFINITY) {
     const float inv = 1.0f / tot;
 #pragma unroll
     for (int c = 0; c < 8; ++c) acc[c] *= inv;
