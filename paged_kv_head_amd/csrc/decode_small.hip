@@ -43,12 +43,28 @@ typedef __bf16 bf16x8s __attribute__((ext_vector_type(8)));
 typedef float f32x4s __attribute__((ext_vector_type(4)));
 
 constexpr int kSWaves = 4;
-constexpr int kSQuarter = 16;                                 // keys per wave per page
-constexpr int kSPitch = 1168;                                 // LDS bytes per key row
-constexpr int kSRowSlots = kSPitch / 16;                      // 73 16-byte slots
-constexpr int kSCopies = (kSQuarter * kSRowSlots + 63) / 64;  // 19 copies of 1 KiB
-constexpr int kSBuf = kSCopies * 1024;                        // 19456 bytes per buffer
-constexpr int kSSteps = kDqk / 32;                            // 18 k-steps of 32 dims
+constexpr int kSQuarter = 16;  // keys per wave per page
+
+// LDS layout of a staged quarter tile.  bf16 rows (1152 bytes) get a pitch
+// of 1168 bytes; FP8 rows (656 bytes) keep theirs.  Either way 16
+// consecutive rows start on 16 distinct 4-bank groups, so the operand reads
+// below are free of bank conflicts.  Slot 64*c + lane of a buffer is
+// 16-byte chunk `slot % kSlots` of row `slot / kSlots`.
+template <int FMT>
+struct SmallLayout;
+template <>
+struct SmallLayout<0> {
+  static constexpr int kRowBytes = 1152, kPitch = 1168, kSlots = 73, kDataSlots = 72;
+};
+template <>
+struct SmallLayout<1> {
+  static constexpr int kRowBytes = 656, kPitch = 656, kSlots = 41, kDataSlots = 41;
+};
+template <int FMT>
+constexpr int kSCopies = (kSQuarter * SmallLayout<FMT>::kSlots + 63) / 64;  // 19 (bf16), 11 (FP8)
+template <int FMT>
+constexpr int kSBuf = kSCopies<FMT> * 1024;
+constexpr int kSSteps = kDqk / 32;  // 18 k-steps of 32 dims (16 NoPE, 2 RoPE)
 constexpr int kSOPitch = 516;                                 // floats per merge-buffer row
 // The running max a row's probabilities are taken against may lag the true
 // max by up to this much (log2 units): probabilities stay <= 2^64, sums far
@@ -78,32 +94,59 @@ typedef __bf16 bf16x4s __attribute__((ext_vector_type(4)));
 using cint32s = const __attribute__((address_space(4))) int32_t;
 
 // Copies of one quarter tile (keys 16*wave .. +15 of page `page`, logical
-// positions tbase ..) into the LDS buffer at lds: slot 64*c + lane of the
-// buffer is 16-byte chunk `chunk` of key row `key` (73 slots per row, the
-// last one padding); keys at or past L come from the zero row.
+// positions tbase ..) into the LDS buffer at lds (layout above); padding
+// slots and keys at or past L come from the zero row.
+template <int FMT>
 __device__ inline void issue_quarter(const uint8_t* __restrict__ kv, int page, int wave, int tbase,
                                      int L, uint32_t lds, int lane) {
-  const uint8_t* src0 = kv + ((int64_t)page * kPage + kSQuarter * wave) * (kDqk * 2);
-  int key = 0, chunk = lane;  // stepping by 64 slots wraps the chunk at most once
+  using Lay = SmallLayout<FMT>;
+  const uint8_t* src0 = kv + ((int64_t)page * kPage + kSQuarter * wave) * Lay::kRowBytes;
+  // slot 64*c + lane = (key, chunk); stepping by 64 slots wraps the chunk
+  // at most once (73 slots a row) or twice (41)
+  int key = lane / Lay::kSlots, chunk = lane % Lay::kSlots;
 #pragma unroll 1
-  for (int c = 0; c < kSCopies; ++c) {
-    const bool ok = key < kSQuarter && chunk < kSRowSlots - 1 && tbase + key < L;
-    const void* src = ok ? (const void*)(src0 + key * (kDqk * 2) + chunk * 16) : (const void*)g_zero16;
+  for (int c = 0; c < kSCopies<FMT>; ++c) {
+    const bool ok = key < kSQuarter && chunk < Lay::kDataSlots && tbase + key < L;
+    const void* src = ok ? (const void*)(src0 + key * Lay::kRowBytes + chunk * 16) : (const void*)g_zero16;
     dma16_to_lds(src, lds + 1024 * c);
     chunk += 64;
-    if (chunk >= kSRowSlots) {
-      chunk -= kSRowSlots;
+    while (chunk >= Lay::kSlots) {
+      chunk -= Lay::kSlots;
       ++key;
     }
   }
 }
 
-// RB 16-row MFMA blocks per workgroup (the whole unit: RB = 1 for up to 16
-// rows, 2 for up to 32).  K and V operands read from LDS feed all RB blocks.
-template <int RB>
+// bf16(float(e4m3 code) * scale) for 8 codes (bytes of lo, then hi): the
+// FP8 dequantisation rule of the 656-byte row, product in fp32, one
+// rounding to bf16 ("为什么 FlashMLA 的解码内核能跑到 660 TFLOPS", section 设计 2).
+__device__ inline bf16x8s dequant8(uint32_t lo, uint32_t hi, float sc) {
+  const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false);
+  const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
+  const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
+  const auto d = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+  bf16x8s r;
+  r[0] = (__bf16)(a[0] * sc);
+  r[1] = (__bf16)(a[1] * sc);
+  r[2] = (__bf16)(b[0] * sc);
+  r[3] = (__bf16)(b[1] * sc);
+  r[4] = (__bf16)(c[0] * sc);
+  r[5] = (__bf16)(c[1] * sc);
+  r[6] = (__bf16)(d[0] * sc);
+  r[7] = (__bf16)(d[1] * sc);
+  return r;
+}
+
+// FMT: cache row format (0 bf16, 1 the 656-byte FP8 row).  RB 16-row MFMA
+// blocks per workgroup (the whole unit: RB = 1 for up to 16 rows, 2 for up
+// to 32).  K and V operands read from LDS feed all RB blocks.
+template <int FMT, int RB>
 __global__ void __launch_bounds__(64 * kSWaves, 1) decode_small_kernel(DecodeArgs a) {
   constexpr int kRows = 16 * RB;
-  __shared__ __attribute__((aligned(16))) uint8_t kbuf[kSWaves * 2 * kSBuf];
+  constexpr int kPitch = SmallLayout<FMT>::kPitch;
+  constexpr int kBuf = kSBuf<FMT>;
+  constexpr int kCopies = kSCopies<FMT>;
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf[kSWaves * 2 * kBuf];
   __shared__ float m_sh[kSWaves][kRows];
   __shared__ float l_sh[kSWaves][kRows];
 
@@ -117,7 +160,7 @@ __global__ void __launch_bounds__(64 * kSWaves, 1) decode_small_kernel(DecodeArg
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int j16 = lane & 15;  // row within a 16-row block (score and output)
   const int g = lane >> 4;    // lane group: keys 4g .. 4g+3; dims 8g .. of a k-step
-  uint8_t* const buf0 = kbuf + wave * 2 * kSBuf;
+  uint8_t* const buf0 = kbuf + wave * 2 * kBuf;
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)buf0);
 
@@ -158,7 +201,7 @@ __global__ void __launch_bounds__(64 * kSWaves, 1) decode_small_kernel(DecodeArg
     // The first quarter's copies go out while Q is in flight; Q is waited for
     // here, before the loop, so that no wait for it lands inside the loop
     // (it would also wait for the copies in flight there).
-    issue_quarter(a.kv, btc[kfirst], wave, kfirst * kPage + kSQuarter * wave, L, lds0, lane);
+    issue_quarter<FMT>(a.kv, btc[kfirst], wave, kfirst * kPage + kSQuarter * wave, L, lds0, lane);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -183,12 +226,12 @@ __global__ void __launch_bounds__(64 * kSWaves, 1) decode_small_kernel(DecodeArg
       if (kt + 1 < kend) {
         // the other buffer was last read by the previous quarter's products
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        issue_quarter(a.kv, btc[kt + 1], wave, tbase + kPage, L, lds0 + (cur ^ 1) * kSBuf, lane);
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kSCopies) : "memory");  // this quarter has landed
+        issue_quarter<FMT>(a.kv, btc[kt + 1], wave, tbase + kPage, L, lds0 + (cur ^ 1) * kBuf, lane);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kCopies) : "memory");  // this quarter has landed
       } else {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       }
-      const uint8_t* qb = buf0 + cur * kSBuf;
+      const uint8_t* qb = buf0 + cur * kBuf;
       cur ^= 1;
 
       // S^T (16 keys x 16 rows per block); K operands are read kSKAhead
@@ -196,15 +239,31 @@ __global__ void __launch_bounds__(64 * kSWaves, 1) decode_small_kernel(DecodeArg
       f32x4s acc[RB];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) acc[rb] = f32x4s{0.0f, 0.0f, 0.0f, 0.0f};
-      const uint8_t* krow = qb + j16 * kSPitch + 16 * g;
-      bf16x8s kop[kSKAhead];
+      // K operand of step st for key j16, dims 32*st + 8*g .. +7: bf16 rows are
+      // read as is; FP8 rows give 8 codes (NoPE steps, dequantised with the
+      // row's scale of their 128-dim tile) or 8 bf16 RoPE values (steps 16, 17).
+      const uint8_t* krow = qb + j16 * kPitch;
+      f32x4s ksc = f32x4s{0.0f, 0.0f, 0.0f, 0.0f};
+      if constexpr (FMT == 1) ksc = *reinterpret_cast<const f32x4s*>(krow + 512);
+      auto k_raw = [&](int st) -> uint4 {
+        if constexpr (FMT == 0) return *reinterpret_cast<const uint4*>(krow + 64 * st + 16 * g);
+        if (st < 16) {
+          const uint2 c = *reinterpret_cast<const uint2*>(krow + 32 * st + 8 * g);
+          return make_uint4(c.x, c.y, 0u, 0u);
+        }
+        return *reinterpret_cast<const uint4*>(krow + 528 + 64 * (st - 16) + 16 * g);
+      };
+      auto k_operand = [&](uint4 raw, int st) -> bf16x8s {
+        if (FMT == 1 && st < 16) return dequant8(raw.x, raw.y, ksc[st >> 2]);
+        return __builtin_bit_cast(bf16x8s, raw);
+      };
+      uint4 kop[kSKAhead];
 #pragma unroll
-      for (int i = 0; i < kSKAhead; ++i) kop[i] = *reinterpret_cast<const bf16x8s*>(krow + 64 * i);
+      for (int i = 0; i < kSKAhead; ++i) kop[i] = k_raw(i);
 #pragma unroll
       for (int st = 0; st < kSSteps; ++st) {
-        const bf16x8s kcur = kop[st % kSKAhead];
-        if (st + kSKAhead < kSSteps)
-          kop[st % kSKAhead] = *reinterpret_cast<const bf16x8s*>(krow + 64 * (st + kSKAhead));
+        const bf16x8s kcur = k_operand(kop[st % kSKAhead], st);
+        if (st + kSKAhead < kSSteps) kop[st % kSKAhead] = k_raw(st + kSKAhead);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
           acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kcur, qf[rb][st], acc[rb], 0, 0, 0);
@@ -236,21 +295,51 @@ __global__ void __launch_bounds__(64 * kSWaves, 1) decode_small_kernel(DecodeArg
       }
 
       // O^T += V^T P^T: column block cb; V^T[col][key] for keys 4g .. 4g+3 of
-      // column 16*cb + j16, read as 4 bf16.
-      const __bf16* vcol = reinterpret_cast<const __bf16*>(qb) + 4 * g * (kSPitch / 2) + j16;
-      auto v_operand = [&](int cb) {
-        bf16x4s v;
+      // column 16*cb + j16: 4 bf16 values, or 4 FP8 codes dequantised with
+      // their rows' scales of tile cb / 8.
+      const uint8_t* vrow = qb + 4 * g * kPitch;
+      f32x4s vsc[4];
+      if constexpr (FMT == 1) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = vcol[e * (kSPitch / 2) + 16 * cb];
-        return v;
+        for (int e = 0; e < 4; ++e) vsc[e] = *reinterpret_cast<const f32x4s*>(vrow + e * kPitch + 512);
+      }
+      auto v_raw = [&](int cb) -> uint4 {
+        uint4 r;
+        if constexpr (FMT == 0) {
+          const uint16_t* vc = reinterpret_cast<const uint16_t*>(vrow) + 16 * cb + j16;
+          r.x = vc[0];
+          r.y = vc[kPitch / 2];
+          r.z = vc[kPitch];
+          r.w = vc[3 * (kPitch / 2)];
+        } else {
+          const uint8_t* vc = vrow + 16 * cb + j16;
+          r.x = vc[0];
+          r.y = vc[kPitch];
+          r.z = vc[2 * kPitch];
+          r.w = vc[3 * kPitch];
+        }
+        return r;
       };
-      bf16x4s vop[kSVAhead];  // V^T operands read kSVAhead column blocks ahead
+      auto v_operand = [&](uint4 r, int cb) -> bf16x4s {
+        if constexpr (FMT == 0) {
+          return __builtin_bit_cast(bf16x4s, make_uint2(r.x | (r.y << 16), r.z | (r.w << 16)));
+        } else {
+          const int t = cb >> 3;
+          bf16x4s v;
+          v[0] = (__bf16)(__builtin_amdgcn_cvt_pk_f32_fp8(r.x, false)[0] * vsc[0][t]);
+          v[1] = (__bf16)(__builtin_amdgcn_cvt_pk_f32_fp8(r.y, false)[0] * vsc[1][t]);
+          v[2] = (__bf16)(__builtin_amdgcn_cvt_pk_f32_fp8(r.z, false)[0] * vsc[2][t]);
+          v[3] = (__bf16)(__builtin_amdgcn_cvt_pk_f32_fp8(r.w, false)[0] * vsc[3][t]);
+          return v;
+        }
+      };
+      uint4 vop[kSVAhead];  // V^T operands read kSVAhead column blocks ahead
 #pragma unroll
-      for (int i = 0; i < kSVAhead; ++i) vop[i] = v_operand(i);
+      for (int i = 0; i < kSVAhead; ++i) vop[i] = v_raw(i);
 #pragma unroll
       for (int cb = 0; cb < 32; ++cb) {
-        const bf16x4s vcur = vop[cb % kSVAhead];
-        if (cb + kSVAhead < 32) vop[cb % kSVAhead] = v_operand(cb + kSVAhead);
+        const bf16x4s vcur = v_operand(vop[cb % kSVAhead], cb);
+        if (cb + kSVAhead < 32) vop[cb % kSVAhead] = v_raw(cb + kSVAhead);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
           o[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vcur, pf[rb], o[rb][cb], 0, 0, 0);
@@ -341,14 +430,17 @@ __global__ void __launch_bounds__(64 * kSWaves, 1) decode_small_kernel(DecodeArg
 }  // namespace
 
 bool small_decode_applies(const Shape& s) {
-  return s.kv_format == 0 && s.topk == 0 && s.rows <= kSmallMaxRows;
+  return s.topk == 0 && s.rows <= (s.kv_format == 0 ? kSmallMaxRows : kSmallMaxRowsFp8);
 }
 
 hipError_t launch_decode_small(const DecodeArgs& a, hipStream_t stream) {
-  if (a.s.rows <= 16)
-    hipLaunchKernelGGL(decode_small_kernel<1>, dim3(a.num_parts), dim3(64 * kSWaves), 0, stream, a);
+  const dim3 grid(a.num_parts), block(64 * kSWaves);
+  if (a.s.kv_format == 1)
+    hipLaunchKernelGGL((decode_small_kernel<1, 1>), grid, block, 0, stream, a);
+  else if (a.s.rows <= 16)
+    hipLaunchKernelGGL((decode_small_kernel<0, 1>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL(decode_small_kernel<2>, dim3(a.num_parts), dim3(64 * kSWaves), 0, stream, a);
+    hipLaunchKernelGGL((decode_small_kernel<0, 2>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

@@ -10,9 +10,11 @@ constexpr int kDqk = 576;
 constexpr int kDv = 512;
 constexpr int kPage = 64;          // tokens per page == keys per tile
 constexpr int kRowsPerGroup = 128; // query rows one workgroup owns
-// Dense bf16 units of at most kSmallMaxRows rows run on the small-head
-// kernel (one workgroup per part, all rows of the unit in it).
+// Dense units of at most kSmallMaxRows rows (bf16 cache) or
+// kSmallMaxRowsFp8 rows (FP8 cache) run on the small-head kernel (one
+// workgroup per part, all rows of the unit in it).
 constexpr int kSmallMaxRows = 32;
+constexpr int kSmallMaxRowsFp8 = 16;
 constexpr int kSplitPenalty = 3;   // scheduler cost of one segment, in blocks (measured: a
                                     // segment's prologue + epilogue ~ 3 tiles)
 constexpr int kMaxUnits = 16384;   // metadata kernel keeps per-unit arrays in LDS
