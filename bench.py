@@ -45,12 +45,14 @@ def parse():
     ap.add_argument("--num-parts", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-units", type=int, default=None)
-    ap.add_argument("--kernel", choices=["decode", "small", "writer", "prefill"], default="decode",
+    ap.add_argument("--kernel", choices=["decode", "small", "small_fp8", "writer", "prefill"],
+                    default="decode",
                     help="decode: the decode step (default); writer: the FP8 KV writer filling "
                          "128 sequences x 4096 new tokens; prefill: sparse prefill, 4096 query "
                          "tokens x 128 heads over a 32768-row cache, topk 2048; small: decode with "
                          "16 query heads (an 8-way head split of the 128), batch 128, lengths "
-                         "U[1024, 8192]")
+                         "U[1024, 8192]; small_fp8: the same heads over the 656-byte FP8 cache, "
+                         "lengths U[8192, 32768]")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run three 1 GiB device-to-device copies (reference for the HBM byte "
                          "counters under rocprofv3), print nothing else")
@@ -330,6 +332,10 @@ def main():
     if args.kernel == "small":
         w = synth.make_workload(SMALL_WORKLOAD["name"], batch=128, h_q=16, s_q=1,
                                 seqlens=synth.Uniform(1024, 8192), seed=1006, max_pages_per_seq=128)
+    elif args.kernel == "small_fp8":
+        w = synth.make_workload("b128_h16_sq1_fp8_l8k_32k", batch=128, h_q=16, s_q=1,
+                                seqlens=synth.Uniform(8192, 32768), seed=1008,
+                                max_pages_per_seq=512, kv_format=synth.KV_FP8_656)
     else:
         w = synth.config_workload(args.config)
     print(f"[bench] workload {w.name}: generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
@@ -403,8 +409,8 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     tr = traffic_record(w.name)
     roof["traffic"] = None if tr is None else tr["hbm_bytes_per_launch"]
-    roof["kernel"] = "decode_small_kernel" if w.s_q * w.h_q <= 16 and w.kv_format == 0 and w.topk == 0 \
-        else "decode_kernel"
+    small = w.topk == 0 and w.s_q * w.h_q <= (32 if w.kv_format == 0 else 16)
+    roof["kernel"] = "decode_small_kernel" if small else "decode_kernel"
     roof["kernel_ms"] = dec_ms
 
     cpu = None

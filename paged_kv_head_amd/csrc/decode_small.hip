@@ -110,9 +110,15 @@ __device__ inline void issue_quarter(const uint8_t* __restrict__ kv, int page, i
     const void* src = ok ? (const void*)(src0 + key * Lay::kRowBytes + chunk * 16) : (const void*)g_zero16;
     dma16_to_lds(src, lds + 1024 * c);
     chunk += 64;
-    while (chunk >= Lay::kSlots) {
+    if (chunk >= Lay::kSlots) {
       chunk -= Lay::kSlots;
       ++key;
+    }
+    if constexpr (Lay::kSlots < 64) {  // 41-slot rows: a second wrap is possible
+      if (chunk >= Lay::kSlots) {
+        chunk -= Lay::kSlots;
+        ++key;
+      }
     }
   }
 }
@@ -303,24 +309,20 @@ __global__ void __launch_bounds__(64 * kSWaves, 1) decode_small_kernel(DecodeArg
 #pragma unroll
         for (int e = 0; e < 4; ++e) vsc[e] = *reinterpret_cast<const f32x4s*>(vrow + e * kPitch + 512);
       }
-      auto v_raw = [&](int cb) -> uint4 {
-        uint4 r;
+      // The 4 raw values, one per word (bf16 bits or FP8 codes), are packed
+      // or dequantised only where the MFMA takes them, so their LDS reads
+      // have kSVAhead column blocks to land.
+      using VRaw = uint4;
+      auto v_raw = [&](int cb) -> VRaw {
         if constexpr (FMT == 0) {
           const uint16_t* vc = reinterpret_cast<const uint16_t*>(vrow) + 16 * cb + j16;
-          r.x = vc[0];
-          r.y = vc[kPitch / 2];
-          r.z = vc[kPitch];
-          r.w = vc[3 * (kPitch / 2)];
+          return make_uint4(vc[0], vc[kPitch / 2], vc[kPitch], vc[3 * (kPitch / 2)]);
         } else {
           const uint8_t* vc = vrow + 16 * cb + j16;
-          r.x = vc[0];
-          r.y = vc[kPitch];
-          r.z = vc[2 * kPitch];
-          r.w = vc[3 * kPitch];
+          return make_uint4(vc[0], vc[kPitch], vc[2 * kPitch], vc[3 * kPitch]);
         }
-        return r;
       };
-      auto v_operand = [&](uint4 r, int cb) -> bf16x4s {
+      auto v_operand = [&](VRaw r, int cb) -> bf16x4s {
         if constexpr (FMT == 0) {
           return __builtin_bit_cast(bf16x4s, make_uint2(r.x | (r.y << 16), r.z | (r.w << 16)));
         } else {
@@ -333,7 +335,7 @@ __global__ void __launch_bounds__(64 * kSWaves, 1) decode_small_kernel(DecodeArg
           return v;
         }
       };
-      uint4 vop[kSVAhead];  // V^T operands read kSVAhead column blocks ahead
+      VRaw vop[kSVAhead];  // V^T operands read kSVAhead column blocks ahead
 #pragma unroll
       for (int i = 0; i < kSVAhead; ++i) vop[i] = v_raw(i);
 #pragma unroll
