@@ -1,12 +1,12 @@
-// Paged MLA decode for units of few query rows (s_q * h_q <= kSmallMaxRows),
-// dense, bf16 latent cache: the shape a GPU holds when the 128 query heads
-// are split across GPUs ("Modular Platform 设计文档全景导读", section 九:
-// for MLA only the query heads can be split, the latent KV is replicated).
-// It computes what the main decode kernel computes (per row: scores
-// P_t = scale * q.K_t, lse = log2 sum 2^P_t, out = sum 2^(P_t - lse)
-// K_t[:512]; "为什么 FlashMLA 的解码内核能跑到 660 TFLOPS", section 上手示例;
-// online softmax and merges as in the Modular guide, sections 六 and 七),
-// and writes the same outputs and split partials.
+// Paged MLA decode for units of few query rows (s_q * h_q <= 32 over a bf16
+// latent cache, <= 16 over the 656-byte FP8 cache), dense: the shape a GPU
+// holds when the 128 query heads are split across GPUs ("Modular Platform
+// 设计文档全景导读", section 九: for MLA only the query heads can be split,
+// the latent KV is replicated).  It computes what the main decode kernel
+// computes (per row: scores P_t = scale * q.K_t, lse = log2 sum 2^P_t,
+// out = sum 2^(P_t - lse) K_t[:512]; "为什么 FlashMLA 的解码内核能跑到 660
+// TFLOPS", section 上手示例; online softmax and merges as in the Modular
+// guide, sections 六 and 七), and writes the same outputs and split partials.
 //
 // With so few rows the work per key is small and the cache stream from HBM
 // is the bound, so the design keeps loads flowing instead of sharing tiles.
@@ -21,6 +21,8 @@
 //     (K from LDS, Q in registers); a lane ends up with 4 keys of one row,
 //     which is exactly the B-operand layout of P^T for O^T += V^T P^T
 //     (16x16x16 MFMAs), so the probabilities never leave the registers;
+//   * FP8 rows are staged raw and dequantised into the MFMA operands (the
+//     page's rule, bf16(float(code) * tile scale)) where they are used;
 //   * O^T keeps one row per lane; the probabilities are taken against the
 //     first max a row sees, which may lag the true max by up to 2^64 (far
 //     inside the fp32 range), so the output is never rescaled in the loop;
@@ -29,11 +31,6 @@
 //   * each wave keeps its own running max, sum and output over its own keys;
 //     at the end of a segment the four are merged in LDS in a fixed order
 //     (deterministic results) and written like the main kernel's.
-//
-// LDS key row pitch is 1168 bytes (1152 + 16): 16 consecutive rows then
-// start on 16 distinct 4-bank groups, so the 16-byte K operand reads are
-// conflict free; the 2-byte V^T reads of four rows 4 apart land 16 banks
-// apart.
 #include "internal.h"
 
 namespace mla {
@@ -65,13 +62,14 @@ constexpr int kSCopies = (kSQuarter * SmallLayout<FMT>::kSlots + 63) / 64;  // 1
 template <int FMT>
 constexpr int kSBuf = kSCopies<FMT> * 1024;
 constexpr int kSSteps = kDqk / 32;  // 18 k-steps of 32 dims (16 NoPE, 2 RoPE)
-constexpr int kSOPitch = 516;                                 // floats per merge-buffer row
+constexpr int kSOPitch = 516;  // floats per merge-buffer row
 // The running max a row's probabilities are taken against may lag the true
 // max by up to this much (log2 units): probabilities stay <= 2^64, sums far
 // inside the fp32 range.  A larger climb restarts the wave's segment.
 constexpr float kSLag = 64.0f;
-// LDS operand reads in flight ahead of their MFMA (at most 15 LDS reads may
-// be outstanding: 2 K reads per step, 4 V reads per column block)
+// LDS operand reads in flight ahead of their MFMA (the LDS counter holds at
+// most 15 outstanding reads: one K read per step, four V reads per column
+// block, and the two phases do not overlap)
 constexpr int kSKAhead = 4;
 constexpr int kSVAhead = 3;
 
