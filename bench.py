@@ -53,6 +53,9 @@ def parse():
                          "16 query heads (an 8-way head split of the 128), batch 128, lengths "
                          "U[1024, 8192]; small_fp8: the same heads over the 656-byte FP8 cache, "
                          "lengths U[8192, 32768]")
+    ap.add_argument("--no-measured-peaks", action="store_true",
+                    help="skip the reference measurements of HBM copy bandwidth and bf16 GEMM "
+                         "throughput on this GPU")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run three 1 GiB device-to-device copies (reference for the HBM byte "
                          "counters under rocprofv3), print nothing else")
@@ -73,6 +76,50 @@ def copy_calibration():
     for _ in range(3):
         b.copy_(a)
     torch.cuda.synchronize()
+
+
+def measured_peaks():
+    """What this GPU reaches on plain reference work, after the timed region:
+    HBM bandwidth of a 1 GiB device-to-device copy (bytes read + written per
+    second) and bf16 matrix-core throughput of an 8192^3 library GEMM.  The
+    roofline fractions are also reported against these."""
+    import torch
+
+    out = {}
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    out["hbm_copy_gbps"] = 2 * n * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
+    m = 8192
+    x = torch.randn(m, m, device="cuda").to(torch.bfloat16)
+    y = torch.randn(m, m, device="cuda").to(torch.bfloat16)
+    for _ in range(5):
+        torch.matmul(x, y)
+    e0.record()
+    for _ in range(20):
+        torch.matmul(x, y)
+    e1.record()
+    torch.cuda.synchronize()
+    out["bf16_gemm_tflops"] = 2 * m ** 3 * 20 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    return out
+
+
+def with_measured(roof, peaks):
+    """Adds the fraction of the measured reference peak to a roofline record."""
+    if peaks is None:
+        return None
+    ref = peaks["hbm_copy_gbps"] if roof["unit"] == "GB/s" else peaks["bf16_gemm_tflops"]
+    return dict(peaks, frac_of_measured=roof["achieved"] / ref)
 
 
 def traffic_record(config_name: str, source: str = "decode.hip", prefix: str = "decode"):
@@ -189,6 +236,7 @@ def bench_writer(args):
     alg_bytes = tokens * (1152 + 656) + 4 * pages + 4 * B
     achieved = alg_bytes / (k_ms * 1e-3) / 1e9
     tr = traffic_record(w.name, "kv_writer.hip", "kv_writer")
+    peaks = None if args.no_measured_peaks else measured_peaks()
     cpu = None if args.no_cpu_baseline else writer_cpu_baseline(w)
     line = {
         "metric": "FP8 KV writer GB/s (bf16 576-value rows -> 656-byte paged FP8 rows), % of HBM roofline",
@@ -202,6 +250,7 @@ def bench_writer(args):
                      "frac": achieved / PEAK_HBM_GBPS,
                      "traffic": None if tr is None else tr["hbm_bytes_per_launch"],
                      "kernel": "kv_quantize_fp8_kernel", "kernel_ms": k_ms},
+        "measured_peaks": with_measured({"unit": "GB/s", "achieved": achieved}, peaks),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -283,6 +332,7 @@ def bench_prefill(args):
     flops = w.flops()
     alg_bytes = w.algorithmic_bytes()
     achieved = flops / (call_ms * 1e-3) / 1e12
+    peaks = None if args.no_measured_peaks else measured_peaks()
     cpu = None if args.no_cpu_baseline else prefill_cpu_baseline(w)
     line = {
         "metric": "sparse MLA prefill TFLOPS (h_q=128, d_qk=576, d_v=512, topk=2048), % of roofline",
@@ -298,6 +348,7 @@ def bench_prefill(args):
                      "kernel": "mla_sparse_prefill call (identity table; per 2048-token chunk: "
                                "metadata, decode_kernel, combine_kernel)",
                      "kernel_ms": call_ms},
+        "measured_peaks": with_measured({"unit": "TFLOP/s", "achieved": achieved}, peaks),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -413,6 +464,7 @@ def main():
     roof["kernel"] = "decode_small_kernel" if small else "decode_kernel"
     roof["kernel_ms"] = dec_ms
 
+    peaks = None if args.no_measured_peaks else measured_peaks()
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
@@ -432,6 +484,7 @@ def main():
                    "num_parts": plan.num_parts, "kv_copies": copies,
                    "flops_per_step": flops, "algorithmic_bytes_per_step": alg_bytes},
         "roofline": roof,
+        "measured_peaks": with_measured(roof, peaks),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
