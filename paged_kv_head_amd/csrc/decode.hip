@@ -1105,13 +1105,13 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
       asm volatile("" ::: "memory");
       if constexpr (SPARSE) {
         pg2 = bt_row[pg_idx];
-        // The raw index of tile kt+3, loaded from assembly and waited for
-        // at the end of the tile: a compiler-visible load next to its use
-        // gets a wait right here, which also waits for every copy issued
-        // before it.  Validity is applied at the end of the tile.
+        // The raw index of tile kt+3.  Its only reader until the end of the
+        // tile is an empty asm statement there, so the compiler's wait for
+        // it lands at the end of the tile; a select next to the load would
+        // be waited for here, and with it every copy issued before it.
+        // Validity is applied at the end of the tile.
         const int k = (kt + 3) * kPage + lane;
-        const int32_t* ip = idx_row + (k < s.topk ? k : s.topk - 1);
-        asm volatile("global_load_dword %0, %1, off" : "=v"(t3) : "v"(ip) : "memory");
+        t3 = idx_row[k < s.topk ? k : s.topk - 1];
         t3_ok = kt + 3 < kend && k < s.topk;
       }
       asm volatile("" ::: "memory");
@@ -1140,7 +1140,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
       // 5. finish resolving tile kt+2
       if constexpr (SPARSE) {
         res_off = offset_of(res_t, pg2);
-        asm volatile("s_waitcnt vmcnt(0)" : "+v"(t3) :: "memory");
+        asm volatile("" : "+v"(t3));
         res_t = t3_ok ? t3 : -1;
       }
     }
