@@ -89,6 +89,15 @@ __device__ inline uint16_t to_bf16_bits(float x) {
 }
 
 typedef __bf16 bf16x4s __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2s __attribute__((ext_vector_type(2)));
+typedef float f32x2s __attribute__((ext_vector_type(2)));
+
+// Two fp32 values rounded to bf16 (nearest even), lo in bits 0..15, as one
+// paired conversion: built as a bf16 vector that the MFMA operand then
+// reinterprets, the compiler would convert each value on its own and pack.
+__device__ inline uint32_t pk_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2s{lo, hi}, bf16x2s));
+}
 using cint32s = const __attribute__((address_space(4))) int32_t;
 
 // Copies of one quarter tile (keys 16*wave .. +15 of page `page`, logical
@@ -290,12 +299,13 @@ __global__ void __launch_bounds__(64 * kSWaves, 1) decode_small_kernel(DecodeArg
         mseen[rb] = fmaxf(mseen[rb], mx);
         if (m[rb] == -INFINITY) m[rb] = mx;  // first visible keys: output and sum still zero
         restart |= mx > m[rb] + kSLag;
+        float p[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const float p = x[v] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(x[v] - m[rb]);
-          l[rb] += p;
-          pf[rb][v] = (__bf16)p;
+          p[v] = x[v] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(x[v] - m[rb]);
+          l[rb] += p[v];
         }
+        pf[rb] = __builtin_bit_cast(bf16x4s, make_uint2(pk_bf16(p[0], p[1]), pk_bf16(p[2], p[3])));
       }
 
       // O^T += V^T P^T: column block cb; V^T[col][key] for keys 4g .. 4g+3 of
@@ -325,12 +335,11 @@ __global__ void __launch_bounds__(64 * kSWaves, 1) decode_small_kernel(DecodeArg
           return __builtin_bit_cast(bf16x4s, make_uint2(r.x | (r.y << 16), r.z | (r.w << 16)));
         } else {
           const int t = cb >> 3;
-          bf16x4s v;
-          v[0] = (__bf16)(__builtin_amdgcn_cvt_pk_f32_fp8(r.x, false)[0] * vsc[0][t]);
-          v[1] = (__bf16)(__builtin_amdgcn_cvt_pk_f32_fp8(r.y, false)[0] * vsc[1][t]);
-          v[2] = (__bf16)(__builtin_amdgcn_cvt_pk_f32_fp8(r.z, false)[0] * vsc[2][t]);
-          v[3] = (__bf16)(__builtin_amdgcn_cvt_pk_f32_fp8(r.w, false)[0] * vsc[3][t]);
-          return v;
+          const uint32_t v01 = pk_bf16(__builtin_amdgcn_cvt_pk_f32_fp8(r.x, false)[0] * vsc[0][t],
+                                       __builtin_amdgcn_cvt_pk_f32_fp8(r.y, false)[0] * vsc[1][t]);
+          const uint32_t v23 = pk_bf16(__builtin_amdgcn_cvt_pk_f32_fp8(r.z, false)[0] * vsc[2][t],
+                                       __builtin_amdgcn_cvt_pk_f32_fp8(r.w, false)[0] * vsc[3][t]);
+          return __builtin_bit_cast(bf16x4s, make_uint2(v01, v23));
         }
       };
       VRaw vop[kSVAhead];  // V^T operands read kSVAhead column blocks ahead
