@@ -109,9 +109,11 @@ __device__ inline float wave_sum_pair(float x) {
   return p[0] + p[1];
 }
 
-__device__ inline uint16_t bf16_bits(float x) {
-  __bf16 h = (__bf16)x;  // v_cvt_pk_bf16_f32: round to nearest even
-  return __builtin_bit_cast(uint16_t, h);
+// Two fp32 values rounded to bf16 (nearest even), lo in bits 0..15, in one
+// paired conversion; converting them one by one takes two conversions and a
+// pack.
+__device__ inline uint32_t pk_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 template <int FMT>
@@ -1201,8 +1203,8 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
               f32x4 v = f32x4{o[cb][rb][4 * q4], o[cb][rb][4 * q4 + 1], o[cb][rb][4 * q4 + 2],
                               o[cb][rb][4 * q4 + 3]} * f[0];
               if constexpr (kFlushed) v += fr[4 * cb + q4] * f[1];
-              const uint32_t w0 = (uint32_t)bf16_bits(v[0]) | ((uint32_t)bf16_bits(v[1]) << 16);
-              const uint32_t w1 = (uint32_t)bf16_bits(v[2]) | ((uint32_t)bf16_bits(v[3]) << 16);
+              const uint32_t w0 = pk_bf16(v[0], v[1]);
+              const uint32_t w1 = pk_bf16(v[2], v[3]);
               const int chunk = (16 * ow + 4 * cb + q4) ^ (on & 15);  // columns 128ow + 32cb + 8q4 ..
               *reinterpret_cast<uint2*>(stg + on * 1024 + chunk * 16 + 8 * oh) = make_uint2(w0, w1);
             }
