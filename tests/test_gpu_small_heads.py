@@ -132,47 +132,3 @@ def test_small_heads_single_key_bit_exact(kv_format):
         row = oracle.decode_row(w.kv[w.block_table[b, 0], 0], kv_format)
         assert np.array_equal(out[b, 0], np.broadcast_to(row[:512], (16, 512))), b
 
-
-def test_small_heads_fp8_scores_dequantise_exactly():
-    """FP8 rows on the small-head kernel: one key per sequence and one-hot
-    queries make each head's score a single dequantised K element, and its
-    base-2 LSE (softmax scale 1) that element itself, so every head's LSE
-    must equal the oracle's bf16(float(code) * tile scale) bit for bit, for
-    every finite code (subnormals and negative zero included) in every
-    128-dim tile; the output must be the dequantised V row."""
-    rng = np.random.default_rng(76)
-    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
-    combos = [(int(c), t) for c in codes for t in range(4)]
-    rng.shuffle(combos)
-    B, H = -(-len(combos) // 16), 16
-    w = synth.make_workload("fp8_exact_scores", batch=B, h_q=H, s_q=1, seqlens=[1] * B, seed=77,
-                            kv_format=synth.KV_FP8_656, softmax_scale=1.0)
-    q = np.zeros(w.q.shape, dtype=np.uint16)
-    pos = np.zeros((B, H), dtype=np.int64)
-    for b in range(B):
-        row = np.empty(656, dtype=np.uint8)
-        row[:512] = rng.choice(codes, size=512)
-        scales = (np.exp2(rng.integers(-60, 61, size=4)) * rng.uniform(1, 2, size=4)).astype(np.float32)
-        row[512:528] = scales.view(np.uint8)
-        row[528:] = synth.bf16_bits_from_f32(rng.standard_normal(64).astype(np.float32)).view(np.uint8)
-        cols = rng.permutation(128)
-        for h in range(H):
-            c, t = combos[(b * H + h) % len(combos)]
-            pos[b, h] = 128 * t + int(cols[h])
-            row[pos[b, h]] = c
-            q[b, 0, h, pos[b, h]] = 0x3F80  # 1.0
-        w.kv[w.block_table[b, 0], 0] = row
-    w.q = q
-    out, lse = run(w)
-    expect = np.zeros((B, 1, H), dtype=np.float32)
-    for b in range(B):
-        row = oracle.decode_row(w.kv[w.block_table[b, 0], 0], synth.KV_FP8_656)
-        # + 0: a zero element gives +0 in the fp32 accumulator
-        expect[b, 0] = row[pos[b]].astype(np.float32) + np.float32(0.0)
-        # one key: the output is the dequantised V row, bit for bit
-        assert np.array_equal(out[b, 0], np.broadcast_to(row[:512], (H, 512))), b
-    bad = np.argwhere(lse.view(np.uint32) != expect.view(np.uint32))
-    if len(bad):
-        b, _, h = bad[0]
-        raise AssertionError(f"{len(bad)} heads differ; first b={b} h={h} pos={pos[b, h]}: "
-                             f"gpu {lse[b, 0, h]!r} expected {expect[b, 0, h]!r}")
