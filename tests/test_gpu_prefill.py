@@ -90,3 +90,28 @@ def test_prefill_full_size_sampled():
     ref_out, ref_lse = sparse_prefill(w.q[pick], w.kv, w.indices[pick], w.softmax_scale, 0)
     assert_close(out[pick], lse[pick], ref_out, ref_lse, what="prefill full size sample")
     assert np.isfinite(out).all() and np.isfinite(lse).all()
+
+
+def prefill_case(seed: int):
+    rng = np.random.default_rng(40_000 + seed)
+    s_q = int(rng.integers(1, 90))
+    h_q = int(rng.choice([1, 16, 33, 64, 128]))
+    s_kv = int(rng.integers(1, 3000))
+    topk = int(rng.integers(1, min(s_kv, 400) + 1))
+    return dict(s_q=s_q, h_q=h_q, s_kv=s_kv, topk=topk, fmt=int(rng.integers(0, 2)),
+                invalid=float(rng.choice([0.0, 0.0, 0.1, 0.5])), natural=bool(rng.random() < 0.3),
+                parts=[None, None, 1, 5, 200][int(rng.integers(0, 5))])
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_prefill_random_shapes(seed):
+    """Seeded random shapes: query tokens, heads, cache size, top-k, format,
+    invalid entries, base and forced split counts."""
+    c = prefill_case(seed)
+    print(f"prefill sweep {seed}: {c}", flush=True)
+    w = synth.make_sparse_prefill(f"prefill_sweep_{seed}", s_q=c["s_q"], h_q=c["h_q"], s_kv=c["s_kv"],
+                                  topk=c["topk"], seed=50_000 + seed, kv_format=c["fmt"],
+                                  invalid_frac=c["invalid"])
+    out, lse = gpu_prefill(w, natural=c["natural"], num_parts=c["parts"])
+    ref_out, ref_lse = sparse_prefill(w.q, w.kv, w.indices, w.softmax_scale, c["fmt"], c["natural"])
+    assert_close(out, lse, ref_out, ref_lse, what=f"prefill sweep {seed} {c}")
