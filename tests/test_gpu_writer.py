@@ -175,3 +175,23 @@ def test_writer_then_fp8_decode_end_to_end():
     ref_out, ref_lse = oracle.mla_decode(w)
     assert_close(out, lse, ref_out, ref_lse, what="writer -> fp8 decode")
     assert math.isfinite(float(np.abs(out).max()))
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_writer_random_shapes(seed):
+    """Seeded random shapes: batch, new tokens, start positions (negative
+    ones included), value scales, tables narrower than the appended range
+    and holes (-1) in the table; the pool must match the oracle's byte for
+    byte."""
+    rng = np.random.default_rng(60_000 + seed)
+    batch = int(rng.integers(1, 12))
+    n_new = int(rng.integers(1, 300))
+    start = [int(x) for x in rng.integers(-40, 400, size=batch)]
+    width = [None, 2, 5][int(rng.integers(0, 3))]
+    scale = [None, "mixed", 1e-4, 30.0][int(rng.integers(0, 4))]
+    print(f"writer sweep {seed}: batch {batch} n_new {n_new} width {width} scale {scale}", flush=True)
+    w = synth.make_append(f"append_sweep_{seed}", batch=batch, n_new=n_new, start_pos=start,
+                          seed=70_000 + seed, max_pages_per_seq=width, value_scale=scale, pool_fill=None)
+    holes = rng.random(w.block_table.shape) < 0.1
+    w.block_table = np.where(holes, -1, w.block_table).astype(np.int32)
+    assert_pools_equal(gpu_append(w), oracle_append(w))
