@@ -100,28 +100,60 @@ __device__ inline uint32_t pk_bf16(float lo, float hi) {
 }
 using cint32s = const __attribute__((address_space(4))) int32_t;
 
+// The copy slots of a lane, the same for every quarter: copy c loads slot
+// 64*c + lane of the buffer, which is chunk `slot % kSlots` of key
+// `slot / kSlots`.  FP8 rows keep them in registers, packed as
+// (key << 16) | byte offset of the chunk in the quarter; padding slots get
+// key 16, past every key, so one unsigned compare against
+// (visible keys << 16) picks the cache row or the zero row.  bf16 rows (19
+// copies, in a kernel short of registers) walk the slots as they go.
+template <int FMT>
+struct CopySlots {
+  __device__ inline void init(int) {}
+};
+template <>
+struct CopySlots<1> {
+  uint32_t v[kSCopies<1>];
+  __device__ inline void init(int lane) {
+    using Lay = SmallLayout<1>;
+#pragma unroll
+    for (int c = 0; c < kSCopies<1>; ++c) {
+      const int slot = 64 * c + lane, key = slot / Lay::kSlots, chunk = slot % Lay::kSlots;
+      v[c] = key < kSQuarter ? ((uint32_t)key << 16) | (uint32_t)(key * Lay::kRowBytes + chunk * 16)
+                             : (uint32_t)kSQuarter << 16;
+    }
+  }
+};
+
 // Copies of one quarter tile (keys 16*wave .. +15 of page `page`, logical
 // positions tbase ..) into the LDS buffer at lds (layout above); padding
 // slots and keys at or past L come from the zero row.
 template <int FMT>
 __device__ inline void issue_quarter(const uint8_t* __restrict__ kv, int page, int wave, int tbase,
-                                     int L, uint32_t lds, int lane) {
+                                     int L, uint32_t lds, int lane, const CopySlots<FMT>& slots) {
   using Lay = SmallLayout<FMT>;
   const uint8_t* src0 = kv + ((int64_t)page * kPage + kSQuarter * wave) * Lay::kRowBytes;
-  // slot 64*c + lane = (key, chunk); stepping by 64 slots wraps the chunk
-  // at most once (73 slots a row) or twice (41)
-  int key = lane / Lay::kSlots, chunk = lane % Lay::kSlots;
-#pragma unroll 1
-  for (int c = 0; c < kSCopies<FMT>; ++c) {
-    const bool ok = key < kSQuarter && chunk < Lay::kDataSlots && tbase + key < L;
-    const void* src = ok ? (const void*)(src0 + key * Lay::kRowBytes + chunk * 16) : (const void*)g_zero16;
-    dma16_to_lds(src, lds + 1024 * c);
-    chunk += 64;
-    if (chunk >= Lay::kSlots) {
-      chunk -= Lay::kSlots;
-      ++key;
+  if constexpr (FMT == 1) {
+    static_assert(Lay::kDataSlots == Lay::kSlots && kSQuarter * Lay::kRowBytes <= 0x10000,
+                  "every in-row slot holds data; offsets fit in 16 bits");
+    const uint32_t lim = (uint32_t)min(max(L - tbase, 0), kSQuarter) << 16;
+#pragma unroll
+    for (int c = 0; c < kSCopies<FMT>; ++c) {
+      const uint32_t sl = slots.v[c];
+      const void* src = sl < lim ? (const void*)(src0 + (sl & 0xFFFFu)) : (const void*)g_zero16;
+      dma16_to_lds(src, lds + 1024 * c);
     }
-    if constexpr (Lay::kSlots < 64) {  // 41-slot rows: a second wrap is possible
+  } else {
+    // slot 64*c + lane = (key, chunk); stepping by 64 slots wraps the chunk
+    // at most once (73 slots a row)
+    static_assert(Lay::kSlots >= 64, "one wrap per step");
+    int key = lane / Lay::kSlots, chunk = lane % Lay::kSlots;
+#pragma unroll 1
+    for (int c = 0; c < kSCopies<FMT>; ++c) {
+      const bool ok = key < kSQuarter && chunk < Lay::kDataSlots && tbase + key < L;
+      const void* src = ok ? (const void*)(src0 + key * Lay::kRowBytes + chunk * 16) : (const void*)g_zero16;
+      dma16_to_lds(src, lds + 1024 * c);
+      chunk += 64;
       if (chunk >= Lay::kSlots) {
         chunk -= Lay::kSlots;
         ++key;
@@ -176,6 +208,8 @@ __global__ void __launch_bounds__(64 * kSWaves, 1) decode_small_kernel(DecodeArg
   uint8_t* const buf0 = kbuf + wave * 2 * kBuf;
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)buf0);
+  CopySlots<FMT> slots;
+  slots.init(lane);
 
   for (int u = ub; u < s.units && (u < ue || (u == ue && ke > 0)); ++u) {
     const int L = a.seqlens[u];
@@ -214,7 +248,7 @@ __global__ void __launch_bounds__(64 * kSWaves, 1) decode_small_kernel(DecodeArg
     // The first quarter's copies go out while Q is in flight; Q is waited for
     // here, before the loop, so that no wait for it lands inside the loop
     // (it would also wait for the copies in flight there).
-    issue_quarter<FMT>(a.kv, btc[kfirst], wave, kfirst * kPage + kSQuarter * wave, L, lds0, lane);
+    issue_quarter<FMT>(a.kv, btc[kfirst], wave, kfirst * kPage + kSQuarter * wave, L, lds0, lane, slots);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -239,7 +273,7 @@ __global__ void __launch_bounds__(64 * kSWaves, 1) decode_small_kernel(DecodeArg
       if (kt + 1 < kend) {
         // the other buffer was last read by the previous quarter's products
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        issue_quarter<FMT>(a.kv, btc[kt + 1], wave, tbase + kPage, L, lds0 + (cur ^ 1) * kBuf, lane);
+        issue_quarter<FMT>(a.kv, btc[kt + 1], wave, tbase + kPage, L, lds0 + (cur ^ 1) * kBuf, lane, slots);
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kCopies) : "memory");  // this quarter has landed
       } else {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
