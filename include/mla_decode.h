@@ -156,7 +156,7 @@ mla_status mla_decode_get_metadata(const mla_problem* p, const int32_t* cache_se
  *   lse          float [B, s_q, h_q]
  * Rows of units with exactly one segment are final after this call; the
  * others need mla_decode_combine.
- * Dense units of at most 32 query rows (s_q * h_q; 16 over the FP8 cache)
+ * Dense units of at most 32 query rows (s_q * h_q), either cache format,
  * run on a streaming kernel that keeps a whole unit in one workgroup;
  * larger units and sparse calls run on the 128-row tile kernel.  For a given
  * num_parts the results are deterministic: the same bits on every run and

@@ -1,5 +1,5 @@
-// Paged MLA decode for units of few query rows (s_q * h_q <= 32 over a bf16
-// latent cache, <= 16 over the 656-byte FP8 cache), dense: the shape a GPU
+// Paged MLA decode for units of few query rows (s_q * h_q <= 32, over a bf16
+// latent cache or the 656-byte FP8 cache), dense: the shape a GPU
 // holds when the 128 query heads are split across GPUs ("Modular Platform
 // 设计文档全景导读", section 九: for MLA only the query heads can be split,
 // the latent KV is replicated).  It computes what the main decode kernel
@@ -194,6 +194,7 @@ __global__ void __launch_bounds__(64 * kSWaves, 1) decode_small_kernel(DecodeArg
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[kSWaves * 2 * kBuf];
   __shared__ float m_sh[kSWaves][kRows];
   __shared__ float l_sh[kSWaves][kRows];
+  static_assert(kRows * kSOPitch * sizeof(float) <= sizeof(kbuf), "the merge buffer reuses the quarter buffers");
 
   const Shape& s = a.s;
   const int part = blockIdx.x;
@@ -478,8 +479,10 @@ bool small_decode_applies(const Shape& s) {
 
 hipError_t launch_decode_small(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid(a.num_parts), block(64 * kSWaves);
-  if (a.s.kv_format == 1)
+  if (a.s.kv_format == 1 && a.s.rows <= 16)
     hipLaunchKernelGGL((decode_small_kernel<1, 1>), grid, block, 0, stream, a);
+  else if (a.s.kv_format == 1)
+    hipLaunchKernelGGL((decode_small_kernel<1, 2>), grid, block, 0, stream, a);
   else if (a.s.rows <= 16)
     hipLaunchKernelGGL((decode_small_kernel<0, 1>), grid, block, 0, stream, a);
   else

@@ -14,7 +14,7 @@ constexpr int kRowsPerGroup = 128; // query rows one workgroup owns
 // kSmallMaxRowsFp8 rows (FP8 cache) run on the small-head kernel (one
 // workgroup per part, all rows of the unit in it).
 constexpr int kSmallMaxRows = 32;
-constexpr int kSmallMaxRowsFp8 = 16;
+constexpr int kSmallMaxRowsFp8 = 32;
 constexpr int kSplitPenalty = 3;   // scheduler cost of one segment, in blocks (measured: a
                                     // segment's prologue + epilogue ~ 3 tiles)
 constexpr int kMaxUnits = 16384;   // metadata kernel keeps per-unit arrays in LDS

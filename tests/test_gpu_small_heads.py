@@ -1,5 +1,5 @@
 """GPU parity of decode at small head counts (h_q * s_q <= 64, dense, bf16
-and FP8 caches): units of at most 32 rows (bf16) or 16 rows (FP8) run on
+and FP8 caches): units of at most 32 rows (either format) run on
 their own kernel, larger ones on the main kernel; row counts below and between 16-row blocks, causal rows, the lazy rescale, forced split counts, bit identity under page
 permutation and across runs, and a seeded sample at the benchmark's size."""
 
@@ -48,7 +48,8 @@ def test_small_heads_base_and_scale(natural, scale, kv_format):
 
 
 @pytest.mark.parametrize("h_q,kv_format", [(16, synth.KV_BF16), (32, synth.KV_BF16),
-                                          (128, synth.KV_BF16), (16, synth.KV_FP8_656)])
+                                          (128, synth.KV_BF16), (16, synth.KV_FP8_656),
+                                          (32, synth.KV_FP8_656)])
 def test_small_heads_growing_scores_rescale(h_q, kv_format):
     """Scores that climb by far more than any lag the running max may have
     (here by ~500 in log2 units over the sequence) force the recovery path:
@@ -73,7 +74,8 @@ def test_small_heads_growing_scores_rescale(h_q, kv_format):
         assert_close(out, lse, ref_out, ref_lse, what=f"growing parts={parts}")
 
 
-@pytest.mark.parametrize("h_q,s_q,kv_format", [(24, 2, synth.KV_BF16), (8, 2, synth.KV_FP8_656)])
+@pytest.mark.parametrize("h_q,s_q,kv_format", [(24, 2, synth.KV_BF16), (8, 2, synth.KV_FP8_656),
+                                                (12, 2, synth.KV_FP8_656)])
 def test_small_heads_bit_identity(h_q, s_q, kv_format):
     """Same results bit for bit across runs and after permuting the physical
     pages (the block table rewritten to match)."""

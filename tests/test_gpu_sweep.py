@@ -2,7 +2,7 @@
 tokens, lengths (zero, ragged, past a page), cache format, causal or sparse
 (top-k, with invalid entries) and forced split counts, each case against the
 oracle at the stated tolerance.  The cases cross every dispatch boundary of
-the decode entry point: the small-head kernel (up to 32 bf16 or 16 FP8 rows
+the decode entry point: the small-head kernel (up to 32 rows
 per unit), the main kernel with one or several 128-row groups, dense and
 sparse."""
 
