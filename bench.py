@@ -37,10 +37,15 @@ DEFAULT_CONFIG = 3  # dense bf16, h_q=128, s_q=2 causal: the workload the target
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # The GPU raises its clock over the first tens of milliseconds of
-    # sustained work; the default warm-up covers that ramp.
+    # The GPU raises its clock over the first tens to hundreds of
+    # milliseconds of sustained work: a time-based settle phase runs first,
+    # whatever the warm-up count.
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--settle-ms", type=float, default=600.0,
+                    help="untimed settle phase before the warm-up: at least this many ms of "
+                         "steps, then until the per-step time is stable")
+    ap.add_argument("--settle-max-ms", type=float, default=3000.0)
     ap.add_argument("--config", type=int, default=DEFAULT_CONFIG, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--num-parts", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -122,17 +127,58 @@ def with_measured(roof, peaks):
     return dict(peaks, frac_of_measured=roof["achieved"] / ref)
 
 
-def traffic_record(config_name: str, source: str = "decode.hip", prefix: str = "decode"):
+def traffic_record(config_name: str, prefix: str = "decode"):
     """HBM traffic of a kernel from the committed rocprofv3 counter summary,
-    if it was taken on the current kernel source; else None."""
+    if it was taken on the current source of the kernel it names; else None."""
     path = os.path.join(ROOT, "profiles", f"{prefix}_{config_name}_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = open(os.path.join(ROOT, "paged_kv_head_amd", "csrc", source), "rb").read()
+    source = rec.get("source", "decode.hip")
+    src_path = os.path.join(ROOT, "paged_kv_head_amd", "csrc", source)
+    if not os.path.exists(src_path):
+        return None
+    src = open(src_path, "rb").read()
     if rec.get("source_sha256", rec.get("decode_source_sha256")) != hashlib.sha256(src).hexdigest():
         return None
     return rec
+
+
+def settle(step, min_ms: float, max_ms: float, window: int = 20):
+    """Untimed steps before the warm-up: the GPU raises its clock over the
+    first tens to hundreds of milliseconds of sustained work.  Steps run in
+    windows until at least min_ms of wall time has passed and the mean step
+    time of the last window is within 2 % of the one before (or max_ms has
+    passed).  Returns (elapsed ms, steps)."""
+    import torch
+
+    t0 = time.perf_counter()
+    n = 0
+    last = None
+    while True:
+        ts = time.perf_counter()
+        for _ in range(window):
+            step(n)
+            n += 1
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - ts) / window
+        elapsed = (time.perf_counter() - t0) * 1e3
+        if elapsed >= max_ms:
+            break
+        if elapsed >= min_ms and last is not None and abs(dt - last) <= 0.02 * last:
+            break
+        last = dt
+    return elapsed, n
+
+
+def clock_record():
+    """Shader clock right after the timed region, from the library's probe
+    (the matrix cores kept busy by every workgroup)."""
+    import paged_kv_head_amd as mla
+
+    return {"shader_clock_mhz": round(mla.shader_clock_mhz(), 1),
+            "method": "s_memtime / s_memrealtime (100 MHz) over ~2 ms of bf16 MFMA chains on "
+                      "256 workgroups, measured right after the timed region"}
 
 
 def cpu_baseline(w, sample_units, min_seconds=10.0, max_reps=6):
@@ -215,6 +261,8 @@ def bench_writer(args):
     B, n_new = int(kv_new.shape[0]), int(kv_new.shape[1])
     call = (B, n_new, 64, int(pool.shape[0]), int(bt.shape[1]), P(kv_new.data_ptr()),
             P(sp.data_ptr()), P(bt.data_ptr()), P(pool.data_ptr()), P(stream.cuda_stream))
+    settle_ms, settle_steps = settle(lambda i: lib.mla_kv_quantize_fp8(*call), args.settle_ms,
+                                     args.settle_max_ms)
     for _ in range(args.warmup):
         lib.mla_kv_quantize_fp8(*call)
     torch.cuda.synchronize()
@@ -231,11 +279,12 @@ def bench_writer(args):
     wall = time.perf_counter() - t_start
     k_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
     ms_per_step = wall * 1e3 / args.steps
+    clock = clock_record()
     tokens = w.tokens
     pages = int((w.block_table >= 0).sum())
     alg_bytes = tokens * (1152 + 656) + 4 * pages + 4 * B
     achieved = alg_bytes / (k_ms * 1e-3) / 1e9
-    tr = traffic_record(w.name, "kv_writer.hip", "kv_writer")
+    tr = traffic_record(w.name, "kv_writer")
     peaks = None if args.no_measured_peaks else measured_peaks()
     cpu = None if args.no_cpu_baseline else writer_cpu_baseline(w)
     line = {
@@ -243,7 +292,8 @@ def bench_writer(args):
         "value": alg_bytes / (ms_per_step * 1e-3) / 1e9, "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
-        "data": "synthetic",
+        "data": "synthetic", "settle_ms": round(settle_ms, 1), "settle_steps": settle_steps,
+        "clock": clock,
         "config": {"workload": w.name, "batch": B, "n_new": n_new, "tokens": tokens,
                    "num_pages": int(pool.shape[0]), "algorithmic_bytes_per_step": alg_bytes},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
@@ -313,6 +363,8 @@ def bench_prefill(args):
             P(out.data_ptr()), P(lse.data_ptr()), P(stream.cuda_stream))
     warm = max(3, args.warmup // 20)
     steps = max(5, args.steps // 10)
+    settle_ms, settle_steps = settle(lambda i: lib.mla_sparse_prefill(*call), args.settle_ms,
+                                     args.settle_max_ms, window=2)
     for _ in range(warm):
         lib.mla_sparse_prefill(*call)
     torch.cuda.synchronize()
@@ -329,6 +381,7 @@ def bench_prefill(args):
     wall = time.perf_counter() - t_start
     call_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
     ms_per_step = wall * 1e3 / steps
+    clock = clock_record()
     flops = w.flops()
     alg_bytes = w.algorithmic_bytes()
     achieved = flops / (call_ms * 1e-3) / 1e12
@@ -339,7 +392,8 @@ def bench_prefill(args):
         "value": flops / (ms_per_step * 1e-3) / 1e12, "unit": "TFLOPS", "n_gpus": 1, "steps": steps,
         "warmup": warm, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "arithmetic_intensity": flops / alg_bytes,
+        "arithmetic_intensity": flops / alg_bytes, "settle_ms": round(settle_ms, 1),
+        "settle_steps": settle_steps, "clock": clock,
         "config": {"workload": w.name, "s_q": w.s_q, "h_q": w.h_q, "s_kv": w.s_kv, "topk": w.topk,
                    "kv_format": "bf16", "num_parts": parts, "flops_per_step": flops,
                    "algorithmic_bytes_per_step": alg_bytes},
@@ -375,7 +429,6 @@ def main():
 
     import paged_kv_head_amd as mla
     import synth
-    from tests.harness import problem, to_device
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
@@ -390,8 +443,8 @@ def main():
     else:
         w = synth.config_workload(args.config)
     print(f"[bench] workload {w.name}: generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
-    p = problem(w)
-    q, kv, bt, sl, idx = to_device(w, dev)
+    p = mla.problem_for(w)
+    q, kv, bt, sl, idx = mla.workload_tensors(w, dev)
     pool_bytes = kv.numel()
     copies = max(2, math.ceil(1.0e9 / pool_bytes))
     kvs = [kv] + [kv.clone() for _ in range(copies - 1)]
@@ -433,6 +486,7 @@ def main():
         if rc:
             raise RuntimeError(mla.mla_last_error())
 
+    settle_ms, settle_steps = settle(step, args.settle_ms, args.settle_max_ms)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -445,6 +499,7 @@ def main():
     wall = time.perf_counter() - t_start
     dec_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
     ms_per_step = wall * 1e3 / args.steps
+    clock = clock_record()
 
     flops = w.flops()
     alg_bytes = w.algorithmic_bytes()
@@ -460,8 +515,7 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     tr = traffic_record(w.name)
     roof["traffic"] = None if tr is None else tr["hbm_bytes_per_launch"]
-    small = w.topk == 0 and w.s_q * w.h_q <= (32 if w.kv_format == 0 else 16)
-    roof["kernel"] = "decode_small_kernel" if small else "decode_kernel"
+    roof["kernel"] = mla.mla_decode_kernel_name(p)
     roof["kernel_ms"] = dec_ms
 
     peaks = None if args.no_measured_peaks else measured_peaks()
@@ -478,6 +532,7 @@ def main():
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "hbm_gbps": gbps, "arithmetic_intensity": intensity,
+        "settle_ms": round(settle_ms, 1), "settle_steps": settle_steps, "clock": clock,
         "config": {"workload": w.name, "batch": w.batch, "s_q": w.s_q, "h_q": w.h_q,
                    "kv_format": "bf16" if w.kv_format == 0 else "fp8_656", "topk": w.topk,
                    "is_causal": w.is_causal, "sum_seqlen": int(w.cache_seqlens.astype(np.int64).sum()),

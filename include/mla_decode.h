@@ -108,22 +108,32 @@ typedef struct mla_problem {
 
 /* Number of work units U: dense -> B (each covers s_q*h_q query rows);
  * sparse -> B*s_q (each covers h_q rows, one query token's index list).
- * Returns -1 if `p` is NULL. */
+ * Returns -1 if `p` is NULL.  Source: the FlashMLA page above, section
+ * 上手示例 (the metadata call is sized by the query rows per KV head,
+ * s_q*h_q/h_kv, and, for sparse decode, by topk per query token). */
 int32_t mla_decode_num_units(const mla_problem* p);
 
 /* Recommended number of split-KV parts for `device` (one workgroup per
  * compute unit for each 128-row group of a unit).  Any value in
- * [1, 65536] may be passed to the calls below instead. */
+ * [1, 65536] may be passed to the calls below instead.  Source: the FlashMLA
+ * page above, section 设计 5 (the tile scheduler spreads the requests' blocks
+ * evenly over the compute units). */
 mla_status mla_decode_num_parts(const mla_problem* p, int device, int32_t* num_parts);
 
 /* Device memory the caller provides for the metadata:
  *   sched       int32 [num_parts * 8]
- *   num_splits  int32 [U + 1] */
+ *   num_splits  int32 [U + 1]
+ * Source: the FlashMLA page above, section 上手示例 (the metadata call
+ * returns the tile-scheduler metadata and the per-sequence split counts
+ * that every decode call of the step then reads). */
 mla_status mla_decode_metadata_size(const mla_problem* p, int32_t num_parts,
                                     size_t* sched_ints, size_t* num_splits_ints);
 
 /* Bytes of device workspace mla_decode_paged/mla_decode_combine need for
- * split partial results (an upper bound computed from host values only). */
+ * split partial results (an upper bound computed from host values only).
+ * Source: the FlashMLA page above, section 设计 5 (a sequence split over
+ * several compute units leaves partial results, each with its log-sum-exp,
+ * for a merge step). */
 mla_status mla_decode_workspace_bytes(const mla_problem* p, int32_t num_parts, size_t* bytes);
 
 /* Split-KV tile scheduler.  Reads cache_seqlens (int32 [B], device) and
@@ -266,8 +276,26 @@ mla_status mla_sparse_prefill(int32_t s_q, int32_t h_q, int32_t s_kv, int32_t to
                               int32_t num_parts, void* workspace, size_t workspace_bytes,
                               void* out, float* lse, void* stream);
 
-/* Message of the last failed call on this thread ("" if none). */
+/* Message of the last failed call on this thread ("" if none); it names
+ * the offending argument.  Source: "max.nn.kernels 内核封装模块全解析",
+ * section 输入校验 (the kernel wrappers reject malformed inputs before any
+ * kernel runs and report which argument is wrong). */
 const char* mla_last_error(void);
+
+/* Name of the kernel mla_decode_paged launches for this problem
+ * ("decode_kernel": 128-row tiles; "decode_small_kernel": dense units of at
+ * most 32 query rows), or NULL if the problem is invalid.  A helper for
+ * profiling tools that look kernels up by name; it reads host memory only. */
+const char* mla_decode_kernel_name(const mla_problem* p);
+
+/* Shader-clock probe, a measurement helper (not part of the decode path).
+ * Launches `workgroups` workgroups that keep the matrix cores busy for
+ * `spins` iterations of four bf16 MFMAs per wave and writes, per workgroup w,
+ * out[2w] = elapsed shader-clock cycles (s_memtime) and out[2w+1] = elapsed
+ * ticks of the 100 MHz constant-rate counter (s_memrealtime) over the same
+ * interval; cycles / ticks * 100 MHz is the shader clock under that load.
+ * `out` is a device int64 [2 * workgroups], 8-byte aligned. */
+mla_status mla_clock_probe(int64_t* out, int32_t workgroups, int32_t spins, void* stream);
 
 #ifdef __cplusplus
 }

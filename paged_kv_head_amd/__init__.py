@@ -22,6 +22,8 @@ __all__ = [
     "mla_decode_paged_fp8", "mla_decode_sparse_fp8", "mla_decode_combine", "mla_last_error",
     "mla_decode_with_kvcache", "mla_kv_quantize_fp8", "mla_sparse_prefill_workspace_bytes",
     "mla_sparse_prefill", "mla_sparse_prefill_num_parts", "mla_decode_check_inputs",
+    "mla_decode_kernel_name", "mla_clock_probe", "shader_clock_mhz", "problem_for",
+    "workload_tensors",
 ]
 
 MLA_KV_BF16 = 0
@@ -108,6 +110,10 @@ def _load():
         getattr(lib, fn).restype = ctypes.c_int
     lib.mla_last_error.argtypes = []
     lib.mla_last_error.restype = ctypes.c_char_p
+    lib.mla_decode_kernel_name.argtypes = [PP]
+    lib.mla_decode_kernel_name.restype = ctypes.c_char_p
+    lib.mla_clock_probe.argtypes = [P, I32, I32, P]
+    lib.mla_clock_probe.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -175,6 +181,58 @@ def _stream(stream) -> ctypes.c_void_p:
     if stream is None:
         stream = torch.cuda.current_stream()
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+def problem_for(w, *, natural: bool = False, softmax_scale=None) -> Problem:
+    """``Problem`` of a workload object (attributes batch, s_q, h_q,
+    num_pages, max_pages_per_seq, softmax_scale, topk, kv_format, is_causal),
+    optionally with another scale or the natural base."""
+    return Problem.make(
+        batch=w.batch, s_q=w.s_q, h_q=w.h_q, num_pages=w.num_pages,
+        max_pages_per_seq=w.max_pages_per_seq,
+        softmax_scale=w.softmax_scale if softmax_scale is None else softmax_scale,
+        topk=w.topk, kv_format=w.kv_format, is_causal=w.is_causal,
+        flags=MLA_FLAG_NATURAL_BASE if natural else 0)
+
+
+def workload_tensors(w, device="cuda"):
+    """Device tensors of a workload's host arrays: (q bf16, kv_pool uint8,
+    block_table int32, cache_seqlens int32, indices int32 or None)."""
+    import numpy as np
+
+    dev = torch.device(device)
+    q = torch.from_numpy(np.ascontiguousarray(w.q).view(np.int16)).to(dev).view(torch.bfloat16)
+    kv = torch.from_numpy(np.ascontiguousarray(w.kv)).to(dev)
+    bt = torch.from_numpy(np.ascontiguousarray(w.block_table)).to(dev)
+    sl = torch.from_numpy(np.ascontiguousarray(w.cache_seqlens)).to(dev)
+    idx = None if w.indices is None else torch.from_numpy(np.ascontiguousarray(w.indices)).to(dev)
+    return q, kv, bt, sl, idx
+
+
+def mla_decode_kernel_name(p: Problem) -> str:
+    """Name of the kernel mla_decode_paged launches for this problem."""
+    name = _load().mla_decode_kernel_name(ctypes.byref(p))
+    if name is None:
+        _check(MLA_ERR_INVALID_ARGUMENT)
+    return name.decode()
+
+
+def mla_clock_probe(out, workgroups: int, spins: int, stream=None):
+    """Enqueue the shader-clock probe; ``out`` is a device int64 tensor of
+    2 * workgroups elements (cycles, 100 MHz ticks per workgroup)."""
+    _expect("out", out, torch.int64, 2 * workgroups, at_least=True)
+    _check(_load().mla_clock_probe(_ptr(out), int(workgroups), int(spins), _stream(stream)))
+
+
+def shader_clock_mhz(device="cuda", workgroups: int = 256, spins: int = 20000) -> float:
+    """Median shader clock (MHz) of the workgroups of one probe launch with
+    the matrix cores busy; synchronises the device."""
+    out = torch.zeros(2 * workgroups, dtype=torch.int64, device=device)
+    mla_clock_probe(out, workgroups, spins)
+    torch.cuda.synchronize()
+    v = out.view(workgroups, 2).cpu().double()
+    ratio = (v[:, 0] / v[:, 1].clamp(min=1)).median().item()
+    return 100.0 * ratio
 
 
 def mla_decode_num_units(p: Problem) -> int:

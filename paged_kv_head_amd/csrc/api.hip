@@ -155,6 +155,22 @@ mla_status mla_decode_num_parts(const mla_problem* p, int device, int32_t* num_p
   return ok();
 }
 
+const char* mla_decode_kernel_name(const mla_problem* p) {
+  mla::Shape s;
+  if (check_problem(p, &s) != MLA_OK) return nullptr;
+  ok();
+  return mla::small_decode_applies(s) ? "decode_small_kernel" : "decode_kernel";
+}
+
+mla_status mla_clock_probe(int64_t* out, int32_t workgroups, int32_t spins, void* stream) {
+  if (workgroups < 1 || workgroups > 65536)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "workgroups: must be in [1, 65536] (got %d)", workgroups);
+  if (spins < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "spins: must be >= 1 (got %d)", spins);
+  MLA_CHECK(check_ptr(out, "out", 8));
+  return hip_status(mla::launch_clock_probe(out, workgroups, spins, (hipStream_t)stream),
+                    "clock probe kernel launch");
+}
+
 mla_status mla_decode_metadata_size(const mla_problem* p, int32_t num_parts, size_t* sched_ints,
                                     size_t* num_splits_ints) {
   mla::Shape s;

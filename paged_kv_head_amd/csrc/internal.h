@@ -71,8 +71,9 @@ inline size_t ws_total_bytes(int32_t num_parts, int32_t units, int32_t rows, int
 hipError_t launch_metadata(const Shape& s, const int32_t* seqlens, int32_t num_parts,
                            int32_t* sched, int32_t* num_splits, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
-// Units of at most kSmallMaxRows query rows (dense, bf16 cache) run on a kernel built
-// for the HBM-bound small-head shape; same inputs, outputs and workspace.
+// Dense units of at most kSmallMaxRows query rows (either cache format) run on a
+// kernel built for the HBM-bound small-head shape; same inputs, outputs and
+// workspace.
 bool small_decode_applies(const Shape& s);
 hipError_t launch_decode_small(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_combine(const Shape& s, const int32_t* num_splits, const float* ws_lse,
@@ -83,6 +84,7 @@ hipError_t launch_kv_quantize_fp8(int32_t batch, int32_t n_new, int32_t num_page
                                   uint8_t* kv_pool, hipStream_t stream);
 hipError_t launch_check_inputs(const Shape& s, const int32_t* block_table, const int32_t* seqlens,
                                int32_t* result, hipStream_t stream);
+hipError_t launch_clock_probe(int64_t* out, int32_t workgroups, int32_t spins, hipStream_t stream);
 hipError_t launch_identity_table(int32_t* table, int32_t pages, int32_t* seqlen, int32_t s_kv,
                                  hipStream_t stream);
 

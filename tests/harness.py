@@ -17,22 +17,11 @@ LSE_ABS = 1e-3
 
 
 def to_device(w: synth.Workload, device="cuda"):
-    dev = torch.device(device)
-    q = torch.from_numpy(w.q.view(np.int16)).to(dev).view(torch.bfloat16)
-    kv = torch.from_numpy(w.kv).to(dev)
-    bt = torch.from_numpy(w.block_table).to(dev)
-    sl = torch.from_numpy(w.cache_seqlens).to(dev)
-    idx = None if w.indices is None else torch.from_numpy(w.indices).to(dev)
-    return q, kv, bt, sl, idx
+    return mla.workload_tensors(w, device)
 
 
 def problem(w: synth.Workload, natural=False, softmax_scale=None) -> mla.Problem:
-    return mla.Problem.make(
-        batch=w.batch, s_q=w.s_q, h_q=w.h_q, num_pages=w.num_pages,
-        max_pages_per_seq=w.max_pages_per_seq,
-        softmax_scale=w.softmax_scale if softmax_scale is None else softmax_scale,
-        topk=w.topk, kv_format=w.kv_format, is_causal=w.is_causal,
-        flags=mla.MLA_FLAG_NATURAL_BASE if natural else 0)
+    return mla.problem_for(w, natural=natural, softmax_scale=softmax_scale)
 
 
 def run(w: synth.Workload, *, num_parts=None, natural=False, tensors=None, softmax_scale=None,

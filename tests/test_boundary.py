@@ -244,3 +244,26 @@ def test_check_inputs_rejects_bad_arguments():
     assert lib.mla_decode_check_inputs(ctypes.byref(p), None, ctypes.c_void_p(FAKE),
                                        ctypes.c_void_p(FAKE), None) == mla.MLA_ERR_INVALID_ARGUMENT
     assert mla.mla_last_error().startswith("block_table")
+
+
+def test_decode_kernel_name():
+    """The kernel the library picks for a problem, read on the host: dense
+    units of at most 32 rows (either format) go to the small-head kernel."""
+    assert mla.mla_decode_kernel_name(good(h_q=16)) == "decode_small_kernel"
+    assert mla.mla_decode_kernel_name(good(h_q=16, s_q=2)) == "decode_small_kernel"
+    assert mla.mla_decode_kernel_name(good(h_q=32, kv_format=mla.MLA_KV_FP8_656)) == "decode_small_kernel"
+    assert mla.mla_decode_kernel_name(good(h_q=33)) == "decode_kernel"
+    assert mla.mla_decode_kernel_name(good(h_q=128, s_q=2)) == "decode_kernel"
+    assert mla.mla_decode_kernel_name(good(h_q=16, topk=64)) == "decode_kernel"
+    with pytest.raises(ValueError, match="s_q"):
+        mla.mla_decode_kernel_name(good(s_q=0))
+
+
+def test_clock_probe_rejects_bad_arguments():
+    lib = mla._load()
+    assert lib.mla_clock_probe(None, 256, 10, None) == mla.MLA_ERR_INVALID_ARGUMENT
+    assert "out" in mla.mla_last_error()
+    assert lib.mla_clock_probe(ctypes.c_void_p(FAKE), 0, 10, None) == mla.MLA_ERR_INVALID_ARGUMENT
+    assert "workgroups" in mla.mla_last_error()
+    assert lib.mla_clock_probe(ctypes.c_void_p(FAKE), 4, 0, None) == mla.MLA_ERR_INVALID_ARGUMENT
+    assert "spins" in mla.mla_last_error()
