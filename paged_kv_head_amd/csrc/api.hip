@@ -188,7 +188,7 @@ mla_status mla_decode_workspace_bytes(const mla_problem* p, int32_t num_parts, s
   MLA_CHECK(check_problem(p, &s));
   MLA_CHECK(check_parts(num_parts));
   if (!bytes) return fail(MLA_ERR_INVALID_ARGUMENT, "bytes: NULL pointer");
-  *bytes = mla::ws_total_bytes(num_parts, s.units, s.rows, s.groups);
+  *bytes = mla::ws_total_bytes(num_parts, s.units, s.rows);
   return ok();
 }
 
@@ -228,7 +228,7 @@ mla_status mla_decode_paged(const mla_problem* p, const void* q, const void* kv_
   MLA_CHECK(check_ptr(workspace, "workspace", 16));
   MLA_CHECK(check_ptr(out, "out", 16));
   MLA_CHECK(check_ptr(lse, "lse", 4));
-  const size_t need = mla::ws_total_bytes(num_parts, s.units, s.rows, s.groups);
+  const size_t need = mla::ws_total_bytes(num_parts, s.units, s.rows);
   if (workspace_bytes < need)
     return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes: %zu given, %zu needed", workspace_bytes, need);
   if (s.units == 0) return ok();
@@ -245,7 +245,6 @@ mla_status mla_decode_paged(const mla_problem* p, const void* q, const void* kv_
   const size_t slots = mla::ws_slots(num_parts, s.units);
   a.ws_lse = (float*)workspace;
   a.ws_o = (uint16_t*)((char*)workspace + mla::ws_lse_bytes(slots, s.rows));
-  a.ws_flush = (float*)((char*)workspace + mla::ws_lse_bytes(slots, s.rows) + mla::ws_o_bytes(slots, s.rows));
   a.out = (uint16_t*)out;
   a.lse = lse;
   if (mla::small_decode_applies(s))
@@ -289,7 +288,7 @@ mla_status mla_decode_combine(const mla_problem* p, int32_t num_parts, const int
   MLA_CHECK(check_ptr(workspace, "workspace", 16));
   MLA_CHECK(check_ptr(out, "out", 16));
   MLA_CHECK(check_ptr(lse, "lse", 4));
-  const size_t need = mla::ws_total_bytes(num_parts, s.units, s.rows, s.groups);
+  const size_t need = mla::ws_total_bytes(num_parts, s.units, s.rows);
   if (workspace_bytes < need)
     return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes: %zu given, %zu needed", workspace_bytes, need);
   if (s.units == 0) return ok();

@@ -31,23 +31,31 @@
 //      (global_load_lds_dwordx4, no registers) while this one is computed.
 //      bf16 tiles are double buffered; FP8 rows land in a staging buffer and
 //      are dequantised into the bf16 tile: bf16(float(e4m3) * tile scale)
-//      (FlashMLA page, section 设计 2).  Keys that are not visible are copied
-//      from a zero row, so masked keys contribute exactly 0 to P*V.
+//      (FlashMLA page, section 设计 2).  Keys that are not visible are
+//      masked to -inf before the softmax; their rows are copied from a zero
+//      row (FP8, sparse) or from the tile's last visible row (dense bf16), so
+//      they hold finite values and contribute exactly 0 to P*V.
 //   3. S^T for half 0, then S^T for half 1 with the softmax of half 0
 //      interleaved between its MFMAs: mask, scale, max, exp2, row sum, and
 //      the bf16 P^T of the half written to LDS.
 //   4. Barrier; O^T += V^T P^T for half 0 with the softmax of half 1
 //      interleaved; barrier; O^T += V^T P^T for half 1.
-//   Online softmax in base 2 with a lazily refreshed running max: the
-//   running output is never rescaled in the loop; if some row's max grows by
-//   more than 8, every wave parks its partial outputs in a per-lane flush
-//   record and restarts them from zero (rare), merged back exactly at the end.
+//   The dense bf16 kernel runs P*V half a tile behind the scores (the
+//   schedule is spelled out at its tile loop).
+//   Online softmax in base 2 against a fixed reference: a row's
+//   probabilities are taken against the first finite maximum the row sees,
+//   so the running output is never rescaled in the loop (the correction
+//   factor of section 六 is 1 throughout).  Probabilities may exceed 1 by up
+//   to 2^kRestartMargin, far inside fp32.  If some row of the workgroup climbs
+//   further, the workgroup runs its segment again against the exact row
+//   maxima the first pass found (rare: scores that grow along the sequence).
 // Epilogue: a unit processed in one segment writes bf16 out and lse; a split
-// unit writes normalised fp32 partials and their lse to the workspace for the
-// combine kernel.
+// unit writes its normalised bf16 partial and fp32 lse to the workspace for
+// the combine kernel.
 //
-// LDS tile layout.  A key row of 576 bf16 is 72 chunks of 16 bytes; chunk c
-// of row r sits at chunk position
+// LDS tile layout of the FP8 and sparse kernels (the dense bf16 layout is
+// described at nope_row below).  A key row of 576 bf16 is 72 chunks of 16
+// bytes; chunk c of row r sits at chunk position
 //     (c / 8) * 512 + r * 8 + ((c + swz(r)) % 8),
 //     swz(r) = (r/4)%4 + 4*((r/2)%2).
 // Grouping by c / 8 makes every 1 KiB direct copy cover 8 rows x 8 chunks
@@ -81,7 +89,6 @@ typedef short i16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kThreads = 256;
 constexpr int kQSteps = kDqk / 16;   // 36 MFMA k-steps over the 576 dims
-constexpr float kRescaleThreshold = 8.0f;
 constexpr int kTileBytes = kPage * kDqk * 2;  // 73728: 72 chunk groups of 1 KiB
 constexpr int kTileLoads = kTileBytes / 1024;  // 72 direct copies, 18 per wave
 constexpr int kRopeOffset = 8 * 512 * 16;      // chunk group 8: dims 512..575
@@ -89,6 +96,14 @@ constexpr int kStageGroups = 6;                // raw FP8 row: 41 chunks in 6 gr
 constexpr int kStageBytes = kStageGroups * 8 * 16 * kPage;  // 49152
 constexpr int kStageLoads = kStageBytes / 1024;             // 48, 12 per wave
 constexpr int kPHalfBytes = kRowsPerGroup * 32 * 2;         // 8192: P^T of half a tile
+// Dense bf16 tile (the pipelined kernel).  The 1 KiB NoPE part of a key
+// row is copied by one contiguous copy; rows sit at a 1040-byte pitch in
+// groups of 16, row q of a group in slot nope_slot(q); the RoPE parts (64
+// rows x 128 B) follow in the 16-byte chunk rotation of the tile layout.
+constexpr int kNopeSlot = 1040;
+constexpr int kNopeGroup = 16 * kNopeSlot;                  // 16640
+constexpr int kDenseRope = 4 * kNopeGroup;                  // 66560
+constexpr int kDenseTileBytes = kDenseRope + kPage * 128;   // 74752
 
 template <typename T>
 __device__ inline __attribute__((address_space(3))) T* lds_ptr(const void* p) {
@@ -100,9 +115,22 @@ __device__ inline f32x2 swap_halves(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return f32x2{__uint_as_float(r[0]), __uint_as_float(r[1])};
 }
+// Maxima of scores in plain v_max3/v_max instructions: fmaxf would first
+// quiet possible signalling NaNs (an extra instruction per operand), which
+// MFMA results never are.
+__device__ inline float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ inline float max2f(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 __device__ inline float wave_max_pair(float x) {
   const f32x2 p = swap_halves(x);
-  return fmaxf(p[0], p[1]);
+  return max2f(p[0], p[1]);
 }
 __device__ inline float wave_sum_pair(float x) {
   const f32x2 p = swap_halves(x);
@@ -132,6 +160,15 @@ __device__ inline int tile_chunk(int r, int c) {
 
 // Byte offset of 16-byte chunk c (< 4) of query row r in a P^T half buffer.
 __device__ inline int p_chunk(int r, int c) { return (r * 4 + (c ^ ((r >> 2) & 3))) * 16; }
+
+// Dense layout: byte offset of the NoPE part of key row r, and of RoPE chunk
+// c (< 8) of row r.  Slot s(q) = 4*(q%4) + q/4 puts the 16 rows of a group
+// on 16 distinct bank groups (K operand reads: 16 rows at one chunk) and any
+// 4 consecutive rows 4 bank groups apart (transposed V reads: 4 rows x 4
+// adjacent chunks).
+__device__ inline int nope_slot(int q) { return 4 * (q & 3) + (q >> 2); }
+__device__ inline int nope_row(int r) { return kNopeGroup * (r >> 4) + kNopeSlot * nope_slot(r & 15); }
+__device__ inline int rope_chunk(int r, int c) { return kDenseRope + 128 * r + 16 * ((c + swz(r)) & 7); }
 
 // Zero bytes that stand in for the cache row of a key that is not visible.
 __device__ __attribute__((aligned(16))) const uint8_t g_zero_row[1168] = {};
@@ -254,57 +291,77 @@ struct TileCopy {
     constexpr int t = slot(PHASE, STEP);
     if constexpr (t >= 0) issue<t>(lane);
   }
-  // Schedule of dense bf16 tiles, whose P*V runs half a tile behind the
-  // scores.  During the first score chain: rows 0..31 of chunk groups 0..7
-  // (copies 0, 2, .., 14, after MFMAs 2, 6, .., 30).  During the second:
-  // the RoPE group of rows 0..31 (copy 16) first, then rows 32..63 of
-  // groups 0..7 (copies 1, 3, .., 15) and their RoPE group (17), after
-  // MFMAs 1, 4, .., 28.  Rows 0..31 of the tile are complete once at most
-  // kLateCopies copies are in flight; all of it once at most kEarlyCopies
-  // (those of the next tile's first chain) are.
-  static constexpr int kEarlyCopies = 8;
-  static constexpr int kLateCopies = 9;
-  static constexpr int slot_split(int phase, int step) {
-    if (phase == 0) return (step % 4 == 2 && step / 4 < kEarlyCopies) ? 2 * (step / 4) : -1;
-    if (step % 3 != 1 || step / 3 > kLateCopies) return -1;
-    const int i = step / 3;
-    return i == 0 ? 16 : (i == kLateCopies ? 17 : 2 * i - 1);
-  }
-  static constexpr bool split_slots_cover_copies() {
-    int seen[kCopies] = {};
-    for (int phase = 0; phase < 2; ++phase)
-      for (int step = 0; step < 36; ++step) {
-        const int t = slot_split(phase, step);
-        if (t >= kCopies) return false;
-        if (t >= 0) ++seen[t];
-      }
-    for (int t = 0; t < kCopies; ++t)
-      if (seen[t] != 1) return false;
-    // rows 0..31 (even copies) before rows 32..63, and copy 16 first in the
-    // second chain: exactly kLateCopies follow it
-    int after16 = 0;
-    bool past16 = false;
-    for (int step = 0; step < 36; ++step) {
-      const int t = slot_split(1, step);
-      if (t < 0) continue;
-      if (past16) ++after16;
-      if (t == 16) past16 = true;
-      else if (!past16) return false;
-      else if (t % 2 == 0) return false;
-    }
-    return after16 == kLateCopies;
-  }
-  template <int PHASE, int STEP>
-  __device__ inline void issue_split(int lane) const {
-    constexpr int t = slot_split(PHASE, STEP);
-    if constexpr (t >= 0) issue<t>(lane);
-  }
 };
 
 static_assert(TileCopy<0>::slots_cover_copies() && TileCopy<1>::slots_cover_copies(),
               "copy schedule must issue every copy of a tile once");
-static_assert(TileCopy<0>::split_slots_cover_copies(),
-              "split copy schedule must issue every copy of a tile once, rows 0..31 first");
+// Copy of one dense bf16 tile in the layout of the pipelined kernel, 18
+// copies per wave: copies 0..15 take the NoPE parts of key rows 4i + wave
+// (i = copy), one contiguous 1 KiB read each; copies 16 and 17 take the
+// RoPE parts of rows 8j .. 8j+7 for j = wave and wave + 4 (lane L: row
+// 8j + L/8, LDS slot L%8, which holds chunk (L%8 - swz(row)) mod 8).  A copy
+// whose source is one contiguous range moves far faster than one gathered
+// from eight rows.  Rows past the tile's visible range read the last visible
+// row instead: finite values whose probabilities are zero.
+struct DenseCopy {
+  const uint8_t* page;  // cache address of the tile's page (wave-uniform)
+  uint32_t mbase;       // LDS address of the tile buffer + 4 * kNopeSlot * wave (wave-uniform)
+  uint32_t rbase;       // LDS address of the buffer's RoPE region (wave-uniform)
+  int nvm1;             // last row of the tile to read (0..63)
+  uint32_t nlane;       // byte offset of this lane's 16 bytes in row `wave` of the page
+  uint32_t ncap;        // the same in row nvm1
+  __device__ inline void prepare(const uint8_t* __restrict__ kv, int pg, int tile, int vis,
+                                 uint32_t buf) {
+    // A tile with no visible row (the one past a segment's end) is copied
+    // from page 0 of the pool: its block-table entry may lie past the
+    // sequence's pages (an unused slot), and nothing reads the copy.
+    page = kv + (vis > tile * kPage ? (int64_t)pg * (kPage * 1152) : (int64_t)0);
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // nope_row(4i + w) = kNopeGroup * (i / 4) + kNopeSlot * (4w + i % 4)
+    mbase = buf + 4 * kNopeSlot * w;
+    rbase = buf + kDenseRope;
+    nvm1 = __builtin_amdgcn_readfirstlane(min(kPage - 1, max(vis - tile * kPage - 1, 0)));
+    const uint32_t l16 = 16 * (threadIdx.x & 63);
+    nlane = (uint32_t)w * 1152 + l16;
+    ncap = (uint32_t)nvm1 * 1152 + l16;
+  }
+  template <int I>
+  __device__ inline void issue() const {
+    if constexpr (I < 16) {
+      // row min(4I + wave, nvm1); the LDS destination is an immediate offset
+      // from this wave's base (M0 set by one scalar add)
+      const uint32_t voff = min(nlane + 4 * 1152 * I, ncap);
+      asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                   :: "v"(voff), "s"(page), "s"(mbase), "n"(kNopeGroup * (I >> 2) + kNopeSlot * (I & 3))
+                   : "memory", "m0", "scc");
+    } else {
+      int tid = threadIdx.x;
+      asm volatile("" : "+v"(tid));  // recomputed here rather than kept in registers
+      const int lane = tid & 63;
+      const int j = 4 * (I - 16) + (tid >> 6);
+      const int rd = 8 * j + (lane >> 3);  // row in the tile
+      const uint32_t voff = (uint32_t)(min(rd, nvm1) * 1152 + 1024 + 16 * (((lane & 7) - swz(rd)) & 7));
+      const uint32_t m0 = __builtin_amdgcn_readfirstlane(rbase + 1024 * j);
+      asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                   :: "v"(voff), "s"(page), "s"(m0) : "memory", "m0");
+    }
+  }
+  template <int I = 0>
+  __device__ inline void issue_all() const {
+    if constexpr (I < 18) {
+      issue<I>();
+      issue_all<I + 1>();
+    }
+  }
+};
+// Copies of tile kt+1 per phase of tile kt (18 per wave), all between P*V
+// MFMAs (the score chains keep the LDS busy with their K operand reads):
+//   B (P*V 1 of kt-1): NoPE rows 0..31      D (P*V 0): RoPE, rows 32..63
+// B1 of tile kt+1 needs B's copies and D's two RoPE copies (D's 8 NoPE
+// copies may be in flight); B2 of tile kt+1 needs D's (the 8 of B of tile
+// kt+1 may be in flight).
+constexpr int kDenseB1InFlight = 8;
+constexpr int kDenseB2InFlight = 8;
 
 // f(integral_constant<I>) for I = B .. E-1, unrolled at compile time.
 template <int B, int E, class F>
@@ -389,13 +446,15 @@ struct HalfDequant {
 // Back-to-back MFMAs chained through srcC need no wait states; the drain
 // below pads the chain before any VALU reads the result (an MFMA result read
 // by the VALU needs wait states the compiler cannot see through asm).
-// The leading s_nop 1 covers a VALU write of an operand register right
-// before the MFMA (two wait states), which the compiler cannot see either.
+// Their operands come from LDS reads (K) or are set once per segment (Q),
+// so no VALU instruction writes one within the two wait states before an
+// MFMA that the hardware would need; a build check verifies this on the
+// generated code of every instance.
 __device__ inline void mfma_s_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a), "v"(b));
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a), "v"(b));
 }
 __device__ inline void mfma_s_acc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
 __device__ inline void mfma_s_drain(f32x16& acc) {
   asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15" : "+v"(acc));
@@ -445,35 +504,21 @@ __device__ inline __attribute__((always_inline)) void score_chain(f32x16& acc, c
   score_chain_run(acc, kp, kb, k_off, qf, hook);
 }
 
-// Four accumulator values of a lane, copied out through the lane's private
-// 16-byte LDS slot.  Doing VALU arithmetic only on such copies keeps the
-// output accumulators in AGPRs for the whole kernel (arithmetic directly on
-// them makes the register allocator spill).
-__device__ inline f32x4 acc_quad(const f32x16& acc, int q4, f32x4* slot) {
-  *slot = f32x4{acc[4 * q4 + 0], acc[4 * q4 + 1], acc[4 * q4 + 2], acc[4 * q4 + 3]};
-  asm volatile("" ::: "memory");
-  const f32x4 v = *slot;
-  asm volatile("" ::: "memory");
-  return v;
-}
-
-// exp2(x - M) for a merge of partial sums, 0 for a part that saw no key.
-__device__ inline float merge_factor(float x, float M) {
-  return x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(x - M);
-}
-
 // Per-half softmax state of a lane (its row, its 16 keys of the half).
 struct HalfSoftmax {
   float tmax;   // max of the masked raw scores, then of the scaled row
-  float mnew;   // candidate running max
-  bool grow;    // the row's max grew past the refresh threshold
-  float mo;     // running max before this half's update
   float nmuse;  // minus the reference the probabilities are taken against
   float lh;     // this half's part of the row sum
-  float x, e;   // scaled score and probability in flight between steps
-  bf16x8 pf[2]; // bf16 probabilities, MFMA operand order
+  float x;      // scaled score in flight between steps
+  float e[2];   // the last two probabilities (paired for the bf16 conversion)
+  u32x4 pw[2];  // bf16 probability pairs, MFMA operand order
 };
-constexpr int kSoftmaxSteps = 29;
+constexpr int kSoftmaxSteps = 25;
+// The probabilities of a row are taken against a fixed reference: the row's
+// first finite maximum.  A row whose scores climb more than this (log2
+// units) above it sends the segment to a second pass against the exact row
+// maximum, so no probability ever exceeds 2^kRestartMargin.
+constexpr float kRestartMargin = 20.0f;
 // P*V reads V^T this many column groups (4 MFMAs each) ahead of its use.
 constexpr int kVAhead = 2;
 
@@ -482,25 +527,19 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
   // bf16: two tile buffers (double buffering).  FP8: one bf16 tile plus a
   // staging buffer for the raw rows of the next tile.  Separate objects let
   // the compiler see that copies into one buffer never alias reads of the
-  // other.
-  __shared__ __attribute__((aligned(16))) uint8_t lds0[kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t lds1[FMT == 0 ? kTileBytes : kStageBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t pbuf[kPHalfBytes];  // P^T of half 0
-  // FP8: P^T of half 1 (bf16 keeps it in the tile's RoPE chunk group; FP8
-  // overwrites rows 0..31 of the tile, RoPE chunks included, during the
-  // second P*V half)
-  __shared__ __attribute__((aligned(16))) uint8_t pbuf1[FMT == 1 ? kPHalfBytes : 16];
-  __shared__ float mold_s[2][kRowsPerGroup];  // per row: running max before each half's update
-  // per half, lane and wave: some row of the wave grew (every lane writes
-  // the wave's value to its own word, so the write needs no branch; the
-  // four waves' words of lane 0 are read as one 16-byte load)
-  __shared__ __attribute__((aligned(16))) uint32_t gflag[2][64][4];
-  __shared__ f32x4 oslots[kThreads];  // per-lane slot for copying accumulators
-  f32x4* const oslot = &oslots[threadIdx.x];
+  // other.  P^T of the two halves of a tile have buffers of their own, so
+  // the copies of the next tile never wait for them.
+  constexpr bool kPipelined = FMT == 0 && !SPARSE;  // tile loop order and layout, below
+  __shared__ __attribute__((aligned(256))) uint8_t lds0[kPipelined ? kDenseTileBytes : kTileBytes];
+  __shared__ __attribute__((aligned(256))) uint8_t
+      lds1[kPipelined ? kDenseTileBytes : (FMT == 0 ? kTileBytes : kStageBytes)];
+  __shared__ __attribute__((aligned(256))) uint8_t pbuf[kPHalfBytes];  // P^T of half 0
+  // P^T of half 1 (the pipelined kernel keeps it in the RoPE region of the
+  // tile it belongs to, dead once the tile's scores are done)
+  __shared__ __attribute__((aligned(256))) uint8_t pbuf1[kPipelined ? 16 : kPHalfBytes];
 
   const Shape& s = a.s;
   constexpr int kRowBytes = RowBytes<FMT>::value;
-  constexpr bool kPipelined = FMT == 0 && !SPARSE;  // tile loop order, below
 
   // Workgroup -> (part, row group).  Workgroups are dealt round-robin to
   // the 8 XCDs (XCD = id % 8).  XCD x takes the parts
@@ -511,7 +550,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
   // rather than in a chain of rounds along their first uses.
   asm volatile("" ::"s"(a.q), "s"(a.kv), "s"(a.block_table), "s"(a.seqlens), "s"(a.indices),
                "s"(a.sched), "s"(a.num_splits), "s"(a.num_parts), "s"(a.ws_lse), "s"(a.ws_o),
-               "s"(a.ws_flush), "s"(a.out), "s"(a.lse), "s"(s.units), "s"(s.rows), "s"(s.groups),
+               "s"(a.out), "s"(a.lse), "s"(s.units), "s"(s.rows), "s"(s.groups),
                "s"(s.s_q), "s"(s.h_q), "s"(s.topk), "s"(s.max_pages), "s"(s.is_causal),
                "s"(s.natural), "s"(s.scale_log2));
   // The schedule, sequence lengths, split counts and (dense) block table
@@ -535,15 +574,6 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
   const int rs = wave * 32 + n;                 // score row of this lane, in the group
   const int r = grp * kRowsPerGroup + rs;       // ... in the unit
   const bool row_ok = r < s.rows;
-  // per-lane flush record: 256 output values (block (cb, rb) at 16*(4cb+rb)),
-  // the 4 output rows' maxima, the score row's sum and maximum
-  // (recomputed where used, so no register holds it through the tile loop)
-  const int64_t rec_wg = (int64_t)(part * s.groups + grp) * kThreads;
-  auto flush_rec = [&]() -> float* {
-    int tid = threadIdx.x;
-    asm volatile("" : "+v"(tid));
-    return a.ws_flush + (rec_wg + tid) * kFlushFloats;
-  };
 
   // Lane-constant parts of the LDS operand addresses (tile layout above).
   // K operand, step st: row 32*kb2 + n, chunk 2*st + h.
@@ -566,6 +596,17 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
   int p_off[2];
 #pragma unroll
   for (int sp = 0; sp < 2; ++sp) p_off[sp] = p_chunk(n, 2 * sp + h);
+  // Dense layout (pipelined kernel).  K operand of row 32*kb2 + n, chunk
+  // 2*st + h: NoPE at kbase + 33280*kb2 + 32*st (st < 32), RoPE at
+  // rope_off[st - 32] + 4096*kb2.  V^T operand of row 32*kb2 + 16*sp + 8*e4
+  // + 4*h + j16/4, chunk 16*wave + 4*cb + 2*(n/16) + (j16%4)/2, byte
+  // 8*(j16%2): vbase + 2080*e4 + 16640*(2*kb2 + sp) + 64*cb.
+  const int kbase = nope_row(n) + 16 * h;
+  int rope_off[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) rope_off[i] = rope_chunk(n, 2 * i + h);
+  const int vbase = kNopeSlot * (4 * (j16 >> 2) + h) +
+                    16 * (16 * wave + 2 * (n >> 4) + ((j16 & 3) >> 1)) + 8 * (j16 & 1);
 
   for (int u = ub; u < s.units && (u < ue || (u == ue && ke > 0)); ++u) {
     // The previous segment is fully consumed (tiles, P^T, epilogue staging
@@ -636,535 +677,574 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
       tlim = L - s.s_q + (int)(((float)qr + 0.5f) * s.inv_h_q);
     }
 
-    float m = -INFINITY;  // running (possibly stale) max of the score row, log2 units
-    float l = 0.0f;       // running sum of this lane's half of the keys
-    bool flushed = false; // workgroup-uniform: outputs parked in the flush records
+    float m;              // reference of the row's probabilities, log2 units
+    float l;              // running sum of this lane's half of the keys
+    float rmax;           // running maximum of the row's scaled scores
     f32x16 o[4][4];       // O^T block (column block cb of this wave, row block rb)
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) o[cb][rb] = f32x16{};
-
-    // Row resolution of sparse tiles.  Every wave resolves all 64 keys of a
-    // tile (lane k: key k) and takes the rows it copies from the resolving
-    // lanes.
-    //   res_t:   logical position of key `lane` in tile kt+2
-    //   res_off: cache byte offset of key `lane` in tile kt+1 (-1: masked)
-    const int32_t* idx_row = SPARSE ? a.indices + (int64_t)u * s.topk : nullptr;
-    auto position = [&](int tile) -> int {  // logical key position, or -1
-      const int k = tile * kPage + lane;
-      if constexpr (SPARSE) {
-        const int t = idx_row[k < s.topk ? k : s.topk - 1];  // always one load
-        return (tile < kend && k < s.topk) ? t : -1;
-      }
-      return tile < kend ? k : -1;
-    };
-    auto visible = [&](int t) { return t >= 0 && t < L; };
-    auto page_of = [&](int t) -> int { return bt_row[visible(t) ? (t >> 6) : 0]; };  // one load
-    auto offset_of = [&](int t, int page) -> int64_t {
-      return visible(t) ? ((int64_t)page * kPage + (t & 63)) * kRowBytes : (int64_t)-1;
-    };
-    // Dense: the page of tile kt+1 (wave-uniform, a scalar load issued one
-    // tile ahead).  Sparse: the per-key resolution below.
-    int pg_next = 0;
-    constexpr int kResolveLoads = SPARSE ? 2 : 0;  // vector loads per thread per tile
-    int res_t = -1, pg2 = 0, t3 = -1;
-    bool t3_ok = false;  // sparse: tile kt+3's slot of this lane holds an index
-    int64_t res_off = -1;
-    uint64_t vm_cur = 0;  // keys of the current tile that are visible (sparse masking)
-    {
-      TileCopy<FMT> first;
-      if constexpr (SPARSE) {
-        const int t0 = position(kfirst);
-        const int t1 = position(kfirst + 1);
-        res_t = position(kfirst + 2);
-        const int64_t off0 = offset_of(t0, page_of(t0));
-        res_off = offset_of(t1, page_of(t1));
-        vm_cur = __ballot(off0 >= 0);
-        first.prepare(a.kv, off0, lds_addr(FMT == 0 ? lds0 : lds1), wave, lane);
-      } else {
-        // (past the segment's end the second page is not used: its rows
-        // are copied from the zero row)
-        first.prepare_page(a.kv, pg_first, kfirst, L, lds_addr(FMT == 0 ? lds0 : lds1), wave, lane);
-        pg_next = pg_second;
-      }
-      first.issue_all(lane);
-      if constexpr (SPARSE) load_q();
-      if constexpr (FMT == 1) {
-        MLA_WAIT_VMCNT(0);
-        __syncthreads();
-        HalfDequant dq;
-        dq.all(lds1, lds0, 0);  // rows 32..63 are dequantised during the first score chain
-      }
-    }
-    // Everything loaded so far (Q, rows, the first tile) is needed before the
-    // first compute anyway.  Waiting here also keeps the compiler from
-    // placing its own waits for the Q loads inside the tile loop, where they
-    // would stall on the next tile's copies that it cannot see.
-    MLA_WAIT_VMCNT(0);
-    // The kernel works with a positive score scale: scale * (q.k) equals
-    // |scale| * ((-q).k) for a negative scale (a sign flip of bf16 is exact)
-    // and 1 * (0.k) = 0 for a zero scale.
-    if (s.scale_log2 <= 0.0f) {
-      const uint32_t flip = s.scale_log2 < 0.0f ? 0x80008000u : 0u;
-      const uint32_t keep = s.scale_log2 < 0.0f ? 0xffffffffu : 0u;
-#pragma unroll
-      for (int st = 0; st < kQSteps; ++st) {
-        u32x4 w = __builtin_bit_cast(u32x4, qf[st]);
-        w = (w & keep) ^ flip;
-        qf[st] = __builtin_bit_cast(bf16x8, w);
-      }
-    }
-
-    // Park this lane's outputs (all 16 blocks) and its score row's sum in
-    // the flush record and restart them from zero.  Two partial results
-    // with references m1, m2 merge as M = max, each scaled by 2^(m_i - M).
-    // Every party to a row applies the same sequence of maxima, so the
-    // copies of a row's record maximum stay identical.
-    auto flush = [&](int half, float mo_own) __attribute__((always_inline)) {
-      float* rec = flush_rec();
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        const float mo = mold_s[half][32 * rb + n];
-        float M = mo, fa = 0.0f, fc = 1.0f;
-        if (flushed) {
-          const float mr = rec[256 + rb];
-          M = fmaxf(mr, mo);
-          fa = merge_factor(mr, M);
-          fc = merge_factor(mo, M);
-        }
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            f32x4* dst = reinterpret_cast<f32x4*>(rec + (4 * cb + rb) * 16 + 4 * q4);
-            const f32x4 old = flushed ? *dst * fa : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            *dst = old + acc_quad(o[cb][rb], q4, oslot) * fc;
-          }
-          // zero through the MFMA unit: keeps the accumulators in AGPRs
-          o[cb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf16x8{}, bf16x8{}, f32x16{}, 0, 0, 0);
-        }
-        rec[256 + rb] = M;
-      }
-      float M = mo_own, fa = 0.0f, fc = 1.0f;
-      if (flushed) {
-        const float mr = rec[261];
-        M = fmaxf(mr, mo_own);
-        fa = merge_factor(mr, M);
-        fc = merge_factor(mo_own, M);
-      }
-      rec[260] = (flushed ? rec[260] * fa : 0.0f) + l * fc;
-      rec[261] = M;
+    uint8_t* ks = lds0;   // buffer of the tile being scored
+    // Second pass: the exact row maximum of the first, parked in LDS (thread
+    // slot, behind the restart votes) so that no register carries it across
+    // the pass.  It is read back before the first barrier of the pass, and
+    // no P^T store reaches this part of pbuf before that barrier.
+    float* mref_slot = reinterpret_cast<float*>(pbuf + 4096 + 256);
+    for (int pass = 0;; ++pass) {
+      m = pass == 0 ? -INFINITY : mref_slot[threadIdx.x];
       l = 0.0f;
-      flushed = true;
-    };
+      rmax = -INFINITY;
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) o[cb][rb] = f32x16{};
 
-    // Per-tile state read by the softmax and P*V steps below.
-    uint8_t* ks = lds0;               // buffer of the tile being scored
-    uint64_t vm = 0;                  // sparse: visible keys of that tile
-    uint32_t lanemask[2] = {0u, 0u};  // sparse: visibility of keys 32*kb2 + 4*h + (0..31)
-    int jlim = 63;                    // dense: keys j <= jlim of that tile may count
-
-    // The softmax of half kb2 (raw scores in sc; scores in log2 units are
-    // scale * raw with scale > 0), cut into kSoftmaxSteps small steps of a
-    // few VALU instructions each.  One step goes between two MFMAs: an
-    // MFMA cannot issue while the matrix core is busy, and only the
-    // independent instructions that precede it in program order run in
-    // the shadow of the previous one.
-    //   0..3   mask the half if any of its keys is not visible (step 0),
-    //          max of the raw scores
-    //   4..9   row max across the lane pair, running max update, publish
-    //   9..26  probabilities, software-pipelined so no step waits on a
-    //          result of the same step: step 10+v takes the exponential of
-    //          score v, the scaled score v+1 and the row sum and bf16
-    //          operand of probability v-1
-    //   27, 28 store the half's P^T
-    auto softmax_step = [&](int kb2, f32x16& sc, HalfSoftmax& hs, int u) __attribute__((always_inline)) {
-      if (u == 0) {
-        // dense: visible keys are a prefix of the tile (tail and causal
-        // limits folded into jlim); sparse: the per-key validity mask
-        // (bit 8*(v/4) + v%4 of the lane's mask word is key
-        // 32*kb2 + 8*(v/4) + 4*h + v%4)
-        bool full;
+      // Row resolution of sparse tiles.  Every wave resolves all 64 keys of a
+      // tile (lane k: key k) and takes the rows it copies from the resolving
+      // lanes.
+      //   res_t:   logical position of key `lane` in tile kt+2
+      //   res_off: cache byte offset of key `lane` in tile kt+1 (-1: masked)
+      const int32_t* idx_row = SPARSE ? a.indices + (int64_t)u * s.topk : nullptr;
+      auto position = [&](int tile) -> int {  // logical key position, or -1
+        const int k = tile * kPage + lane;
         if constexpr (SPARSE) {
-          uint32_t word = (uint32_t)(vm >> (32 * kb2));
-          asm volatile("" : "+s"(word));  // a 32-bit scalar test, not a 64-bit constant compare
-          full = word == 0xffffffffu;
+          const int t = idx_row[k < s.topk ? k : s.topk - 1];  // always one load
+          return (tile < kend && k < s.topk) ? t : -1;
+        }
+        return tile < kend ? k : -1;
+      };
+      auto visible = [&](int t) { return t >= 0 && t < L; };
+      auto page_of = [&](int t) -> int { return bt_row[visible(t) ? (t >> 6) : 0]; };  // one load
+      auto offset_of = [&](int t, int page) -> int64_t {
+        return visible(t) ? ((int64_t)page * kPage + (t & 63)) * kRowBytes : (int64_t)-1;
+      };
+      // Dense: the page of tile kt+1 (wave-uniform, a scalar load issued one
+      // tile ahead).  Sparse: the per-key resolution below.
+      int pg_next = 0;
+      constexpr int kResolveLoads = SPARSE ? 2 : 0;  // vector loads per thread per tile
+      int res_t = -1, pg2 = 0, t3 = -1;
+      bool t3_ok = false;  // sparse: tile kt+3's slot of this lane holds an index
+      int64_t res_off = -1;
+      uint64_t vm_cur = 0;  // keys of the current tile that are visible (sparse masking)
+      {
+        TileCopy<FMT> first;
+        if constexpr (SPARSE) {
+          const int t0 = position(kfirst);
+          const int t1 = position(kfirst + 1);
+          res_t = position(kfirst + 2);
+          const int64_t off0 = offset_of(t0, page_of(t0));
+          res_off = offset_of(t1, page_of(t1));
+          vm_cur = __ballot(off0 >= 0);
+          first.prepare(a.kv, off0, lds_addr(FMT == 0 ? lds0 : lds1), wave, lane);
+        } else if constexpr (kPipelined) {
+          DenseCopy fd;
+          fd.prepare(a.kv, pg_first, kfirst, L, lds_addr(lds0));
+          fd.issue_all();
+          pg_next = pg_second;
         } else {
-          full = __builtin_amdgcn_readfirstlane(__all(jlim >= 32 * kb2 + 31) ? 1 : 0) != 0;
+          // (past the segment's end the second page is not used: its rows
+          // are copied from the zero row)
+          first.prepare_page(a.kv, pg_first, kfirst, L, lds_addr(FMT == 0 ? lds0 : lds1), wave, lane);
+          pg_next = pg_second;
         }
-        if (!full) {
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int key = kb2 * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-            const bool ok = SPARSE ? ((lanemask[kb2] >> (8 * (v >> 2) + (v & 3))) & 1) != 0 : key <= jlim;
-            sc[v] = ok ? sc[v] : -INFINITY;
-          }
+        if constexpr (!kPipelined) first.issue_all(lane);
+        if (SPARSE || pass > 0) load_q();
+        if constexpr (FMT == 1) {
+          MLA_WAIT_VMCNT(0);
+          __syncthreads();
+          HalfDequant dq;
+          dq.all(lds1, lds0, 0);  // rows 32..63 are dequantised during the first score chain
         }
-        hs.tmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-      } else if (u < 4) {
-        hs.tmax = fmaxf(fmaxf(hs.tmax, sc[4 * u]), fmaxf(sc[4 * u + 1], fmaxf(sc[4 * u + 2], sc[4 * u + 3])));
-      } else if (u == 4) {
-        hs.tmax = wave_max_pair(hs.tmax) * scale;  // scale > 0 keeps the max; -inf stays -inf
-      } else if (u == 5) {
-        hs.mnew = fmaxf(m, hs.tmax);
-        // A row that has seen no visible key yet holds O = 0 and l = 0:
-        // it adopts the new max for free.
-        if (m == -INFINITY) m = hs.mnew;
-      } else if (u == 6) {
-        hs.grow = hs.mnew > m + kRescaleThreshold;
-        hs.mo = m;
-        if (hs.grow) m = hs.mnew;
-      } else if (u == 7) {
-        hs.nmuse = (m == -INFINITY) ? 0.0f : -m;
-        hs.lh = 0.0f;
-      } else if (u == 8) {
-        // the row index is recomputed here rather than kept in a register
-        // (both lanes of a row pair hold the same maximum and write it)
-        int tid = threadIdx.x;
-        asm volatile("" : "+v"(tid));
-        mold_s[kb2][((tid >> 6) << 5) + (tid & 31)] = hs.mo;
-      } else if (u == 9) {
-        const bool any_grow = __ballot(hs.grow) != 0;
-        int tid = threadIdx.x;  // (address recomputed, not kept in a register)
-        asm volatile("" : "+v"(tid));
-        gflag[kb2][tid & 63][tid >> 6] = any_grow ? 1u : 0u;
-        hs.x = __builtin_fmaf(sc[0], scale, hs.nmuse);
-      } else if (u < 27) {
-        const int v = u - 10;  // 0..16
-        float e = 0.0f;
-        if (v < 16) e = __builtin_amdgcn_exp2f(hs.x);
-        if (v < 15) hs.x = __builtin_fmaf(sc[v + 1], scale, hs.nmuse);
-        if (v > 0) {
-          hs.lh += hs.e;
-          // keeps the add in this step: otherwise the compiler sinks all 16
-          // into one dependent chain at the row-sum update, with every
-          // probability held in a register until then
-          asm volatile("" : "+v"(hs.lh));
-          hs.pf[(v - 1) >> 3][(v - 1) & 7] = (__bf16)hs.e;
-        }
-        hs.e = e;
-      } else if (u < 29) {
-        const int sp = u - 27;
-        uint8_t* pb = kb2 == 0 ? pbuf : (FMT == 1 ? pbuf1 : ks + kRopeOffset);
-        // the address is recomputed from the thread index, not kept in a
-        // register through the tile loop
-        int tid = threadIdx.x;
-        asm volatile("" : "+v"(tid));
-        const int pw = tid >> 6, pn = tid & 31, ph = (tid >> 5) & 1;
-        *reinterpret_cast<bf16x8*>(pb + 2048 * pw + p_chunk(pn, 2 * sp + ph)) = hs.pf[sp];
       }
-    };
-
-    // Whether some row of the workgroup grew in half kb2 (readable once
-    // the barrier after that half's softmax has passed): the LDS words, and
-    // the wave-uniform answer.  Reading them well before the P*V half that
-    // depends on them keeps the LDS round trip off its start.
-    auto grew_word = [&](int kb2) -> u32x4 { return *reinterpret_cast<const u32x4*>(gflag[kb2][0]); };
-    auto grew_any = [&](u32x4 w) -> bool {
-      return __builtin_amdgcn_readfirstlane(w[0] | w[1] | w[2] | w[3]) != 0;
-    };
-    // Before the P*V of a half: if any wave saw a row grow, every wave
-    // parks its outputs; then this lane's row sum takes the half's part.
-    auto settle = [&](int kb2, float mo, float lh, bool grew) __attribute__((always_inline)) {
-      if (grew) flush(kb2, mo);
-      l += lh;
-    };
-
-    // O^T += V^T P^T for half kb2 of the tile in buffer vt, over this wave's
-    // 4 column blocks and the 4 row blocks: 8 groups g = (key step sp = g/4, column block cb = g%4)
-    // of 4 MFMAs, hook(j) after MFMA j (32 of them).  Within each 16-lane
-    // group, transpose read: lane j points at 4 consecutive columns of one
-    // key row (key j/4 of the group's 4) and lane i receives column i of
-    // those 4 keys.  k slot (h, e) <-> key 32*kb2 + 16*sp + 8*(e/4) + 4*h +
-    // e%4.  V^T operands rotate through kVAhead + 1 registers; the first
-    // kVAhead groups' operands are tile data and are read before the
-    // barrier that publishes the half's P^T (pv_prefetch).
-    auto load_v = [&](const uint8_t* vt, int kb2, int g) {
-      const int sp = g >> 2, cb = g & 3;
-      const uint8_t* vb = vt + 8192 * (2 * wave + (cb >> 1)) + 4096 * kb2 + 2048 * sp;
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_ptr<i16x4>(vb + v_off[cb & 1][0]));
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_ptr<i16x4>(vb + v_off[cb & 1][1]));
-      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    };
-    constexpr int kVRegs = kVAhead + 1;
-    constexpr int kVPrefetchReads = 2 * kVAhead;  // LDS reads issued by pv_prefetch
-    auto pv_prefetch = [&](const uint8_t* vt, int kb2, bf16x8* vf) __attribute__((always_inline)) {
+      // Everything loaded so far (Q, rows, the first tile) is needed before the
+      // first compute anyway.  Waiting here also keeps the compiler from
+      // placing its own waits for the Q loads inside the tile loop, where they
+      // would stall on the next tile's copies that it cannot see.
+      MLA_WAIT_VMCNT(0);
+      // The kernel works with a positive score scale: scale * (q.k) equals
+      // |scale| * ((-q).k) for a negative scale (a sign flip of bf16 is exact)
+      // and 1 * (0.k) = 0 for a zero scale.
+      if (s.scale_log2 <= 0.0f) {
+        const uint32_t flip = s.scale_log2 < 0.0f ? 0x80008000u : 0u;
+        const uint32_t keep = s.scale_log2 < 0.0f ? 0xffffffffu : 0u;
 #pragma unroll
-      for (int g = 0; g < kVAhead; ++g) vf[g] = load_v(vt, kb2, g);
-    };
-    auto load_p = [&](const uint8_t* pb, int sp, int rb) {
-      return *reinterpret_cast<const bf16x8*>(pb + 2048 * rb + p_off[sp]);
-    };
-    // Every first operand of a half: V^T as pv_prefetch, and the P^T blocks
-    // of the first key step (once the half's P^T is visible).
-    constexpr int kPVBeginReads = kVPrefetchReads + 4;
-    auto pv_begin = [&](const uint8_t* vt, int kb2, const uint8_t* pb, bf16x8* vf, bf16x8* pfr)
-        __attribute__((always_inline)) {
-      pv_prefetch(vt, kb2, vf);
+        for (int st = 0; st < kQSteps; ++st) {
+          u32x4 w = __builtin_bit_cast(u32x4, qf[st]);
+          w = (w & keep) ^ flip;
+          qf[st] = __builtin_bit_cast(bf16x8, w);
+        }
+      }
+
+      // Per-tile state read by the softmax and P*V steps below.
+      uint64_t vm = 0;                  // sparse: visible keys of that tile
+      uint32_t lanemask[2] = {0u, 0u};  // sparse: visibility of keys 32*kb2 + 4*h + (0..31)
+      int jlim = 63;                    // dense: keys j <= jlim of that tile may count
+
+      // The softmax of half kb2 (raw scores in sc; scores in log2 units are
+      // scale * raw with scale > 0), cut into kSoftmaxSteps small steps of a
+      // few VALU instructions each.  One step goes between two MFMAs: an
+      // MFMA cannot issue while the matrix core is busy, and only the
+      // independent instructions that precede it in program order run in
+      // the shadow of the previous one.
+      //   0..3   mask the half if any of its keys is not visible (step 0),
+      //          max of the raw scores
+      //   4, 5   row max across the lane pair, running maximum; a row that
+      //          has seen no finite score yet adopts this half's maximum as
+      //          its reference (its output and sum are still zero)
+      //   6..22  probabilities, software-pipelined so no step waits on a
+      //          result of the same step: step 6+v takes the exponential of
+      //          score v, the scaled score v+1, the row sum of probability
+      //          v-1 and, at even v, the bf16 pair of probabilities v-2, v-1
+      //   23, 24 store the half's P^T
+      auto softmax_step = [&](int kb2, f32x16& sc, HalfSoftmax& hs, int u, int jl, uint8_t* pdst)
+          __attribute__((always_inline)) {
+        if (u == 0) {
+          // dense: visible keys are a prefix of the tile (tail and causal
+          // limits folded into jlim); sparse: the per-key validity mask
+          // (bit 8*(v/4) + v%4 of the lane's mask word is key
+          // 32*kb2 + 8*(v/4) + 4*h + v%4)
+          bool full;
+          if constexpr (SPARSE) {
+            uint32_t word = (uint32_t)(vm >> (32 * kb2));
+            asm volatile("" : "+s"(word));  // a 32-bit scalar test, not a 64-bit constant compare
+            full = word == 0xffffffffu;
+          } else {
+            full = __builtin_amdgcn_readfirstlane(__all(jl >= 32 * kb2 + 31) ? 1 : 0) != 0;
+          }
+          if (!full) {
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) pfr[rb] = load_p(pb, 0, rb);
-    };
-    auto pv_run = [&](int kb2, const uint8_t* vt, const uint8_t* pb, bf16x8* vf, bf16x8* pfr,
-                      auto&& pre, auto&& hook) __attribute__((always_inline)) {
-      pre();  // runs while the first operands are in flight
-      static_for<0, 8>([&](auto g_c) __attribute__((always_inline)) {
-        constexpr int g = decltype(g_c)::value;
-        constexpr int cb = g & 3;
-        if constexpr (g + kVAhead < 8) vf[(g + kVAhead) % kVRegs] = load_v(vt, kb2, g + kVAhead);
-        static_for<0, 4>([&](auto rb_c) __attribute__((always_inline)) {
-          constexpr int rb = decltype(rb_c)::value;
-          o[cb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[g % kVRegs], pfr[rb], o[cb][rb], 0, 0, 0);
-          // the second key step's P^T block rb, right after its last use
-          if constexpr (g == 3) pfr[rb] = load_p(pb, 1, rb);
-          hook(std::integral_constant<int, 4 * g + rb>{});
-          __builtin_amdgcn_sched_barrier(0);
+            for (int v = 0; v < 16; ++v) {
+              const int key = kb2 * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+              const bool ok = SPARSE ? ((lanemask[kb2] >> (8 * (v >> 2) + (v & 3))) & 1) != 0 : key <= jl;
+              sc[v] = ok ? sc[v] : -INFINITY;
+            }
+          }
+          hs.tmax = max3f(max3f(sc[0], sc[1], sc[2]), sc[3], sc[4]);
+        } else if (u < 4) {
+          // scores 5u .. 5u+4 (u = 3: 15 only)
+          hs.tmax = u < 3 ? max3f(max3f(hs.tmax, sc[5 * u], sc[5 * u + 1]), sc[5 * u + 2], max2f(sc[5 * u + 3], sc[5 * u + 4]))
+                          : max2f(hs.tmax, sc[15]);
+        } else if (u == 4) {
+          hs.tmax = wave_max_pair(hs.tmax) * scale;  // scale > 0 keeps the max; -inf stays -inf
+          rmax = max2f(rmax, hs.tmax);
+        } else if (u == 5) {
+          if (m == -INFINITY) m = hs.tmax;
+          hs.nmuse = (m == -INFINITY) ? 0.0f : -m;
+          hs.lh = 0.0f;
+          hs.x = __builtin_fmaf(sc[0], scale, hs.nmuse);
+        } else if (u < 23) {
+          const int v = u - 6;  // 0..16
+          if (v >= 2 && (v & 1) == 0) {
+            const int w = (v - 2) >> 1;  // bf16 pair of probabilities v-2, v-1
+            hs.pw[w >> 2][w & 3] = pk_bf16(hs.e[0], hs.e[1]);
+          }
+          if (v > 0) {
+            hs.lh += hs.e[(v - 1) & 1];
+            // keeps the add in this step: otherwise the compiler sinks all 16
+            // into one dependent chain at the end, with every probability
+            // held in a register until then
+            asm volatile("" : "+v"(hs.lh));
+          }
+          if (v < 16) hs.e[v & 1] = __builtin_amdgcn_exp2f(hs.x);
+          if (v < 15) hs.x = __builtin_fmaf(sc[v + 1], scale, hs.nmuse);
+          if (v == 16) l += hs.lh;
+        } else if (u < 25) {
+          const int sp = u - 23;
+          // the address is recomputed from the thread index, not kept in a
+          // register through the tile loop
+          int tid = threadIdx.x;
+          asm volatile("" : "+v"(tid));
+          const int pw = tid >> 6, pn = tid & 31, ph = (tid >> 5) & 1;
+          asm volatile("" ::: "memory");  // LDS accesses stay in program order around the store
+          *reinterpret_cast<u32x4*>(pdst + 2048 * pw + p_chunk(pn, 2 * sp + ph)) = hs.pw[sp];
+          asm volatile("" ::: "memory");
+        }
+      };
+
+      // O^T += V^T P^T for half kb2 of the tile in buffer vt, over this wave's
+      // 4 column blocks and the 4 row blocks: 8 groups g = (key step sp = g/4, column block cb = g%4)
+      // of 4 MFMAs, hook(j) after MFMA j (32 of them).  Within each 16-lane
+      // group, transpose read: lane j points at 4 consecutive columns of one
+      // key row (key j/4 of the group's 4) and lane i receives column i of
+      // those 4 keys.  k slot (h, e) <-> key 32*kb2 + 16*sp + 8*(e/4) + 4*h +
+      // e%4.  V^T operands rotate through kVAhead + 1 registers; the first
+      // kVAhead groups' operands are tile data and are read before the
+      // barrier that publishes the half's P^T (pv_prefetch).
+      auto load_v = [&](const uint8_t* vt, int kb2, int g) {
+        const int sp = g >> 2, cb = g & 3;
+        i16x4 lo, hi;
+        if constexpr (kPipelined) {
+          const uint8_t* vb = vt + vbase + kNopeGroup * (2 * kb2 + sp) + 64 * cb;
+          lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_ptr<i16x4>(vb));
+          hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_ptr<i16x4>(vb + 2 * kNopeSlot));
+        } else {
+          const uint8_t* vb = vt + 8192 * (2 * wave + (cb >> 1)) + 4096 * kb2 + 2048 * sp;
+          lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_ptr<i16x4>(vb + v_off[cb & 1][0]));
+          hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_ptr<i16x4>(vb + v_off[cb & 1][1]));
+        }
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      constexpr int kVRegs = kVAhead + 1;
+      constexpr int kVPrefetchReads = 2 * kVAhead;  // LDS reads issued by pv_prefetch
+      auto pv_prefetch = [&](const uint8_t* vt, int kb2, bf16x8* vf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int g = 0; g < kVAhead; ++g) vf[g] = load_v(vt, kb2, g);
+      };
+      // (the lane's address is formed once per key step and kept opaque, so
+      // the row blocks are immediate offsets rather than one VALU add each:
+      // P^T buffers lie beyond the 64 KiB an immediate offset reaches)
+      using lds_u8 = const __attribute__((address_space(3))) uint8_t;
+      auto p_lane = [&](const uint8_t* pb, int sp) {
+        lds_u8* b = lds_ptr<const uint8_t>(pb + p_off[sp]);  // an LDS pointer: ds_read, not flat
+        asm volatile("" : "+v"(b));
+        return b;
+      };
+      auto load_p = [&](lds_u8* pl, int rb) {
+        return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(pl + 2048 * rb);
+      };
+      // Every first operand of a half: V^T as pv_prefetch, and the P^T blocks
+      // of the first key step (once the half's P^T is visible).
+      auto pv_begin = [&](const uint8_t* vt, int kb2, const uint8_t* pb, bf16x8* vf, bf16x8* pfr)
+          __attribute__((always_inline)) {
+        pv_prefetch(vt, kb2, vf);
+        lds_u8* pl = p_lane(pb, 0);
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) pfr[rb] = load_p(pl, rb);
+      };
+      auto pv_run = [&](int kb2, const uint8_t* vt, const uint8_t* pb, bf16x8* vf, bf16x8* pfr,
+                        auto&& hook) __attribute__((always_inline)) {
+        lds_u8* pl1 = p_lane(pb, 1);
+        static_for<0, 8>([&](auto g_c) __attribute__((always_inline)) {
+          constexpr int g = decltype(g_c)::value;
+          constexpr int cb = g & 3;
+          if constexpr (g + kVAhead < 8) vf[(g + kVAhead) % kVRegs] = load_v(vt, kb2, g + kVAhead);
+          static_for<0, 4>([&](auto rb_c) __attribute__((always_inline)) {
+            constexpr int rb = decltype(rb_c)::value;
+            o[cb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[g % kVRegs], pfr[rb], o[cb][rb], 0, 0, 0);
+            // the second key step's P^T block rb, right after its last use
+            if constexpr (g == 3) pfr[rb] = load_p(pl1, rb);
+            hook(std::integral_constant<int, 4 * g + rb>{});
+            __builtin_amdgcn_sched_barrier(0);
+          });
         });
-      });
-    };
-    auto pv_half = [&](int kb2, const uint8_t* vt, const uint8_t* pb, bf16x8* vf, auto&& pre,
-                       auto&& hook) __attribute__((always_inline)) {
-      bf16x8 pfr[4];
+      };
+      auto pv_half = [&](int kb2, const uint8_t* vt, const uint8_t* pb, bf16x8* vf, auto&& pre,
+                         auto&& hook) __attribute__((always_inline)) {
+        bf16x8 pfr[4];
+        lds_u8* pl = p_lane(pb, 0);
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) pfr[rb] = load_p(pb, 0, rb);
-      pv_run(kb2, vt, pb, vf, pfr, pre, hook);
-    };
+        for (int rb = 0; rb < 4; ++rb) pfr[rb] = load_p(pl, rb);
+        pre();  // runs while the first operands are in flight
+        pv_run(kb2, vt, pb, vf, pfr, hook);
+      };
 
-    // Dense bf16 tiles run one P*V half behind the scores, so that both
-    // softmax halves sit between P*V MFMAs (register-fed, with room for
-    // VALU work) rather than between score MFMAs (which wait on LDS):
-    //   B1 | scores 0 of kt (copies: rows 0..31 of kt+1)
-    //      | P*V 1 of kt-1 + softmax 0 of kt
-    //   B2 | scores 1 of kt (copies: RoPE group and rows 32..63 of kt+1)
-    //   B3 | P*V 0 of kt + softmax 1 of kt (its P^T into kt's RoPE group)
-    // The copies of rows 32..63 and of the RoPE group overwrite what P*V 1
-    // of kt-1 reads, so they wait for B2; they need to land only by B1 / B2
-    // of kt+1.
-    if constexpr (kPipelined) {
-      const __attribute__((address_space(4))) int32_t* bt_const =
-          (const __attribute__((address_space(4))) int32_t*)bt_row;  // scalar loads
-      float prev_mo = -INFINITY, prev_lh = 0.0f;  // softmax 1 of tile kt-1, for its P*V
-      bf16x8 vf[kVRegs];
-      for (int kt = kfirst; kt < kend; ++kt) {
-        const bool odd = ((kt - kfirst) & 1) != 0;
-        // 1. rows 0..31 (with their RoPE chunks) of tile kt have landed:
-        //    only the copies issued after that RoPE group may still be in
-        //    flight.  Every wave is done with P*V 0 of tile kt-1 (P^T half 0
-        //    and its maxima are free); softmax 1 of tile kt-1 is published.
-        MLA_WAIT_VMCNT(TileCopy<0>::kLateCopies);
+      // Dense bf16 tiles run one P*V half behind the scores.  The score
+      // chains are bound by their K operand reads from LDS (one 1 KiB read
+      // per MFMA and wave); the P*V halves are fed from registers and two
+      // LDS reads per MFMA.  The softmax of a half is spread over both
+      // kinds of phase: its first steps (mask, maxima, the first
+      // exponentials) run between the MFMAs of the P*V half that follows
+      // the half's scores, the rest between the MFMAs of the next score
+      // chain, which publishes the half's P^T with a barrier of its own and
+      // then reads the first operands of the P*V half after it.  Tile kt:
+      //   B1 | A: scores 0 of kt; softmax 1 of kt-1, second part (P^T into
+      //      |    the RoPE region of kt-1's buffer) | barrier |     (copies)
+      //      | B: P*V 1 of kt-1; softmax 0 of kt, first part       (copies)
+      //   B2 | C: scores 1 of kt; softmax 0 of kt, second part (P^T into
+      //      |    pbuf) | barrier |                                (copies)
+      //      | D: P*V 0 of kt; softmax 1 of kt, first part         (copies)
+      // B1 waits for rows 0..31 and the RoPE region of tile kt and frees
+      // rows 0..31 of the other buffer (P*V 0 of kt-1 is done) and pbuf;
+      // B2 waits for rows 32..63 of tile kt and frees rows 32..63 and the
+      // RoPE region of the other buffer (P*V 1 of kt-1 is done).
+      if constexpr (kPipelined) {
+        const __attribute__((address_space(4))) int32_t* bt_const =
+            (const __attribute__((address_space(4))) int32_t*)bt_row;  // scalar loads
+        bf16x8 vf[kVRegs];
+        bf16x8 pfr[4];
+        // Softmax 1 of the tile before, carried into the next tile's first
+        // chain.  The first tile of a segment has none: scores of -inf and a
+        // cleared state make its second part add nothing.
+        f32x16 sacc1;
+        HalfSoftmax hs1;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc1[i] = -INFINITY;
+        hs1.tmax = -INFINITY;
+        hs1.nmuse = 0.0f;
+        hs1.lh = 0.0f;
+        hs1.x = -INFINITY;
+        hs1.e[0] = hs1.e[1] = 0.0f;
+        hs1.pw[0] = hs1.pw[1] = u32x4{0u, 0u, 0u, 0u};
+        int jl_prev = 63;
+        // K operand of step st of the chain over rows 32*kb2 .. +31 of buffer kb
+        auto k_dense = [&](const uint8_t* kb, int kb2, int st) {
+          return *reinterpret_cast<const bf16x8*>(
+              kb + (st < 32 ? kbase + 33280 * kb2 + 32 * st : rope_off[st - 32] + 4096 * kb2));
+        };
+        // 36 score MFMAs of half kb2 with hook(st) after MFMA st; K operands
+        // are read kKPrefetch steps ahead
+        auto chain = [&](f32x16& acc, const uint8_t* kb, int kb2, auto&& hook) __attribute__((always_inline)) {
+          bf16x8 kf[kKPrefetch];
+#pragma unroll
+          for (int st = 0; st < kKPrefetch; ++st) kf[st] = k_dense(kb, kb2, st);
+          static_for<0, kQSteps>([&](auto st_c) __attribute__((always_inline)) {
+            constexpr int st = decltype(st_c)::value;
+            const bf16x8 cur_k = kf[st % kKPrefetch];
+            if constexpr (st + kKPrefetch < kQSteps) kf[st % kKPrefetch] = k_dense(kb, kb2, st + kKPrefetch);
+            if constexpr (st == 0)
+              mfma_s_first(acc, cur_k, qf[st]);
+            else
+              mfma_s_acc(acc, cur_k, qf[st]);
+            hook(st_c);
+            __builtin_amdgcn_sched_barrier(0);
+          });
+          mfma_s_drain(acc);
+        };
+        // Softmax steps 0 .. kSplit-1 go after P*V MFMAs 3, 5, .., steps
+        // kSplit .. 24 after score MFMAs 1, 2, ..; the P^T stores (steps 23,
+        // 24, after MFMAs 11 and 12) precede the chain's barrier (after MFMA
+        // 16) by exactly four LDS reads, the K operands of steps 17 to 20.
+        constexpr int kSplit = 13;
+        constexpr int kChainBarrierStep = kSoftmaxSteps - kSplit + 4;  // 16
+        constexpr int kReadsAfterStores = 4;
+        auto in_pv = [](int j) { return j >= 3 && (j & 1) == 1 && (j - 3) / 2 < kSplit; };
+        for (int kt = kfirst; kt < kend; ++kt) {
+          const bool odd = ((kt - kfirst) & 1) != 0;
+          // B1
+          MLA_WAIT_VMCNT(kDenseB1InFlight);
+          MLA_BARRIER_NO_FENCE();
+          ks = odd ? lds1 : lds0;
+          uint8_t* const kprev = odd ? lds0 : lds1;
+          DenseCopy next;
+          next.prepare(a.kv, pg_next, kt + 1, kt + 1 < kend ? L : 0, lds_addr(kprev));
+          const int jl = min(63, tlim - kt * kPage);
+
+          HalfSoftmax hs0;
+          f32x16 sacc0;
+          // A.
+          chain(sacc0, ks, 0, [&](auto st_c) __attribute__((always_inline)) {
+            constexpr int st = decltype(st_c)::value;
+            if constexpr (st >= 1 && st <= kSoftmaxSteps - kSplit)
+              softmax_step(1, sacc1, hs1, kSplit + st - 1, jl_prev, kprev + kDenseRope);
+            if constexpr (st == kChainBarrierStep) MLA_BARRIER_NO_FENCE_KEEP(kReadsAfterStores);
+            if constexpr (st == kChainBarrierStep + 1 || st == kChainBarrierStep + 2)
+              vf[st - kChainBarrierStep - 1] = load_v(kprev, 1, st - kChainBarrierStep - 1);
+            if constexpr (st == kChainBarrierStep + 3 || st == kChainBarrierStep + 4) {
+              constexpr int r0 = 2 * (st - kChainBarrierStep - 3);
+              lds_u8* pl = p_lane(kprev + kDenseRope, 0);
+              pfr[r0] = load_p(pl, r0);
+              pfr[r0 + 1] = load_p(pl, r0 + 1);
+            }
+          });
+          // B. (the first tile of a segment has no P*V 1 of a previous tile)
+          if (kt > kfirst) {
+            pv_run(1, kprev, kprev + kDenseRope, vf, pfr, [&](auto j_c) __attribute__((always_inline)) {
+              constexpr int j = decltype(j_c)::value;
+              if constexpr (j % 4 == 2) next.template issue<j / 4>();  // copies 0..7
+              if constexpr (in_pv(j)) softmax_step(0, sacc0, hs0, (j - 3) / 2, jl, pbuf);
+            });
+          } else {
+            static_for<0, 8>([&](auto i_c) __attribute__((always_inline)) {
+              next.template issue<decltype(i_c)::value>();
+            });
+            static_for<0, kSplit>([&](auto u_c) __attribute__((always_inline)) {
+              softmax_step(0, sacc0, hs0, decltype(u_c)::value, jl, pbuf);
+            });
+          }
+          // B2
+          MLA_WAIT_VMCNT(kDenseB2InFlight);
+          MLA_BARRIER_NO_FENCE();
+          // C.
+          chain(sacc1, ks, 1, [&](auto st_c) __attribute__((always_inline)) {
+            constexpr int st = decltype(st_c)::value;
+            if constexpr (st >= 1 && st <= kSoftmaxSteps - kSplit)
+              softmax_step(0, sacc0, hs0, kSplit + st - 1, jl, pbuf);
+            if constexpr (st == kChainBarrierStep) MLA_BARRIER_NO_FENCE_KEEP(kReadsAfterStores);
+            if constexpr (st == kChainBarrierStep + 1 || st == kChainBarrierStep + 2)
+              vf[st - kChainBarrierStep - 1] = load_v(ks, 0, st - kChainBarrierStep - 1);
+            if constexpr (st == kChainBarrierStep + 3 || st == kChainBarrierStep + 4) {
+              constexpr int r0 = 2 * (st - kChainBarrierStep - 3);
+              lds_u8* pl = p_lane(pbuf, 0);
+              pfr[r0] = load_p(pl, r0);
+              pfr[r0 + 1] = load_p(pl, r0 + 1);
+            }
+          });
+          // D.
+          pv_run(0, ks, pbuf, vf, pfr, [&](auto j_c) __attribute__((always_inline)) {
+            constexpr int j = decltype(j_c)::value;
+            // the RoPE copies first (needed at the end of the next tile's first chain)
+            if constexpr (j == 0 || j == 1) next.template issue<16 + j>();
+            if constexpr (j % 3 == 2 && j / 3 < 8) next.template issue<8 + j / 3>();  // copies 8..15
+            if constexpr (in_pv(j)) softmax_step(1, sacc1, hs1, (j - 3) / 2, jl, ks + kDenseRope);
+          });
+          jl_prev = jl;
+          // the page of tile kt+2, for the next tile's copies (a scalar load,
+          // waited for by the barrier that starts the next tile)
+          pg_next = bt_const[min(kt + 2, nb - 1)];
+        }
+        // Second part of softmax 1 and P*V 1 of the last tile.  Its P^T goes
+        // into the RoPE region of the tile, which other waves may still read
+        // at the end of their second score chain: a barrier first.
         MLA_BARRIER_NO_FENCE();
-        ks = odd ? lds1 : lds0;
-        const uint8_t* kprev = odd ? lds0 : lds1;
-        // the chain's first K reads go out before the copy address arithmetic
-        KOperands kp;
-        score_chain_begin(kp, ks, k_off);
-        __builtin_amdgcn_sched_barrier(0);
-        const u32x4 g1 = grew_word(1);  // softmax 1 of tile kt-1 (published by B1)
-        __builtin_amdgcn_sched_barrier(0);
-        TileCopy<0> next;
-        const uint32_t next_buf = lds_addr(odd ? lds0 : lds1);
-        next.prepare_page(a.kv, pg_next, kt + 1, kt + 1 < kend ? L : 0, next_buf, wave, lane);
-        pg_next = bt_const[min(kt + 2, nb - 1)];  // for the next tile
-        jlim = min(63, tlim - kt * kPage);
-        const bool grew1 = grew_any(g1);
+        static_for<kSplit, kSoftmaxSteps>([&](auto u_c) __attribute__((always_inline)) {
+          softmax_step(1, sacc1, hs1, decltype(u_c)::value, jl_prev, ks + kDenseRope);
+        });
+        pv_prefetch(ks, 1, vf);
+        MLA_BARRIER_NO_FENCE_KEEP(kVPrefetchReads);
+        pv_half(1, ks, ks + kDenseRope, vf, [] {}, [](auto) {});
+      }
+
+      // One tile: the copy of tile kt+1 and the row resolution of kt+2/kt+3
+      // are issued, then tile kt is computed.  bf16 tiles alternate between
+      // the two buffers, starting with lds0.
+      for (int kt = kfirst; kt < kend && !kPipelined; ++kt) {
+        const bool odd = ((kt - kfirst) & 1) != 0;
+        // 1. tile kt has landed (this thread's copies, then everyone's); every
+        //    wave is done with tile kt-1, its buffer and both P^T halves
+        if constexpr (FMT == 0) MLA_WAIT_VMCNT(kResolveLoads);
+        MLA_BARRIER_NO_FENCE();
+        vm = vm_cur;
+        // Sparse: address of tile kt+2's page-table entry.  res_t was loaded
+        // during the previous tile; using it here, where only that tile's two
+        // resolve loads can still be in flight, keeps the wait the compiler
+        // places for it from also waiting for this tile's copies.  (Dense
+        // positions are arithmetic: no wait, no early address needed.)
+        int pg_idx = 0;
+        if constexpr (SPARSE) {
+          pg_idx = visible(res_t) ? (res_t >> 6) : 0;
+          asm volatile("" : "+v"(pg_idx));
+        }
+        // 2. sources of tile kt+1's copy; the copies themselves are issued
+        //    between the MFMAs of the first score chain (res_off is -1 for
+        //    every key past the unit's last tile)
+        TileCopy<FMT> next;
+        const uint32_t next_buf = lds_addr(FMT == 1 ? lds1 : (odd ? lds0 : lds1));
+        if constexpr (SPARSE) {
+          next.prepare(a.kv, res_off, next_buf, wave, lane);
+          vm_cur = __ballot(res_off >= 0);
+        } else {
+          // tile kt+1 past the segment: zero rows
+          next.prepare_page(a.kv, pg_next, kt + 1, kt + 1 < kend ? L : 0, next_buf, wave, lane);
+          pg_next = bt_row[min(kt + 2, nb - 1)];  // for the next tile; a scalar load
+        }
+
+        ks = (FMT == 0 && odd) ? lds1 : lds0;
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) lanemask[kb2] = SPARSE ? (uint32_t)(vm >> (kb2 * 32 + 4 * h)) : 0u;
+        jlim = SPARSE ? 63 : min(63, tlim - kt * kPage);
 
         HalfSoftmax hs0, hs1;
         f32x16 sacc0, sacc1;
-        bf16x8 pfr[4];
-        // P*V 1 of tile kt-1 reads operands published at B1: its first reads
-        // go out during the last MFMAs of the chain (for the first tile of
-        // a segment they read the idle buffer and are not used)
-        score_chain_run(sacc0, kp, ks, k_off, qf, [&](auto st_c) __attribute__((always_inline)) {
+        // 3. scores of half 0; scores of half 1 with the softmax of half 0
+        // Issued unconditionally: after a unit's last tile every key of "tile
+        // kt+1" resolves to the zero row, so the copies fill the free buffer
+        // with zeros, which nothing reads; the next unit starts with a barrier
+        // that waits for them.  No branch keeps the chain's registers simple.
+        // FP8: rows 32..63 of tile kt are dequantised from the stage between
+        // the MFMAs of the first chain, which reads rows 0..31 only (they were
+        // dequantised during the previous tile's second P*V half)
+        HalfDequant dqh;
+        score_chain(sacc0, ks, k_off, qf, [&](auto st_c) __attribute__((always_inline)) {
           constexpr int st = decltype(st_c)::value;
-          next.template issue_split<0, st>(lane);
-          if constexpr (st == kQSteps - 3) pv_begin(kprev, 1, kprev + kRopeOffset, vf, pfr);
+          next.template issue_at<0, st>(lane);
+          if constexpr (FMT == 1) {
+            if constexpr (st == 0) dqh.load(lds1, 32);
+            if constexpr (st >= 1 && st <= 32) dqh.template convert<st - 1>(ks);
+            if constexpr (st == 20) dqh.load_rope();
+            if constexpr (st == 34) dqh.store_rope(ks);
+          }
         });
-        if (kt > kfirst) {
-          pv_run(1, kprev, kprev + kRopeOffset, vf, pfr, [&] { settle(1, prev_mo, prev_lh, grew1); },
-                 [&](auto j_c) __attribute__((always_inline)) {
-                   constexpr int j = decltype(j_c)::value;
-                   if constexpr (j < kSoftmaxSteps) softmax_step(0, sacc0, hs0, j);
-                 });
-        } else {
-          static_for<0, kSoftmaxSteps>([&](auto u_c) __attribute__((always_inline)) {
-            softmax_step(0, sacc0, hs0, decltype(u_c)::value);
-          });
-        }
-        // 2. half 0's P^T and maxima visible; the other buffer (tile kt-1)
-        //    is free; rows 32..63 of tile kt have landed (only the copies
-        //    issued during scores 0 may still be in flight)
-        MLA_WAIT_VMCNT(TileCopy<0>::kEarlyCopies);
-        MLA_BARRIER_NO_FENCE();
-        const u32x4 g0 = grew_word(0);  // softmax 0 of tile kt (published by B2)
-        __builtin_amdgcn_sched_barrier(0);
-        bool grew0 = false;
+        // FP8: rows 32..63 of tile kt are in place; the stage rows they came
+        // from are free for the next tile's copies
+        if constexpr (FMT == 1) MLA_BARRIER_NO_FENCE();
         score_chain(sacc1, ks + 32 * 128, k_off, qf, [&](auto st_c) __attribute__((always_inline)) {
           constexpr int st = decltype(st_c)::value;
-          next.template issue_split<1, st>(lane);
-          if constexpr (st == 6) grew0 = grew_any(g0);
+          next.template issue_at<1, st>(lane);
+          if constexpr (st < kSoftmaxSteps) softmax_step(0, sacc0, hs0, st, jlim, pbuf);
         });
-        // 3. every wave is past the scores of tile kt: its RoPE chunk group
-        //    takes half 1's P^T.  (Half 0's P^T is visible since B2, so
-        //    all first operands are read before this barrier.)
-        pv_begin(ks, 0, pbuf, vf, pfr);
-        MLA_BARRIER_NO_FENCE_KEEP(kPVBeginReads);
-        pv_run(0, ks, pbuf, vf, pfr, [&] { settle(0, hs0.mo, hs0.lh, grew0); },
-                [&](auto j_c) __attribute__((always_inline)) {
-                  constexpr int j = decltype(j_c)::value;
-                  if constexpr (j < kSoftmaxSteps) softmax_step(1, sacc1, hs1, j);
-                });
-        prev_mo = hs1.mo;
-        prev_lh = hs1.lh;
-      }
-      // P*V 1 of the last tile
-      pv_prefetch(ks, 1, vf);
-      MLA_BARRIER_NO_FENCE_KEEP(kVPrefetchReads);
-      pv_half(1, ks, ks + kRopeOffset, vf, [&] { settle(1, prev_mo, prev_lh, grew_any(grew_word(1))); }, [](auto) {});
-    }
 
-    // One tile: the copy of tile kt+1 and the row resolution of kt+2/kt+3
-    // are issued, then tile kt is computed.  bf16 tiles alternate between
-    // the two buffers, starting with lds0.
-    for (int kt = kfirst; kt < kend && !kPipelined; ++kt) {
-      const bool odd = ((kt - kfirst) & 1) != 0;
-      // 1. tile kt has landed (this thread's copies, then everyone's); every
-      //    wave is done with tile kt-1, its buffer and both P^T halves
-      if constexpr (FMT == 0) MLA_WAIT_VMCNT(kResolveLoads);
-      MLA_BARRIER_NO_FENCE();
-      vm = vm_cur;
-      // Sparse: address of tile kt+2's page-table entry.  res_t was loaded
-      // during the previous tile; using it here, where only that tile's two
-      // resolve loads can still be in flight, keeps the wait the compiler
-      // places for it from also waiting for this tile's copies.  (Dense
-      // positions are arithmetic: no wait, no early address needed.)
-      int pg_idx = 0;
-      if constexpr (SPARSE) {
-        pg_idx = visible(res_t) ? (res_t >> 6) : 0;
-        asm volatile("" : "+v"(pg_idx));
-      }
-      // 2. sources of tile kt+1's copy; the copies themselves are issued
-      //    between the MFMAs of the first score chain (res_off is -1 for
-      //    every key past the unit's last tile)
-      TileCopy<FMT> next;
-      const uint32_t next_buf = lds_addr(FMT == 1 ? lds1 : (odd ? lds0 : lds1));
-      if constexpr (SPARSE) {
-        next.prepare(a.kv, res_off, next_buf, wave, lane);
-        vm_cur = __ballot(res_off >= 0);
-      } else {
-        // tile kt+1 past the segment: zero rows
-        next.prepare_page(a.kv, pg_next, kt + 1, kt + 1 < kend ? L : 0, next_buf, wave, lane);
-        pg_next = bt_row[min(kt + 2, nb - 1)];  // for the next tile; a scalar load
-      }
-
-      ks = (FMT == 0 && odd) ? lds1 : lds0;
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) lanemask[kb2] = SPARSE ? (uint32_t)(vm >> (kb2 * 32 + 4 * h)) : 0u;
-      jlim = SPARSE ? 63 : min(63, tlim - kt * kPage);
-
-      HalfSoftmax hs0, hs1;
-      f32x16 sacc0, sacc1;
-      // 3. scores of half 0; scores of half 1 with the softmax of half 0
-      // Issued unconditionally: after a unit's last tile every key of "tile
-      // kt+1" resolves to the zero row, so the copies fill the free buffer
-      // with zeros, which nothing reads; the next unit starts with a barrier
-      // that waits for them.  No branch keeps the chain's registers simple.
-      // FP8: rows 32..63 of tile kt are dequantised from the stage between
-      // the MFMAs of the first chain, which reads rows 0..31 only (they were
-      // dequantised during the previous tile's second P*V half)
-      HalfDequant dqh;
-      score_chain(sacc0, ks, k_off, qf, [&](auto st_c) __attribute__((always_inline)) {
-        constexpr int st = decltype(st_c)::value;
-        next.template issue_at<0, st>(lane);
-        if constexpr (FMT == 1) {
-          if constexpr (st == 0) dqh.load(lds1, 32);
-          if constexpr (st >= 1 && st <= 32) dqh.template convert<st - 1>(ks);
-          if constexpr (st == 20) dqh.load_rope();
-          if constexpr (st == 34) dqh.store_rope(ks);
+        // 4. half 0's P^T visible
+        bf16x8 vf[kVRegs];
+        pv_prefetch(ks, 0, vf);
+        MLA_BARRIER_NO_FENCE_KEEP(kVPrefetchReads);
+        pv_half(0, ks, pbuf, vf, [] {}, [&](auto j_c) __attribute__((always_inline)) {
+          constexpr int j = decltype(j_c)::value;
+          next.template issue_at<2, j>(lane);
+          if constexpr (j < kSoftmaxSteps) softmax_step(1, sacc1, hs1, j, jlim, pbuf1);
+        });
+        // resolve kt+2 (page lookup) and kt+3 after the last copy: the wait at
+        // the top of the next tile counts these loads as the only ones newer
+        // than the copies
+        asm volatile("" ::: "memory");
+        if constexpr (SPARSE) {
+          pg2 = bt_row[pg_idx];
+          // The raw index of tile kt+3.  Its only reader until the end of the
+          // tile is an empty asm statement there, so the compiler's wait for
+          // it lands at the end of the tile; a select next to the load would
+          // be waited for here, and with it every copy issued before it.
+          // Validity is applied at the end of the tile.
+          const int k = (kt + 3) * kPage + lane;
+          t3 = idx_row[k < s.topk ? k : s.topk - 1];
+          t3_ok = kt + 3 < kend && k < s.topk;
         }
-      });
-      // FP8: rows 32..63 of tile kt are in place; the stage rows they came
-      // from are free for the next tile's copies
-      if constexpr (FMT == 1) MLA_BARRIER_NO_FENCE();
-      score_chain(sacc1, ks + 32 * 128, k_off, qf, [&](auto st_c) __attribute__((always_inline)) {
-        constexpr int st = decltype(st_c)::value;
-        next.template issue_at<1, st>(lane);
-        if constexpr (st < kSoftmaxSteps) softmax_step(0, sacc0, hs0, st);
-      });
+        asm volatile("" ::: "memory");
+        // FP8: this thread's copies of tile kt+1 are complete (only the
+        // resolve loads may be newer), so after the barrier every staged row
+        // is visible to the dequantisation below
+        if constexpr (FMT == 1) MLA_WAIT_VMCNT(kResolveLoads);
+        pv_prefetch(ks, 1, vf);
+        MLA_BARRIER_NO_FENCE_KEEP(kVPrefetchReads);  // half 1's P^T visible
+        if constexpr (FMT == 0) {
+          pv_half(1, ks, pbuf1, vf, [] {}, [](auto) {});
+        } else {
+          // rows 0..31 of tile kt are no longer read (half 0 is done): the
+          // staged rows 0..31 of tile kt+1 are dequantised into them between
+          // the MFMAs of half 1 (after a unit's last tile they are zero rows
+          // written into a tile nothing reads any more)
+          HalfDequant dq;
+          pv_half(1, ks, pbuf1, vf, [&] { dq.load(lds1, 0); },
+                  [&](auto j_c) __attribute__((always_inline)) {
+                    dq.template convert<decltype(j_c)::value>(ks);
+                    if constexpr (decltype(j_c)::value == 24) dq.load_rope();
+                    if constexpr (decltype(j_c)::value == 31) dq.store_rope(ks);
+                  });
+        }
 
-      // 4. half 0's P^T and maxima visible; every wave is past the scores,
-      //    so the RoPE chunk group is free for half 1's P^T
-      bf16x8 vf[kVRegs];
-      pv_prefetch(ks, 0, vf);
-      MLA_BARRIER_NO_FENCE_KEEP(kVPrefetchReads);
-      pv_half(0, ks, pbuf, vf, [&] { settle(0, hs0.mo, hs0.lh, grew_any(grew_word(0))); }, [&](auto j_c) __attribute__((always_inline)) {
-        constexpr int j = decltype(j_c)::value;
-        next.template issue_at<2, j>(lane);
-        if constexpr (j < kSoftmaxSteps) softmax_step(1, sacc1, hs1, j);
-      });
-      // resolve kt+2 (page lookup) and kt+3 after the last copy: the wait at
-      // the top of the next tile counts these loads as the only ones newer
-      // than the copies
-      asm volatile("" ::: "memory");
-      if constexpr (SPARSE) {
-        pg2 = bt_row[pg_idx];
-        // The raw index of tile kt+3.  Its only reader until the end of the
-        // tile is an empty asm statement there, so the compiler's wait for
-        // it lands at the end of the tile; a select next to the load would
-        // be waited for here, and with it every copy issued before it.
-        // Validity is applied at the end of the tile.
-        const int k = (kt + 3) * kPage + lane;
-        t3 = idx_row[k < s.topk ? k : s.topk - 1];
-        t3_ok = kt + 3 < kend && k < s.topk;
-      }
-      asm volatile("" ::: "memory");
-      // FP8: this thread's copies of tile kt+1 are complete (only the
-      // resolve loads may be newer), so after the barrier every staged row
-      // is visible to the dequantisation below
-      if constexpr (FMT == 1) MLA_WAIT_VMCNT(kResolveLoads);
-      pv_prefetch(ks, 1, vf);
-      MLA_BARRIER_NO_FENCE_KEEP(kVPrefetchReads);  // half 1's P^T and maxima visible
-      if constexpr (FMT == 0) {
-        pv_half(1, ks, ks + kRopeOffset, vf, [&] { settle(1, hs1.mo, hs1.lh, grew_any(grew_word(1))); }, [](auto) {});
-      } else {
-        // rows 0..31 of tile kt are no longer read (half 0 is done): the
-        // staged rows 0..31 of tile kt+1 are dequantised into them between
-        // the MFMAs of half 1 (after a unit's last tile they are zero rows
-        // written into a tile nothing reads any more)
-        HalfDequant dq;
-        pv_half(1, ks, pbuf1, vf, [&] { dq.load(lds1, 0); settle(1, hs1.mo, hs1.lh, grew_any(grew_word(1))); },
-                [&](auto j_c) __attribute__((always_inline)) {
-                  dq.template convert<decltype(j_c)::value>(ks);
-                  if constexpr (decltype(j_c)::value == 24) dq.load_rope();
-                  if constexpr (decltype(j_c)::value == 31) dq.store_rope(ks);
-                });
+        // 5. finish resolving tile kt+2
+        if constexpr (SPARSE) {
+          res_off = offset_of(res_t, pg2);
+          asm volatile("" : "+v"(t3));
+          res_t = t3_ok ? t3 : -1;
+        }
       }
 
-      // 5. finish resolving tile kt+2
-      if constexpr (SPARSE) {
-        res_off = offset_of(res_t, pg2);
-        asm volatile("" : "+v"(t3));
-        res_t = t3_ok ? t3 : -1;
+      // Restart test: a row whose scores climbed more than kRestartMargin
+      // above its reference sends the whole workgroup through the segment
+      // again, against the exact row maxima this pass found.  Every wave
+      // publishes its vote after its last P*V (pbuf is free: the last reads
+      // of it were before the final barrier), then reads all four.
+      uint32_t* votes = reinterpret_cast<uint32_t*>(pbuf + 4096);
+      if (pass == 0) {
+        const bool over = __ballot(rmax > m + kRestartMargin) != 0;
+        if (lane == 0) votes[wave] = over ? 1u : 0u;
       }
+      MLA_BARRIER_NO_FENCE();
+      if (pass == 0) {
+        const u32x4 vw = *reinterpret_cast<const u32x4*>(votes);
+        if (__builtin_amdgcn_readfirstlane(vw[0] | vw[1] | vw[2] | vw[3]) != 0) {
+          mref_slot[threadIdx.x] = rmax;
+          MLA_BARRIER_NO_FENCE();  // every wave has read the votes
+          continue;
+        }
+      }
+      break;
     }
 
-    // ---- epilogue.  The score-row owner folds in its flush record and
-    // publishes the row's output factors; every wave then normalises and
-    // stores its column blocks.
-    float fa = 0.0f, fc = 1.0f, mfin = m, lfin = l;
-    float* rec = flush_rec();
-    if (flushed) {
-      const float mf = rec[261];
-      mfin = fmaxf(mf, m);
-      fa = merge_factor(mf, mfin);
-      fc = merge_factor(m, mfin);
-      lfin = rec[260] * fa + l * fc;
-    }
-    const float ltot = wave_sum_pair(lfin);
-    const float lse2 = ltot > 0.0f ? mfin + log2f(ltot) : -INFINITY;
+    // ---- epilogue.  The score-row owner publishes the row's output factor;
+    // every wave then normalises and stores its column blocks.
+    const float ltot = wave_sum_pair(l);
+    const float lse2 = ltot > 0.0f ? m + log2f(ltot) : -INFINITY;
     const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
     // half 0's P^T buffer is free: every wave is past the last tile's final barrier
-    f32x2* epi = reinterpret_cast<f32x2*>(pbuf);
-    if (h == 0) epi[rs] = f32x2{fc * inv, fa * inv};
+    float* epi = reinterpret_cast<float*>(pbuf);
+    if (h == 0) epi[rs] = inv;
     MLA_BARRIER_NO_FENCE();
     const bool direct = nsplit == 1;
     // Output rows and columns come from the thread index again rather than
@@ -1182,59 +1262,46 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
     // c ^ (r % 16), which spreads both the slice writes and the row reads
     // over all banks.
     uint16_t* const obase = direct ? a.out : a.ws_o;  // final rows or bf16 split partials
-    auto store_rows = [&](auto flushed_c) __attribute__((always_inline)) {
-      constexpr bool kFlushed = decltype(flushed_c)::value;
-      const float* recp = flush_rec();
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        uint8_t* const stg = ks + 32768 * (rb & 1);
-        {
-          const f32x2 f = epi[32 * rb + on];
-          f32x4 fr[16];  // the row block's parked values, loaded before use
-          if constexpr (kFlushed) {
+    for (int rb = 0; rb < 4; ++rb) {
+      uint8_t* const stg = ks + 32768 * (rb & 1);
+      {
+        const float f = epi[32 * rb + on];
 #pragma unroll
-            for (int k = 0; k < 16; ++k)
-              fr[k] = *reinterpret_cast<const f32x4*>(recp + (4 * (k >> 2) + rb) * 16 + 4 * (k & 3));
-          }
+        for (int cb = 0; cb < 4; ++cb) {
 #pragma unroll
-          for (int cb = 0; cb < 4; ++cb) {
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-              f32x4 v = f32x4{o[cb][rb][4 * q4], o[cb][rb][4 * q4 + 1], o[cb][rb][4 * q4 + 2],
-                              o[cb][rb][4 * q4 + 3]} * f[0];
-              if constexpr (kFlushed) v += fr[4 * cb + q4] * f[1];
-              const uint32_t w0 = pk_bf16(v[0], v[1]);
-              const uint32_t w1 = pk_bf16(v[2], v[3]);
-              const int chunk = (16 * ow + 4 * cb + q4) ^ (on & 15);  // columns 128ow + 32cb + 8q4 ..
-              *reinterpret_cast<uint2*>(stg + on * 1024 + chunk * 16 + 8 * oh) = make_uint2(w0, w1);
-            }
-          }
-        }
-        MLA_BARRIER_NO_FENCE();  // the block is staged; the other area is free again
-        const int ln = tid & 63;
-        const int ows = __builtin_amdgcn_readfirstlane(ow);  // wave-uniform row tests below
-        const int ro8 = grp * kRowsPerGroup + 32 * rb + 8 * ows;  // first output row in the unit
-        auto row_chunk = [&](int i) {
-          const int rr = 8 * ows + i;  // row in the block
-          return *reinterpret_cast<const uint4*>(stg + rr * 1024 + ((ln ^ (rr & 15)) * 16));
-        };
-        if (ro8 + 8 <= s.rows) {  // all 8 rows exist: every read before any store
-          uint4 rowv[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) rowv[i] = row_chunk(i);
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-            *reinterpret_cast<uint4*>(obase + (orow0 + ro8 + i) * kDv + 8 * ln) = rowv[i];
-        } else {
-          for (int i = 0; i < 8 && ro8 + i < s.rows; ++i) {
-            const uint4 v = row_chunk(i);
-            *reinterpret_cast<uint4*>(obase + (orow0 + ro8 + i) * kDv + 8 * ln) = v;
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4 v = f32x4{o[cb][rb][4 * q4], o[cb][rb][4 * q4 + 1], o[cb][rb][4 * q4 + 2],
+                                  o[cb][rb][4 * q4 + 3]} * f;
+            const uint32_t w0 = pk_bf16(v[0], v[1]);
+            const uint32_t w1 = pk_bf16(v[2], v[3]);
+            const int chunk = (16 * ow + 4 * cb + q4) ^ (on & 15);  // columns 128ow + 32cb + 8q4 ..
+            *reinterpret_cast<uint2*>(stg + on * 1024 + chunk * 16 + 8 * oh) = make_uint2(w0, w1);
           }
         }
       }
-    };
-    if (flushed) store_rows(std::integral_constant<bool, true>{});
-    else store_rows(std::integral_constant<bool, false>{});
+      MLA_BARRIER_NO_FENCE();  // the block is staged; the other area is free again
+      const int ln = tid & 63;
+      const int ows = __builtin_amdgcn_readfirstlane(ow);  // wave-uniform row tests below
+      const int ro8 = grp * kRowsPerGroup + 32 * rb + 8 * ows;  // first output row in the unit
+      auto row_chunk = [&](int i) {
+        const int rr = 8 * ows + i;  // row in the block
+        return *reinterpret_cast<const uint4*>(stg + rr * 1024 + ((ln ^ (rr & 15)) * 16));
+      };
+      if (ro8 + 8 <= s.rows) {  // all 8 rows exist: every read before any store
+        uint4 rowv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) rowv[i] = row_chunk(i);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          *reinterpret_cast<uint4*>(obase + (orow0 + ro8 + i) * kDv + 8 * ln) = rowv[i];
+      } else {
+        for (int i = 0; i < 8 && ro8 + i < s.rows; ++i) {
+          const uint4 v = row_chunk(i);
+          *reinterpret_cast<uint4*>(obase + (orow0 + ro8 + i) * kDv + 8 * ln) = v;
+        }
+      }
+    }
     if (row_ok && h == 0) {
       const int64_t row = (int64_t)u * s.rows + r;
       if (direct)

@@ -42,16 +42,12 @@ struct DecodeArgs {
   int32_t num_parts;
   float* ws_lse;  // [slots * R]
   uint16_t* ws_o;  // [slots * R * 512] bf16, normalised split outputs
-  float* ws_flush;  // [num_parts * groups * 256 threads * kFlushFloats]
   uint16_t* out;
   float* lse;
 };
 
-// Workspace layout: split lse block (fp32), split output block (bf16; both
-// for num_parts + U slots of R rows), then one flush record per decode thread
-// (num_parts * groups workgroups of 256 threads, kFlushFloats floats each:
-// 256 output values, 4 row maxima, a row sum and its maximum, padding).
-constexpr int kFlushFloats = 264;
+// Workspace layout: split lse block (fp32), then split output block (bf16);
+// both for num_parts + U slots of R rows, each block 256-byte aligned.
 inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 inline size_t ws_slots(int32_t num_parts, int32_t units) { return (size_t)num_parts + (size_t)units; }
 inline size_t ws_lse_bytes(size_t slots, int32_t rows) {
@@ -60,12 +56,9 @@ inline size_t ws_lse_bytes(size_t slots, int32_t rows) {
 inline size_t ws_o_bytes(size_t slots, int32_t rows) {
   return align256(slots * (size_t)rows * kDv * sizeof(uint16_t));
 }
-inline size_t ws_flush_bytes(int32_t num_parts, int32_t groups) {
-  return (size_t)num_parts * (size_t)groups * 256 * kFlushFloats * sizeof(float);
-}
-inline size_t ws_total_bytes(int32_t num_parts, int32_t units, int32_t rows, int32_t groups) {
-  size_t slots = ws_slots(num_parts, units);
-  return ws_lse_bytes(slots, rows) + ws_o_bytes(slots, rows) + ws_flush_bytes(num_parts, groups);
+inline size_t ws_total_bytes(int32_t num_parts, int32_t units, int32_t rows) {
+  const size_t slots = ws_slots(num_parts, units);
+  return ws_lse_bytes(slots, rows) + ws_o_bytes(slots, rows);
 }
 
 hipError_t launch_metadata(const Shape& s, const int32_t* seqlens, int32_t num_parts,
