@@ -214,25 +214,34 @@ def test_metadata_matches_cpu_reference(n):
     assert np.array_equal(splits, np.array(ref_splits, dtype=np.int32))
 
 
-def test_flush_path_growing_scores():
-    """Scores that climb by far more than the lazy-rescale threshold across
-    tiles force the flush path; results must still match the oracle."""
+@pytest.mark.parametrize("kv_format,topk", [(synth.KV_BF16, 0), (synth.KV_FP8_656, 0),
+                                            (synth.KV_BF16, 200), (synth.KV_FP8_656, 200)])
+def test_restart_pass_growing_scores(kv_format, topk):
+    """Scores that climb by far more than the restart margin along the
+    sequence (~370 in log2 units) send the main kernel's workgroups through a
+    second pass against the exact row maxima, on every instance (bf16 and FP8,
+    dense and sparse); results must still match the oracle."""
     L = 640
-    w = synth.make_workload("t", batch=2, h_q=128, s_q=1, seqlens=[L, 300], seed=42, slack=0)
+    w = synth.make_workload("t", batch=2, h_q=128, s_q=1, seqlens=[L, 300], seed=42, slack=0,
+                            kv_format=kv_format, topk=topk)
     kv = w.kv.copy()
     for b in range(2):
         for t in range(int(w.cache_seqlens[b])):
             page, slot = w.block_table[b, t // 64], t % 64
             x = np.full(576, 0.05 * t, dtype=np.float32)  # scores grow ~ linearly in t
             x[:512] += np.float32(np.sin(t))
-            kv[page, slot] = synth.bf16_bits_from_f32(x).view(np.uint8)
+            bits = synth.bf16_bits_from_f32(x)
+            kv[page, slot] = (bits.view(np.uint8) if kv_format == synth.KV_BF16
+                              else synth.encode_fp8_rows(bits[None])[0])
     w.kv = kv
+    if topk:
+        w.indices = np.sort(w.indices, axis=-1)  # ascending positions: the scores climb tile by tile
     q = np.full(w.q.shape, 0x3F80, dtype=np.uint16)  # all-ones queries
     w.q = q
     for parts in (None, 3):
         out, lse = run(w, num_parts=parts, softmax_scale=0.02)
         ref_out, ref_lse = oracle.mla_decode(w, softmax_scale=0.02)
-        assert_close(out, lse, ref_out, ref_lse, what=f"flush parts={parts}")
+        assert_close(out, lse, ref_out, ref_lse, what=f"restart fmt={kv_format} topk={topk} parts={parts}")
 
 
 def test_check_inputs_finds_bad_lengths_and_pages():

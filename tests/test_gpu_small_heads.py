@@ -1,6 +1,6 @@
 """GPU parity of decode at small head counts (h_q * s_q <= 64, dense, bf16
 and FP8 caches): units of at most 32 rows (either format) run on
-their own kernel, larger ones on the main kernel; row counts below and between 16-row blocks, causal rows, the lazy rescale, forced split counts, bit identity under page
+their own kernel, larger ones on the main kernel; row counts below and between 16-row blocks, causal rows, the restart pass, forced split counts, bit identity under page
 permutation and across runs, and a seeded sample at the benchmark's size."""
 
 import numpy as np
@@ -56,8 +56,8 @@ def test_small_heads_base_and_scale(natural, scale, kv_format):
 def test_small_heads_growing_scores_rescale(h_q, kv_format):
     """Scores that climb by far more than any lag the running max may have
     (here by ~500 in log2 units over the sequence) force the recovery path:
-    a second pass of the segment on the small-head kernel (h_q 16, 32), the
-    flush path on the main kernel (h_q 128)."""
+    a second pass of the segment on the small-head kernel (h_q 16, 32) and
+    on the main kernel (h_q 128)."""
     w = synth.make_workload("small_grow", batch=2, h_q=h_q, s_q=1, seqlens=[900, 300], seed=73,
                             slack=0, kv_format=kv_format)
     kv = w.kv.copy()
