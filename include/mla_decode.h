@@ -193,6 +193,38 @@ mla_status mla_decode_sparse_fp8(const mla_problem* p, const void* q, const void
                                  int32_t num_parts, const int32_t* num_splits, void* workspace,
                                  size_t workspace_bytes, void* out, float* lse, void* stream);
 
+/* Size of the static device scratch behind mla_decode_paged_noalloc: 96 MiB.
+ * The split partials take 1,028 bytes per (segment slot, row), with
+ * num_parts + units slots of s_q * h_q rows (topk > 0: h_q rows); e.g. batch
+ * 128, s_q 2, h_q 128 over 128 parts needs (128 + 128) x 256 x 1,028 bytes
+ * = 64.3 MiB. */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)96 << 20)
+
+/* Decode and combine in one call that allocates nothing, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Arguments are those of
+ * mla_decode_paged without the workspace; `out` and `lse` are final on
+ * return of the launched work (the combine runs on the same stream).  The
+ * split partials go to a static device array of MLA_NOALLOC_SCRATCH_BYTES
+ * bytes inside the library, one per GPU, held until the process ends; the
+ * call makes no allocation of any kind.  Results equal those of
+ * mla_decode_paged followed by mla_decode_combine with the same metadata,
+ * bit for bit.
+ *   Errors: as mla_decode_paged; MLA_ERR_WORKSPACE_TOO_SMALL when
+ *   mla_decode_workspace_bytes for (p, num_parts) exceeds the scratch (a
+ *   smaller num_parts or the workspace entry point then applies).
+ *   Nothing in the scratch has to start at zero: every partial the combine
+ *   reads is written by the decode launch of the same call.
+ *   All calls on one GPU share that GPU's scratch, which keeps the last
+ *   call's contents: calls that overlap on one GPU (several streams or host
+ *   threads) race, and the caller must order them.
+ *   The first call on a device takes the array's device address
+ *   (hipGetSymbolAddress, with the stream's device current) and keeps it. */
+mla_status mla_decode_paged_noalloc(const mla_problem* p, const void* q, const void* kv_pool,
+                                    const int32_t* block_table, const int32_t* cache_seqlens,
+                                    const int32_t* indices, const int32_t* sched, int32_t num_parts,
+                                    const int32_t* num_splits, void* out, float* lse, void* stream);
+
 /* Merge split partial results by their log-sum-exp:
  *   M = max_s lse_s,  lse = M + log2(sum_s 2^(lse_s - M)),
  *   out = sum_s 2^(lse_s - lse) * out_s.

@@ -23,7 +23,7 @@ __all__ = [
     "mla_decode_with_kvcache", "mla_kv_quantize_fp8", "mla_sparse_prefill_workspace_bytes",
     "mla_sparse_prefill", "mla_sparse_prefill_num_parts", "mla_decode_check_inputs",
     "mla_decode_kernel_name", "mla_clock_probe", "shader_clock_mhz", "problem_for",
-    "workload_tensors",
+    "workload_tensors", "mla_decode_paged_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 MLA_KV_BF16 = 0
@@ -97,6 +97,7 @@ def _load():
     lib.mla_decode_paged_fp8.argtypes = [PP, P, P, P, P, P, I32, P, P, SZ, P, P, P]
     lib.mla_decode_sparse_fp8.argtypes = [PP, P, P, P, P, P, P, I32, P, P, SZ, P, P, P]
     lib.mla_decode_combine.argtypes = [PP, I32, P, P, SZ, P, P, P]
+    lib.mla_decode_paged_noalloc.argtypes = [PP, P, P, P, P, P, P, I32, P, P, P, P]
     lib.mla_kv_quantize_fp8.argtypes = [I32, I32, I32, I32, I32, P, P, P, P, P]
     lib.mla_decode_check_inputs.argtypes = [PP, P, P, P, P]
     lib.mla_sparse_prefill_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32, ctypes.POINTER(SZ)]
@@ -106,7 +107,7 @@ def _load():
                "mla_decode_get_metadata", "mla_decode_paged", "mla_decode_paged_fp8",
                "mla_decode_sparse_fp8", "mla_decode_combine", "mla_kv_quantize_fp8",
                "mla_sparse_prefill_workspace_bytes", "mla_sparse_prefill",
-               "mla_decode_check_inputs"):
+               "mla_decode_check_inputs", "mla_decode_paged_noalloc"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.mla_last_error.argtypes = []
     lib.mla_last_error.restype = ctypes.c_char_p
@@ -292,6 +293,23 @@ def mla_decode_sparse_fp8(p: Problem, q, kv_pool, block_table, cache_seqlens, in
         ctypes.byref(p), _ptr(q), _ptr(kv_pool), _ptr(block_table), _ptr(cache_seqlens),
         _ptr(indices), _ptr(sched), int(num_parts), _ptr(num_splits), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(stream)))
+
+
+# Bytes of the library's static scratch behind mla_decode_paged_noalloc.
+NOALLOC_SCRATCH_BYTES = 96 << 20
+
+
+def mla_decode_paged_noalloc(p: Problem, q, kv_pool, block_table, cache_seqlens, indices, sched,
+                             num_parts, num_splits, out, lse, stream=None):
+    """Decode and combine in one call with no workspace: the split partials
+    live in the library's static per-GPU scratch (calls that overlap on one
+    GPU race)."""
+    _check_decode_tensors(p, q, kv_pool, block_table, cache_seqlens, indices, out, lse)
+    _check_meta_tensors(p, num_parts, sched, num_splits)
+    _check(_load().mla_decode_paged_noalloc(
+        ctypes.byref(p), _ptr(q), _ptr(kv_pool), _ptr(block_table), _ptr(cache_seqlens),
+        _ptr(indices), _ptr(sched), int(num_parts), _ptr(num_splits), _ptr(out), _ptr(lse),
+        _stream(stream)))
 
 
 def mla_decode_combine(p: Problem, num_parts, num_splits, workspace, out, lse, stream=None):

@@ -15,6 +15,13 @@
 #include "../../include/mla_decode.h"
 #include "internal.h"
 
+// Scratch of mla_decode_paged_noalloc: the split partials (lse block, then
+// bf16 output block, as in a caller's workspace) of its decode and combine
+// launches.  Every GPU the library runs on holds its own copy until the
+// process ends.  In host code this name is a host-side stand-in: only the
+// device address taken by scratch_address() below may reach a kernel.
+static __device__ __align__(256) uint8_t scratch[MLA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -131,6 +138,44 @@ mla_status hip_status(hipError_t e, const char* what) {
 mla_status check_ptr(const void* ptr, const char* name, size_t align) {
   if (!ptr) return fail(MLA_ERR_INVALID_ARGUMENT, "%s: NULL pointer", name);
   if (!aligned(ptr, align)) return fail(MLA_ERR_INVALID_ARGUMENT, "%s: must be %zu-byte aligned", name, align);
+  return MLA_OK;
+}
+
+// Device address of `scratch` on each GPU, taken once per device, with that
+// device current, on the first no-allocation call that runs there.
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_addr[kScratchDevices] = {};
+
+mla_status scratch_address(hipStream_t stream, void** addr) {
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  int dev = cur;
+  if (stream) {
+    e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipStreamGetDevice: %s", hipGetErrorString(e));
+  }
+  if (dev < 0 || dev >= kScratchDevices)
+    return fail(MLA_ERR_UNSUPPORTED, "stream: device %d is beyond the %d devices the static scratch serves",
+                dev, kScratchDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_addr[dev]) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess)
+      return fail(MLA_ERR_HIP, "hipSetDevice(%d): %s", dev, hipGetErrorString(e));
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t back = hipSetDevice(cur);
+      if (e == hipSuccess) e = back;
+    }
+    if (e != hipSuccess)
+      return fail(MLA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    if (!a || !aligned(a, 256))
+      return fail(MLA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: unusable address %p", dev, a);
+    g_scratch_addr[dev] = a;
+  }
+  *addr = g_scratch_addr[dev];
   return MLA_OK;
 }
 
@@ -298,6 +343,40 @@ mla_status mla_decode_combine(const mla_problem* p, int32_t num_parts, const int
   return hip_status(mla::launch_combine(s, num_splits, ws_lse, ws_o, (uint16_t*)out, lse,
                                         (hipStream_t)stream),
                     "combine kernel launch");
+}
+
+mla_status mla_decode_paged_noalloc(const mla_problem* p, const void* q, const void* kv_pool,
+                                    const int32_t* block_table, const int32_t* cache_seqlens,
+                                    const int32_t* indices, const int32_t* sched, int32_t num_parts,
+                                    const int32_t* num_splits, void* out, float* lse, void* stream) {
+  mla::Shape s;
+  MLA_CHECK(check_problem(p, &s));
+  MLA_CHECK(check_parts(num_parts));
+  MLA_CHECK(check_ptr(q, "q", 16));
+  MLA_CHECK(check_ptr(kv_pool, "kv_pool", 16));
+  MLA_CHECK(check_ptr(block_table, "block_table", 4));
+  MLA_CHECK(check_ptr(cache_seqlens, "cache_seqlens", 4));
+  if (p->topk > 0) {
+    MLA_CHECK(check_ptr(indices, "indices", 4));
+  } else if (indices) {
+    return fail(MLA_ERR_INVALID_ARGUMENT, "indices: must be NULL when topk == 0");
+  }
+  MLA_CHECK(check_ptr(sched, "sched", 4));
+  MLA_CHECK(check_ptr(num_splits, "num_splits", 4));
+  MLA_CHECK(check_ptr(out, "out", 16));
+  MLA_CHECK(check_ptr(lse, "lse", 4));
+  const size_t need = mla::ws_total_bytes(num_parts, s.units, s.rows);
+  if (need > MLA_NOALLOC_SCRATCH_BYTES)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL,
+                "num_parts/batch/s_q/h_q: the split partials need %zu bytes, more than the %zu-byte static "
+                "scratch of mla_decode_paged_noalloc (call mla_decode_paged with a workspace instead)",
+                need, (size_t)MLA_NOALLOC_SCRATCH_BYTES);
+  if (s.units == 0) return ok();
+  void* ws = nullptr;
+  MLA_CHECK(scratch_address((hipStream_t)stream, &ws));
+  MLA_CHECK(mla_decode_paged(p, q, kv_pool, block_table, cache_seqlens, indices, sched, num_parts,
+                             num_splits, ws, need, out, lse, stream));
+  return mla_decode_combine(p, num_parts, num_splits, ws, need, out, lse, stream);
 }
 
 mla_status mla_decode_check_inputs(const mla_problem* p, const int32_t* block_table,

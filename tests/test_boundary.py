@@ -267,3 +267,26 @@ def test_clock_probe_rejects_bad_arguments():
     assert "workgroups" in mla.mla_last_error()
     assert lib.mla_clock_probe(ctypes.c_void_p(FAKE), 4, 0, None) == mla.MLA_ERR_INVALID_ARGUMENT
     assert "spins" in mla.mla_last_error()
+
+
+def call_noalloc(p, parts=4, idx=None):
+    lib = mla._load()
+    v = ctypes.c_void_p
+    return lib.mla_decode_paged_noalloc(ctypes.byref(p), v(FAKE), v(FAKE), v(FAKE), v(FAKE),
+                                        None if idx is None else v(idx), v(FAKE), parts, v(FAKE),
+                                        v(FAKE), v(FAKE), None)
+
+
+def test_noalloc_size_limit_checked_on_the_host():
+    """The allocation-free call rejects a problem whose split partials exceed
+    its static scratch, before any HIP call, naming the limit."""
+    assert mla.NOALLOC_SCRATCH_BYTES == 96 << 20
+    text = open(HEADER).read()
+    assert re.search(r"#define MLA_NOALLOC_SCRATCH_BYTES \(\(size_t\)96 << 20\)", text)
+    p = good(batch=128, s_q=2, h_q=128)
+    fits = max(n for n in range(1, 2049) if mla.mla_decode_workspace_bytes(p, n) <= mla.NOALLOC_SCRATCH_BYTES)
+    assert mla.mla_decode_workspace_bytes(p, 128) <= mla.NOALLOC_SCRATCH_BYTES  # 64.3 MiB
+    assert call_noalloc(p, parts=fits + 1) == mla.MLA_ERR_WORKSPACE_TOO_SMALL
+    assert "static scratch" in mla.mla_last_error()
+    assert call_noalloc(good(), idx=FAKE) == mla.MLA_ERR_INVALID_ARGUMENT
+    assert "indices" in mla.mla_last_error()
