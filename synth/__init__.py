@@ -389,3 +389,79 @@ def make_sparse_prefill(name: str, *, s_q: int, h_q: int, s_kv: int, topk: int, 
     scale = np.float32(1.0 / math.sqrt(D_QK)) if softmax_scale is None else np.float32(softmax_scale)
     return PrefillWorkload(name=name, q=q, kv=np.ascontiguousarray(kv), indices=indices,
                            kv_format=kv_format, softmax_scale=float(scale))
+
+
+@dataclasses.dataclass
+class IndexWorkload:
+    """Inputs of one FP8 top-k indexer call, plus the bf16 query the FP8
+    query was encoded from (the query of the sparse decode that follows).
+
+    Recipe: a dense FP8 decode workload (``make_workload`` with the same seed)
+    over the cache's rows (``ceil(L_b / kpool)`` pooled rows per sequence), its
+    bf16 query ``[B, s_q, h, 576]`` as drawn there; the FP8 query is the first
+    512 values of each (b, i, h) query row encoded like a cache row (per
+    1x128 tile, scale = amax / 448, e4m3fn codes).  ``cache_seqlens`` holds
+    the token counts ``L_b``."""
+
+    name: str
+    batch: int
+    s_q: int
+    h: int
+    topk: int
+    kpool: int
+    is_causal: int
+    q_bf16: np.ndarray       # uint16 [B, s_q, h, 576]
+    q_codes: np.ndarray      # uint8 [B, s_q, h, 512]
+    q_scales: np.ndarray     # float32 [B, s_q, h, 4]
+    kv: np.ndarray           # uint8 [num_pages, 64, 656]
+    block_table: np.ndarray  # int32 [B, max_pages_per_seq]
+    cache_seqlens: np.ndarray  # int32 [B], tokens
+
+    @property
+    def num_pages(self) -> int:
+        return int(self.kv.shape[0])
+
+    @property
+    def max_pages_per_seq(self) -> int:
+        return int(self.block_table.shape[1])
+
+    def rows(self) -> np.ndarray:
+        """Cached (pooled) rows per sequence."""
+        L = self.cache_seqlens.astype(np.int64)
+        return (L + self.kpool - 1) // self.kpool
+
+    def flops(self) -> int:
+        """2 * h * 512 multiply-adds per (query token, cached row) pair."""
+        return 2 * self.h * D_NOPE * self.s_q * int(self.rows().sum())
+
+    def algorithmic_bytes(self) -> int:
+        """The quantised part of every cached row once (512 codes + 16 bytes
+        of scales), the FP8 query with its scales, the block-table entries and
+        lengths read, and the int32 indices written."""
+        pages = (self.rows() + self.page_size - 1) // self.page_size
+        q = self.batch * self.s_q * self.h * (D_NOPE + 16)
+        return (int(self.rows().sum()) * (D_NOPE + 16) + q + 4 * int(pages.sum()) + 4 * self.batch
+                + 4 * self.batch * self.s_q * self.topk)
+
+    page_size: int = 64
+
+
+def make_index_workload(name: str, *, batch: int, s_q: int, h: int, seqlens, seed: int, topk: int,
+                        kpool: int = 1, is_causal: int = 0, max_pages_per_seq: Optional[int] = None,
+                        slack: float = 0.1) -> IndexWorkload:
+    """Seeded indexer workload (recipe in :class:`IndexWorkload`)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if isinstance(seqlens, Uniform):
+        L = rng.integers(seqlens.lo, seqlens.hi, size=batch, endpoint=True).astype(np.int32)
+    else:
+        L = np.asarray(list(seqlens), dtype=np.int32)
+        assert L.shape == (batch,)
+    rows = [(-(-int(l) // kpool)) for l in L]
+    w = make_workload(name, batch=batch, h_q=h, s_q=s_q, seqlens=rows, seed=seed + 1,
+                      kv_format=KV_FP8_656, slack=slack, max_pages_per_seq=max_pages_per_seq)
+    enc = encode_fp8_rows(w.q.reshape(-1, D_QK))
+    q_codes = np.ascontiguousarray(enc[:, :D_NOPE]).reshape(batch, s_q, h, D_NOPE)
+    q_scales = np.ascontiguousarray(enc[:, D_NOPE:D_NOPE + 16]).view(np.float32).reshape(batch, s_q, h, 4)
+    return IndexWorkload(name=name, batch=batch, s_q=s_q, h=h, topk=topk, kpool=kpool,
+                         is_causal=is_causal, q_bf16=w.q, q_codes=q_codes, q_scales=q_scales,
+                         kv=w.kv, block_table=w.block_table, cache_seqlens=L)
