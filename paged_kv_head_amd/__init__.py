@@ -23,7 +23,8 @@ __all__ = [
     "mla_decode_with_kvcache", "mla_kv_quantize_fp8", "mla_sparse_prefill_workspace_bytes",
     "mla_sparse_prefill", "mla_sparse_prefill_num_parts", "mla_decode_check_inputs",
     "mla_decode_kernel_name", "mla_clock_probe", "shader_clock_mhz", "problem_for",
-    "workload_tensors", "mla_decode_paged_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "workload_tensors", "mla_decode_paged_noalloc", "NOALLOC_SCRATCH_BYTES", "IndexProblem",
+    "mla_fp8_index_workspace_bytes", "mla_fp8_index_top_k", "index_problem_for", "index_tensors",
 ]
 
 MLA_KV_BF16 = 0
@@ -68,6 +69,18 @@ class Problem(ctypes.Structure):
                    topk, kv_format, is_causal, flags, float(softmax_scale))
 
 
+class IndexProblem(ctypes.Structure):
+    """Mirror of ``mla_index_problem`` (FP8 top-k indexer)."""
+
+    _fields_ = [(n, ctypes.c_int32) for n in ("batch", "s_q", "h", "d", "page_size", "num_pages",
+                                              "max_pages_per_seq", "topk", "kpool", "is_causal")]
+
+    @classmethod
+    def make(cls, *, batch, s_q, h, num_pages, max_pages_per_seq, topk, kpool=1, is_causal=0,
+             d=512, page_size=64) -> "IndexProblem":
+        return cls(batch, s_q, h, d, page_size, num_pages, max_pages_per_seq, topk, kpool, is_causal)
+
+
 _lib = None
 
 
@@ -98,6 +111,9 @@ def _load():
     lib.mla_decode_sparse_fp8.argtypes = [PP, P, P, P, P, P, P, I32, P, P, SZ, P, P, P]
     lib.mla_decode_combine.argtypes = [PP, I32, P, P, SZ, P, P, P]
     lib.mla_decode_paged_noalloc.argtypes = [PP, P, P, P, P, P, P, I32, P, P, P, P]
+    IP = ctypes.POINTER(IndexProblem)
+    lib.mla_fp8_index_workspace_bytes.argtypes = [IP, ctypes.POINTER(SZ)]
+    lib.mla_fp8_index_top_k.argtypes = [IP, P, P, P, P, P, P, SZ, P, P, P]
     lib.mla_kv_quantize_fp8.argtypes = [I32, I32, I32, I32, I32, P, P, P, P, P]
     lib.mla_decode_check_inputs.argtypes = [PP, P, P, P, P]
     lib.mla_sparse_prefill_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32, ctypes.POINTER(SZ)]
@@ -107,7 +123,8 @@ def _load():
                "mla_decode_get_metadata", "mla_decode_paged", "mla_decode_paged_fp8",
                "mla_decode_sparse_fp8", "mla_decode_combine", "mla_kv_quantize_fp8",
                "mla_sparse_prefill_workspace_bytes", "mla_sparse_prefill",
-               "mla_decode_check_inputs", "mla_decode_paged_noalloc"):
+               "mla_decode_check_inputs", "mla_decode_paged_noalloc",
+               "mla_fp8_index_workspace_bytes", "mla_fp8_index_top_k"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.mla_last_error.argtypes = []
     lib.mla_last_error.restype = ctypes.c_char_p
@@ -208,6 +225,50 @@ def workload_tensors(w, device="cuda"):
     sl = torch.from_numpy(np.ascontiguousarray(w.cache_seqlens)).to(dev)
     idx = None if w.indices is None else torch.from_numpy(np.ascontiguousarray(w.indices)).to(dev)
     return q, kv, bt, sl, idx
+
+
+def index_problem_for(w) -> IndexProblem:
+    """``IndexProblem`` of an indexer workload (attributes batch, s_q, h,
+    num_pages, max_pages_per_seq, topk, kpool, is_causal)."""
+    return IndexProblem.make(batch=w.batch, s_q=w.s_q, h=w.h, num_pages=w.num_pages,
+                             max_pages_per_seq=w.max_pages_per_seq, topk=w.topk, kpool=w.kpool,
+                             is_causal=w.is_causal)
+
+
+def index_tensors(w, device="cuda"):
+    """Device tensors of an indexer workload: (q codes uint8, q scales
+    float32, kv_pool uint8, block_table int32, cache_seqlens int32)."""
+    import numpy as np
+
+    dev = torch.device(device)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    return t(w.q_codes), t(w.q_scales), t(w.kv), t(w.block_table), t(w.cache_seqlens)
+
+
+def mla_fp8_index_workspace_bytes(p: IndexProblem) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_load().mla_fp8_index_workspace_bytes(ctypes.byref(p), ctypes.byref(n)))
+    return int(n.value)
+
+
+def mla_fp8_index_top_k(p: IndexProblem, q_fp8, q_scale, kv_pool, block_table, cache_seqlens,
+                        workspace, indices, scores=None, stream=None):
+    """FP8 top-k indexer: per query token the top-k visible cache rows by the
+    head-summed FP8 score, in ascending row order, -1 fill (see mla_index.h)."""
+    tokens = p.batch * p.s_q
+    _expect("q_fp8", q_fp8, torch.uint8, tokens * p.h * 512)
+    _expect("q_scale", q_scale, torch.float32, tokens * p.h * 4)
+    _expect("kv_pool", kv_pool, None, p.num_pages * p.page_size * 656)
+    _expect("block_table", block_table, torch.int32, p.batch * p.max_pages_per_seq)
+    _expect("cache_seqlens", cache_seqlens, torch.int32, p.batch)
+    _expect("indices", indices, torch.int32, tokens * p.topk)
+    if scores is not None:
+        _expect("scores", scores, torch.float32, tokens * p.topk)
+    _expect("workspace", workspace, None, mla_fp8_index_workspace_bytes(p), at_least=True)
+    _check(_load().mla_fp8_index_top_k(
+        ctypes.byref(p), _ptr(q_fp8), _ptr(q_scale), _ptr(kv_pool), _ptr(block_table),
+        _ptr(cache_seqlens), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _ptr(indices), _ptr(scores), _stream(stream)))
 
 
 def mla_decode_kernel_name(p: Problem) -> str:

@@ -11,7 +11,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmla_decode.so")
 SOURCES = ["api.hip", "metadata.hip", "decode.hip", "decode_small.hip", "combine.hip", "kv_writer.hip", "prefill.hip",
-           "clock_probe.hip"]
+           "clock_probe.hip", "indexer.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

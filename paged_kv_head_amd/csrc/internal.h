@@ -81,6 +81,23 @@ hipError_t launch_clock_probe(int64_t* out, int32_t workgroups, int32_t spins, h
 hipError_t launch_identity_table(int32_t* table, int32_t pages, int32_t* seqlen, int32_t s_kv,
                                  hipStream_t stream);
 
+// FP8 top-k indexer (indexer.hip).
+struct IndexLaunch {
+  int32_t batch, s_q, h, kpool, is_causal, max_pages, topk;
+  const uint8_t* q;
+  const float* qs;
+  const uint8_t* kv;
+  const int32_t* block_table;
+  const int32_t* seqlens;
+  float* ws;  // fp32 scores [batch, s_q, 64 * max_pages]
+  int32_t* indices;
+  float* scores;  // may be null
+};
+// Heads padded to a multiple of 16 rows, query tokens per workgroup and
+// workgroups per sequence for h heads; false when h is out of range.
+bool index_shape(int32_t h, int32_t s_q, int32_t* h16, int32_t* tokens_per_group, int32_t* groups);
+hipError_t launch_index(const IndexLaunch& l, hipStream_t stream);
+
 // Sparse prefill runs the decode path over chunks of at most this many query
 // tokens (each a decode unit), which bounds the split workspace.
 constexpr int kPrefillChunk = 2048;

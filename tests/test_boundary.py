@@ -23,7 +23,8 @@ FAKE = 0x10000  # an aligned non-null address; never dereferenced by these calls
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    inc = os.path.dirname(HEADER)
+    text = "".join(open(os.path.join(inc, f)).read() for f in sorted(os.listdir(inc)) if f.endswith(".h"))
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", text)))
 
@@ -290,3 +291,45 @@ def test_noalloc_size_limit_checked_on_the_host():
     assert "static scratch" in mla.mla_last_error()
     assert call_noalloc(good(), idx=FAKE) == mla.MLA_ERR_INVALID_ARGUMENT
     assert "indices" in mla.mla_last_error()
+
+
+def index_good(**kw):
+    d = dict(batch=2, s_q=2, h=64, num_pages=9, max_pages_per_seq=4, topk=16)
+    d.update(kw)
+    return mla.IndexProblem.make(**d)
+
+
+def call_index(p, ws_bytes=1 << 40, **ptrs):
+    lib = mla._load()
+    a = dict(q=FAKE, qs=FAKE, kv=FAKE, bt=FAKE, sl=FAKE, ws=FAKE, idx=FAKE, sc=None)
+    a.update(ptrs)
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.mla_fp8_index_top_k(ctypes.byref(p), v(a["q"]), v(a["qs"]), v(a["kv"]), v(a["bt"]),
+                                   v(a["sl"]), v(a["ws"]), ws_bytes, v(a["idx"]), v(a["sc"]), None)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("h", 0, mla.MLA_ERR_INVALID_ARGUMENT), ("h", 257, mla.MLA_ERR_UNSUPPORTED),
+    ("d", 576, mla.MLA_ERR_UNSUPPORTED), ("page_size", 32, mla.MLA_ERR_UNSUPPORTED),
+    ("max_pages_per_seq", 1025, mla.MLA_ERR_UNSUPPORTED), ("topk", 0, mla.MLA_ERR_INVALID_ARGUMENT),
+    ("topk", 257, mla.MLA_ERR_INVALID_ARGUMENT), ("kpool", 0, mla.MLA_ERR_INVALID_ARGUMENT),
+    ("is_causal", 2, mla.MLA_ERR_INVALID_ARGUMENT), ("s_q", 0, mla.MLA_ERR_INVALID_ARGUMENT),
+    ("batch", -1, mla.MLA_ERR_INVALID_ARGUMENT), ("num_pages", 0, mla.MLA_ERR_INVALID_ARGUMENT),
+])
+def test_index_problem_fields_rejected(field, value, status):
+    p = index_good()
+    setattr(p, field, value)
+    assert call_index(p) == status
+    assert field in mla.mla_last_error()
+
+
+def test_index_pointers_and_workspace_checked():
+    p = index_good()
+    for name, arg in [("q_fp8", "q"), ("q_scale", "qs"), ("kv_pool", "kv"), ("block_table", "bt"),
+                      ("cache_seqlens", "sl"), ("workspace", "ws"), ("indices", "idx")]:
+        assert call_index(p, **{arg: None}) == mla.MLA_ERR_INVALID_ARGUMENT
+        assert name in mla.mla_last_error()
+    assert call_index(p, q=FAKE + 4) == mla.MLA_ERR_INVALID_ARGUMENT  # alignment
+    need = mla.mla_fp8_index_workspace_bytes(p)
+    assert need == 2 * 2 * 4 * 64 * 4  # fp32 scores [B, s_q, 64 * max_pages]
+    assert call_index(p, ws_bytes=need - 1) == mla.MLA_ERR_WORKSPACE_TOO_SMALL

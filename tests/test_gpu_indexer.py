@@ -1,0 +1,164 @@
+"""GPU parity of the FP8 top-k indexer (mla_fp8_index_top_k) against the fp64
+oracle, and the indexer -> sparse decode chain against the decode oracle.
+
+The selected set is not unique when scores tie or nearly tie, so each token's
+result is checked for validity rather than equality: indices distinct, in
+ascending order and visible; as many as min(topk, visible rows), then -1
+(scores -inf); every returned score within the error bound of the oracle's
+value; and no unselected row whose oracle score exceeds a selected row's by
+more than the two bounds together.
+
+Error bound.  An e4m3 x e4m3 product is exact in fp32, but the FP8 matrix
+instruction does not sum its 64 products in exact fp32: on gfx950 its result
+was measured to deviate from the exact sum by up to 1.8e-4 of the sum of the
+absolute products (random codes over the whole e4m3 range; 2.7e-5 for
+quantised Gaussian rows).  The bound takes 2^-11 per instruction, two
+instructions per 128-dim tile, plus fp32 rounding of the scaling and the
+sums over tiles and heads: |S_gpu - S| <= (2 * 2^-11 + 64 * 2^-24) * A, A the
+same sum over absolute values (oracle.indexer.abs_scores)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_head_amd as mla
+import synth
+from oracle import indexer as ix
+from tests.harness import assert_close
+
+pytestmark = pytest.mark.gpu
+
+EPS_MFMA = 2.0 ** -11
+REL_BOUND = 2 * EPS_MFMA + 64 * 2.0 ** -24
+
+
+def run_index(w, with_scores=True, tensors=None):
+    p = mla.index_problem_for(w)
+    qc, qs, kv, bt, sl = tensors if tensors is not None else mla.index_tensors(w)
+    ws = torch.empty(mla.mla_fp8_index_workspace_bytes(p), dtype=torch.uint8, device="cuda")
+    idx = torch.full((w.batch, w.s_q, w.topk), -7, dtype=torch.int32, device="cuda")
+    sc = torch.full((w.batch, w.s_q, w.topk), float("nan"), dtype=torch.float32, device="cuda") if with_scores else None
+    mla.mla_fp8_index_top_k(p, qc, qs, kv, bt, sl, ws, idx, sc)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), (sc.cpu().numpy() if with_scores else None)
+
+
+def check_token(w, b, i, idx, sc, what=""):
+    """Validity of one token's selection; returns (agreement with the
+    oracle's own selection, max |S_gpu - S| / A)."""
+    S = ix.scores(w, b, i)
+    A = ix.abs_scores(w, b, i)
+    n, k = S.shape[0], w.topk
+    m = min(k, n)
+    got = idx[b, i]
+    assert np.all(got[m:] == -1), f"{what}: fill"
+    assert np.all(np.isneginf(sc[b, i, m:])), f"{what}: fill scores"
+    sel = got[:m]
+    assert np.all((sel >= 0) & (sel < n)), f"{what}: index out of the visible range"
+    assert np.all(np.diff(sel) > 0), f"{what}: not strictly ascending"
+    if m == 0:
+        return 1.0, 0.0
+    tol = REL_BOUND * A
+    err = np.abs(sc[b, i, :m].astype(np.float64) - S[sel])
+    assert np.all(err <= tol[sel]), f"{what}: score off by {np.max(err / tol[sel]):.3g} x the bound"
+    if m < n:
+        mask = np.ones(n, dtype=bool)
+        mask[sel] = False
+        lo = np.min(S[sel] + tol[sel])
+        hi = np.max(S[mask] - tol[mask])
+        assert lo >= hi, f"{what}: an unselected row outscores a selected one beyond the bound"
+    ref = ix.select(S, k)
+    agree = np.intersect1d(ref, sel).shape[0] / m
+    return agree, float(np.max(err / np.maximum(A[sel], 1e-300)))
+
+
+CASES = [
+    # h, s_q, causal, kpool, seqlens, topk
+    (16, 1, 0, 1, [1, 63, 64, 65, 300], 32),
+    (128, 2, 0, 1, [70, 2000, 130], 64),
+    (128, 2, 1, 1, [2, 129, 1000], 100),
+    (64, 3, 1, 4, [5, 700, 257], 20),
+    (8, 4, 0, 1, [90, 3000], 16),
+    (40, 2, 0, 2, [1000, 77, 5], 50),
+    (256, 2, 1, 1, [600, 64], 128),
+    (1, 1, 0, 1, [500, 2], 8),
+    (32, 1, 0, 1, [10, 0, 64], 16),
+    (128, 1, 0, 1, [5000], 4096),
+]
+
+
+@pytest.mark.parametrize("h,s_q,causal,kpool,lens,topk", CASES)
+def test_index_shapes(h, s_q, causal, kpool, lens, topk):
+    w = synth.make_index_workload("idx", batch=len(lens), s_q=s_q, h=h, seqlens=lens, seed=200 + h + s_q,
+                                  topk=topk, kpool=kpool, is_causal=causal)
+    print(f"h {h} s_q {s_q} causal {causal} kpool {kpool} lens {lens} topk {topk}", flush=True)
+    idx, sc = run_index(w)
+    agree = []
+    for b in range(w.batch):
+        for i in range(s_q):
+            a, _ = check_token(w, b, i, idx, sc, what=f"b={b} i={i}")
+            agree.append(a)
+    print(f"   agreement with the oracle's selection: min {min(agree):.4f}", flush=True)
+
+
+def test_index_full_length_sample():
+    """Sequences of 65536 tokens (the sparse decode benchmark's cache), topk
+    2048, 128 heads, two query tokens: sampled tokens against the oracle."""
+    w = synth.make_index_workload("idx_full", batch=8, s_q=2, h=128, seqlens=[65536] * 8, seed=301,
+                                  topk=2048)
+    idx, sc = run_index(w)
+    rng = np.random.default_rng(0)
+    for b, i in [(0, 0), (3, 1), (7, 0), (int(rng.integers(8)), 1)]:
+        a, e = check_token(w, b, i, idx, sc, what=f"b={b} i={i}")
+        print(f"token ({b}, {i}): agreement {a:.4f}, max |S_gpu - S| / A {e:.3g}", flush=True)
+        assert a >= 0.99
+
+
+def test_index_bit_identity_and_page_permutation():
+    w = synth.make_index_workload("idx_bits", batch=3, s_q=2, h=64, seqlens=[3000, 64, 1500], seed=302,
+                                  topk=200)
+    i1, s1 = run_index(w)
+    i2, s2 = run_index(w)
+    assert np.array_equal(i1, i2) and np.array_equal(s1.view(np.int32), s2.view(np.int32))
+    perm = np.random.default_rng(8).permutation(w.num_pages)
+    kv2 = np.empty_like(w.kv)
+    kv2[perm] = w.kv
+    w.kv = kv2
+    w.block_table = np.where(w.block_table >= 0, perm[np.maximum(w.block_table, 0)], -1).astype(np.int32)
+    i3, s3 = run_index(w)
+    assert np.array_equal(i1, i3) and np.array_equal(s1.view(np.int32), s3.view(np.int32))
+
+
+def test_index_without_scores_output():
+    w = synth.make_index_workload("idx_ns", batch=2, s_q=1, h=32, seqlens=[700, 100], seed=303, topk=64)
+    i1, _ = run_index(w)
+    i2, _ = run_index(w, with_scores=False)
+    assert np.array_equal(i1, i2)
+
+
+@pytest.mark.parametrize("topk", [256, 2048])
+def test_indexer_then_sparse_decode(topk):
+    """The indexer's output drives mla_decode_sparse_fp8 directly: the decode
+    over the selected rows matches the decode oracle on the same indices, and
+    the selection is valid."""
+    lens = [3000, 5000, 200, 64]
+    w = synth.make_index_workload("idx_e2e", batch=4, s_q=2, h=128, seqlens=lens, seed=304, topk=topk)
+    idx, sc = run_index(w)
+    for b in range(w.batch):
+        for i in range(w.s_q):
+            check_token(w, b, i, idx, sc, what=f"b={b} i={i}")
+    d = synth.Workload(name="e2e", batch=w.batch, s_q=w.s_q, h_q=w.h, page_size=64,
+                       kv_format=synth.KV_FP8_656, topk=topk, is_causal=0,
+                       softmax_scale=float(np.float32(1.0 / np.sqrt(576.0))), q=w.q_bf16, kv=w.kv,
+                       block_table=w.block_table, cache_seqlens=w.cache_seqlens, indices=idx)
+    p = mla.problem_for(d)
+    q, kv, bt, sl, ind = mla.workload_tensors(d)
+    plan = mla.DecodePlan(p, q.device)
+    out = torch.empty((d.batch, d.s_q, d.h_q, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((d.batch, d.s_q, d.h_q), dtype=torch.float32, device="cuda")
+    plan.metadata(sl)
+    plan.decode(q, kv, bt, sl, ind, out, lse)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle.mla_decode(d)
+    assert_close(out.float().cpu().numpy(), lse.cpu().numpy(), ref_out, ref_lse, what=f"topk={topk}")

@@ -26,6 +26,9 @@ from paged_kv_head_amd import build as build_mod
 
 HIPCC = build_mod.HIPCC
 DECODE = os.path.join(build_mod.CSRC, "decode.hip")
+INDEXER = os.path.join(build_mod.CSRC, "indexer.hip")
+SCORE_KERNEL = "_ZN3mla12_GLOBAL__N_118index_score_kernelENS0_9IndexArgsE"
+TOPK_KERNEL = "_ZN3mla12_GLOBAL__N_117index_topk_kernelENS0_9IndexArgsE"
 KERNELS = {  # (cache format, sparse) -> mangled name
     (0, False): "_ZN3mla12_GLOBAL__N_113decode_kernelILi0ELb0EEEvNS_10DecodeArgsE",
     (1, False): "_ZN3mla12_GLOBAL__N_113decode_kernelILi1ELb0EEEvNS_10DecodeArgsE",
@@ -35,15 +38,24 @@ KERNELS = {  # (cache format, sparse) -> mangled name
 DENSE_IN_FLIGHT = 8  # copies the dense bf16 tile loop leaves outstanding at each of its two waits
 
 
-@pytest.fixture(scope="module")
-def asm(tmp_path_factory):
+def compile_asm(tmp_path_factory, src):
     if not os.path.exists(HIPCC):
         pytest.skip("hipcc not installed")
-    out = str(tmp_path_factory.mktemp("asm") / "decode.s")
+    out = str(tmp_path_factory.mktemp("asm") / (os.path.basename(src) + ".s"))
     flags = [f for f in build_mod.FLAGS if f not in ("-fPIC", "-shared")]
-    subprocess.check_call([HIPCC, *flags, "-S", "--cuda-device-only", DECODE, "-o", out])
+    subprocess.check_call([HIPCC, *flags, "-S", "--cuda-device-only", src, "-o", out])
     with open(out) as f:
         return f.read().split("\n")
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    return compile_asm(tmp_path_factory, DECODE)
+
+
+@pytest.fixture(scope="module")
+def asm_indexer(tmp_path_factory):
+    return compile_asm(tmp_path_factory, INDEXER)
 
 
 def function_body(lines, name):
@@ -61,8 +73,8 @@ def instructions(block_lines):
     return out
 
 
-def innermost_loop(body):
-    """Instructions of the blocks LLVM marks as lying in the deepest loop."""
+def loop_blocks(body):
+    """Loop depth LLVM gives each line's block."""
     depth_of = []
     depth = 0
     for i, l in enumerate(body):
@@ -77,6 +89,12 @@ def innermost_loop(body):
             m = re.findall(r"Depth=(\d+)", " ".join(ctx))
             depth = max(map(int, m)) if m else 0
         depth_of.append(depth)
+    return depth_of
+
+
+def innermost_loop(body):
+    """Instructions of the blocks LLVM marks as lying in the deepest loop."""
+    depth_of = loop_blocks(body)
     deepest = max(depth_of)
     assert deepest >= 1, "no loop found"
     return instructions([l for l, d in zip(body, depth_of) if d == deepest]), deepest
@@ -145,3 +163,22 @@ def test_lds_fits_one_workgroup_per_cu(asm):
                 break
     assert len(sizes) == len(KERNELS)
     assert all(0 < v <= 160 * 1024 for v in sizes.values()), sizes
+
+
+def test_indexer_page_loop_waits_only_for_its_copies(asm_indexer):
+    """The score kernel's page loop (outermost loop) waits on vector memory
+    only through its three explicit waits (two pages ahead, one, none), and
+    neither indexer kernel spills or touches memory through flat pointers
+    in a loop."""
+    body = function_body(asm_indexer, SCORE_KERNEL)
+    depth = loop_blocks(body)
+    page_loop = instructions([l for l, d in zip(body, depth) if d == 1])
+    counts = sorted(int(re.search(r"vmcnt\((\d+)\)", t).group(1)) for t in page_loop
+                    if t.startswith("s_waitcnt") and "vmcnt" in t)
+    assert counts == [0, 8, 16], counts
+    assert sum("mfma" in t for t in page_loop) == 32  # 4 tiles x 2 key blocks x 2 row blocks x 2
+    for name in (SCORE_KERNEL, TOPK_KERNEL):
+        b = function_body(asm_indexer, name)
+        d = loop_blocks(b)
+        in_loops = instructions([l for l, x in zip(b, d) if x >= 1])
+        assert not [t for t in in_loops if t.startswith("scratch_") or t.startswith("flat_")], name
