@@ -50,14 +50,15 @@ def parse():
     ap.add_argument("--num-parts", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-units", type=int, default=None)
-    ap.add_argument("--kernel", choices=["decode", "small", "small_fp8", "writer", "prefill"],
+    ap.add_argument("--kernel", choices=["decode", "small", "small_fp8", "writer", "prefill", "indexer"],
                     default="decode",
                     help="decode: the decode step (default); writer: the FP8 KV writer filling "
                          "128 sequences x 4096 new tokens; prefill: sparse prefill, 4096 query "
                          "tokens x 128 heads over a 32768-row cache, topk 2048; small: decode with "
                          "16 query heads (an 8-way head split of the 128), batch 128, lengths "
                          "U[1024, 8192]; small_fp8: the same heads over the 656-byte FP8 cache, "
-                         "lengths U[8192, 32768]")
+                         "lengths U[8192, 32768]; indexer: the FP8 top-k indexer over 128 x 65536 "
+                         "cached FP8 rows, 2 query tokens x 128 heads, topk 2048")
     ap.add_argument("--no-measured-peaks", action="store_true",
                     help="skip the reference measurements of HBM copy bandwidth and bf16 GEMM "
                          "throughput on this GPU")
@@ -408,6 +409,131 @@ def bench_prefill(args):
     print(json.dumps(line), flush=True)
 
 
+INDEX_WORKLOAD = dict(name="index_b128_sq2_h128_l65536_topk2048", batch=128, s_q=2, h=128, seqlen=65536,
+                      topk=2048, seed=88)
+
+
+def index_cpu_baseline(w, n_tokens=8, min_seconds=10.0, max_reps=6):
+    """The indexer oracle (numpy fp64) on a bounded sample of query tokens;
+    value in GB/s of the sample's algorithmic bytes (its share of the cache
+    rows, query and indices)."""
+    from oracle import indexer as ix
+
+    U = w.batch * w.s_q
+    rng = np.random.default_rng(0)
+    pick = [(int(u) // w.s_q, int(u) % w.s_q) for u in np.sort(rng.choice(U, size=min(n_tokens, U), replace=False))]
+    secs, reps = 0.0, 0
+    while reps < max_reps and (reps == 0 or secs < min_seconds):
+        t = time.perf_counter()
+        ix.top_k(w, tokens=pick)
+        secs += time.perf_counter() - t
+        reps += 1
+    per_token = w.algorithmic_bytes() / U
+    return {"value": per_token * len(pick) * reps / secs / 1e9, "unit": "GB/s",
+            "cores": int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count(), "kind": "oracle",
+            "sample": f"{len(pick)} of {U} query tokens (all {w.h} heads, all {int(w.rows()[0])} rows) of "
+                      f"{w.name}, {reps} pass(es), {secs:.1f} s on the host (numpy fp64; BLAS threads "
+                      f"as the host allows)"}
+
+
+def bench_indexer(args):
+    """FP8 top-k indexer over the sparse decode benchmark's cache: 128
+    sequences of 65536 tokens in the 656-byte FP8 layout, two query tokens of
+    128 heads each, topk 2048.  A step is one mla_fp8_index_top_k call (the
+    score kernel, then the selection kernel), timed as its two phases."""
+    import torch
+
+    import paged_kv_head_amd as mla
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    c = INDEX_WORKLOAD
+    t0 = time.time()
+    w = synth.make_index_workload(c["name"], batch=c["batch"], s_q=c["s_q"], h=c["h"],
+                                  seqlens=[c["seqlen"]] * c["batch"], seed=c["seed"], topk=c["topk"])
+    print(f"[bench] workload {w.name}: generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    p = mla.index_problem_for(w)
+    qc, qs, kv, bt, sl = mla.index_tensors(w)
+    need = mla.mla_fp8_index_workspace_bytes(p)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    idx = torch.empty((w.batch, w.s_q, w.topk), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    mla.mla_fp8_index_top_k(p, qc, qs, kv, bt, sl, ws, idx)  # checked call once
+    lib = mla._load()
+    P = ctypes.c_void_p
+    pp = ctypes.byref(p)
+    st = P(stream.cuda_stream)
+    score_args = (pp, P(qc.data_ptr()), P(qs.data_ptr()), P(kv.data_ptr()), P(bt.data_ptr()),
+                  P(sl.data_ptr()), P(ws.data_ptr()), ctypes.c_size_t(need), st)
+    select_args = (pp, P(sl.data_ptr()), P(ws.data_ptr()), ctypes.c_size_t(need), P(idx.data_ptr()), None, st)
+
+    def step(i, ev=None):
+        if ev:
+            ev[0].record(stream)
+        a = lib.mla_fp8_index_scores(*score_args)
+        if ev:
+            ev[1].record(stream)
+        b = lib.mla_fp8_index_select(*select_args)
+        if ev:
+            ev[2].record(stream)
+        if a or b:
+            raise RuntimeError(mla.mla_last_error())
+
+    settle_ms, settle_steps = settle(step, args.settle_ms, args.settle_max_ms, window=5)
+    warm = max(3, args.warmup // 5)
+    steps = max(10, args.steps // 4)
+    for i in range(warm):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
+    t_start = time.perf_counter()
+    for i in range(steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    score_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    select_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    ms_per_step = wall * 1e3 / steps
+    clock = clock_record()
+    rows = int(w.rows().sum())
+    alg_bytes = w.algorithmic_bytes()
+    # the score kernel alone: quantised part of every row (528 B), the FP8
+    # query, block-table entries and lengths
+    pages = int(((w.rows() + 63) // 64).sum())
+    score_bytes = rows * 528 + w.batch * w.s_q * w.h * 528 + 4 * pages + 4 * w.batch
+    # multiply-adds of the definition (every head); the kernels sum the
+    # heads first and do 512 per (token, row), far below any compute roof,
+    # so the score phase is bound by the cache stream
+    flops = w.flops()
+    roof = {"bound": "hbm", "achieved": score_bytes / (score_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    tr = traffic_record(w.name, "indexer")
+    roof["traffic"] = None if tr is None else tr["hbm_bytes_per_launch"]
+    roof["kernel"] = "index_score_kernel (with index_query_kernel: the mla_fp8_index_scores phase)"
+    roof["kernel_ms"] = score_ms
+    peaks = None if args.no_measured_peaks else measured_peaks()
+    cpu = None if args.no_cpu_baseline else index_cpu_baseline(w)
+    line = {
+        "metric": "FP8 top-k indexer GB/s (656-byte FP8 cache rows scored against an FP8 query of 128 heads, "
+                  "top-2048 per query token), % of roofline",
+        "value": alg_bytes / (ms_per_step * 1e-3) / 1e9, "unit": "GB/s", "n_gpus": 1, "steps": steps,
+        "warmup": warm, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8", "data": "synthetic",
+        "settle_ms": round(settle_ms, 1),
+        "settle_steps": settle_steps, "clock": clock,
+        "config": {"workload": w.name, "batch": w.batch, "s_q": w.s_q, "h": w.h, "seqlen": c["seqlen"],
+                   "topk": w.topk, "rows": rows, "definition_flops_per_step": flops,
+                   "algorithmic_bytes_per_step": alg_bytes, "score_kernel_algorithmic_bytes": score_bytes,
+                   "select_kernel_ms": select_ms},
+        "roofline": roof,
+        "measured_peaks": with_measured({"unit": "GB/s", "achieved": score_bytes / (score_ms * 1e-3) / 1e9},
+                                        peaks),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -420,6 +546,9 @@ def main():
         sys.exit(2)
     if args.kernel == "writer":
         bench_writer(args)
+        return
+    if args.kernel == "indexer":
+        bench_indexer(args)
         return
     if args.kernel == "prefill":
         bench_prefill(args)

@@ -34,11 +34,11 @@
  *   - Output.  indices[b][i][0..] holds the selected rows in ascending j,
  *     then -1 up to topk.  scores (optional) holds S of each selected row,
  *     -inf beside each -1.
- * The kernels compute each tile's code products with FP8 matrix
- * instructions accumulating in fp32 (every product of two e4m3 values is
- * exact in fp32), apply the scales and sum over tiles and heads in fp32,
- * and select on those fp32 scores.  For a given problem the results are the
- * same bits on every run.
+ * The sum over heads is linear, so the kernels take it first: per query
+ * token Qsum[d] = sum_h qs[h][t(d)] * e4m3(q[h][d]) (fp32, heads in order),
+ * then S_j = sum_t s_j[t] * sum_{d in tile t} e4m3(c_j[d]) * Qsum[d] (fp32;
+ * every code converts to fp32 exactly).  Selection is made on those fp32
+ * scores.  For a given problem the results are the same bits on every run.
  */
 #ifndef MLA_INDEX_H_
 #define MLA_INDEX_H_
@@ -52,7 +52,7 @@ extern "C" {
 typedef struct mla_index_problem {
   int32_t batch;             /* B >= 0 */
   int32_t s_q;               /* query tokens per sequence, >= 1 */
-  int32_t h;                 /* index heads, 1..256 */
+  int32_t h;                 /* index heads, 1..4096 */
   int32_t d;                 /* must be 512: the quantised part of a row */
   int32_t page_size;         /* must be 64 */
   int32_t num_pages;         /* pages in the pool, >= 1 */
@@ -63,8 +63,9 @@ typedef struct mla_index_problem {
 } mla_index_problem;
 
 /* Bytes of device workspace mla_fp8_index_top_k needs: fp32 scores of every
- * row a sequence can hold, [B, s_q, 64 * max_pages_per_seq].  Host values
- * only.  Errors: MLA_ERR_INVALID_ARGUMENT / MLA_ERR_UNSUPPORTED as for the
+ * row a sequence can hold, [B, s_q, 64 * max_pages_per_seq], then the
+ * head-summed query of every token, [B, s_q, 512] fp32 (each part 256-byte
+ * aligned).  Host values only.  Errors: MLA_ERR_INVALID_ARGUMENT / MLA_ERR_UNSUPPORTED as for the
  * call below. */
 mla_status mla_fp8_index_workspace_bytes(const mla_index_problem* p, size_t* bytes);
 
@@ -83,13 +84,29 @@ mla_status mla_fp8_index_workspace_bytes(const mla_index_problem* p, size_t* byt
  * All device memory is the caller's; two kernels run on `stream` (scores,
  * then selection) and the call returns without waiting for them.
  * Errors: MLA_ERR_INVALID_ARGUMENT (named argument), MLA_ERR_UNSUPPORTED
- * (d != 512, page_size != 64, h > 256, more than 65536 rows per sequence),
+ * (d != 512, page_size != 64, h > 4096, more than 65536 rows per sequence),
  * MLA_ERR_WORKSPACE_TOO_SMALL, MLA_ERR_HIP (launch failure). */
 mla_status mla_fp8_index_top_k(const mla_index_problem* p, const void* q_fp8, const float* q_scale,
                                const void* kv_pool, const int32_t* block_table,
                                const int32_t* cache_seqlens, void* workspace,
                                size_t workspace_bytes, int32_t* indices, float* scores,
                                void* stream);
+
+/* The two phases of mla_fp8_index_top_k, for callers that want every row's
+ * score or time the phases apart.  mla_fp8_index_scores writes the fp32 score
+ * S of every row of the pages that hold visible rows into the workspace,
+ * [B, s_q, 64 * max_pages_per_seq] (entries of rows that are not visible are
+ * unspecified); mla_fp8_index_select then writes indices and scores from it
+ * exactly as mla_fp8_index_top_k does.  Arguments, layouts and errors as
+ * there; the workspace must be the one the score phase filled, with the same
+ * problem and cache_seqlens. */
+mla_status mla_fp8_index_scores(const mla_index_problem* p, const void* q_fp8, const float* q_scale,
+                                const void* kv_pool, const int32_t* block_table,
+                                const int32_t* cache_seqlens, void* workspace,
+                                size_t workspace_bytes, void* stream);
+mla_status mla_fp8_index_select(const mla_index_problem* p, const int32_t* cache_seqlens,
+                                const void* workspace, size_t workspace_bytes, int32_t* indices,
+                                float* scores, void* stream);
 
 #ifdef __cplusplus
 }

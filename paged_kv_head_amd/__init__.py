@@ -25,6 +25,7 @@ __all__ = [
     "mla_decode_kernel_name", "mla_clock_probe", "shader_clock_mhz", "problem_for",
     "workload_tensors", "mla_decode_paged_noalloc", "NOALLOC_SCRATCH_BYTES", "IndexProblem",
     "mla_fp8_index_workspace_bytes", "mla_fp8_index_top_k", "index_problem_for", "index_tensors",
+    "mla_fp8_index_scores", "mla_fp8_index_select",
 ]
 
 MLA_KV_BF16 = 0
@@ -114,6 +115,8 @@ def _load():
     IP = ctypes.POINTER(IndexProblem)
     lib.mla_fp8_index_workspace_bytes.argtypes = [IP, ctypes.POINTER(SZ)]
     lib.mla_fp8_index_top_k.argtypes = [IP, P, P, P, P, P, P, SZ, P, P, P]
+    lib.mla_fp8_index_scores.argtypes = [IP, P, P, P, P, P, P, SZ, P]
+    lib.mla_fp8_index_select.argtypes = [IP, P, P, SZ, P, P, P]
     lib.mla_kv_quantize_fp8.argtypes = [I32, I32, I32, I32, I32, P, P, P, P, P]
     lib.mla_decode_check_inputs.argtypes = [PP, P, P, P, P]
     lib.mla_sparse_prefill_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32, ctypes.POINTER(SZ)]
@@ -124,7 +127,8 @@ def _load():
                "mla_decode_sparse_fp8", "mla_decode_combine", "mla_kv_quantize_fp8",
                "mla_sparse_prefill_workspace_bytes", "mla_sparse_prefill",
                "mla_decode_check_inputs", "mla_decode_paged_noalloc",
-               "mla_fp8_index_workspace_bytes", "mla_fp8_index_top_k"):
+               "mla_fp8_index_workspace_bytes", "mla_fp8_index_top_k", "mla_fp8_index_scores",
+               "mla_fp8_index_select"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.mla_last_error.argtypes = []
     lib.mla_last_error.restype = ctypes.c_char_p
@@ -269,6 +273,36 @@ def mla_fp8_index_top_k(p: IndexProblem, q_fp8, q_scale, kv_pool, block_table, c
         ctypes.byref(p), _ptr(q_fp8), _ptr(q_scale), _ptr(kv_pool), _ptr(block_table),
         _ptr(cache_seqlens), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _ptr(indices), _ptr(scores), _stream(stream)))
+
+
+def mla_fp8_index_scores(p: IndexProblem, q_fp8, q_scale, kv_pool, block_table, cache_seqlens,
+                         workspace, stream=None):
+    """Score phase of the indexer: fp32 scores [B, s_q, 64 * max_pages_per_seq]
+    into ``workspace`` (rows that are not visible: unspecified)."""
+    tokens = p.batch * p.s_q
+    _expect("q_fp8", q_fp8, torch.uint8, tokens * p.h * 512)
+    _expect("q_scale", q_scale, torch.float32, tokens * p.h * 4)
+    _expect("kv_pool", kv_pool, None, p.num_pages * p.page_size * 656)
+    _expect("block_table", block_table, torch.int32, p.batch * p.max_pages_per_seq)
+    _expect("cache_seqlens", cache_seqlens, torch.int32, p.batch)
+    _expect("workspace", workspace, None, mla_fp8_index_workspace_bytes(p), at_least=True)
+    _check(_load().mla_fp8_index_scores(
+        ctypes.byref(p), _ptr(q_fp8), _ptr(q_scale), _ptr(kv_pool), _ptr(block_table),
+        _ptr(cache_seqlens), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+
+
+def mla_fp8_index_select(p: IndexProblem, cache_seqlens, workspace, indices, scores=None, stream=None):
+    """Selection phase of the indexer, from a workspace the score phase filled."""
+    tokens = p.batch * p.s_q
+    _expect("cache_seqlens", cache_seqlens, torch.int32, p.batch)
+    _expect("indices", indices, torch.int32, tokens * p.topk)
+    if scores is not None:
+        _expect("scores", scores, torch.float32, tokens * p.topk)
+    _expect("workspace", workspace, None, mla_fp8_index_workspace_bytes(p), at_least=True)
+    _check(_load().mla_fp8_index_select(
+        ctypes.byref(p), _ptr(cache_seqlens), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(indices), _ptr(scores), _stream(stream)))
 
 
 def mla_decode_kernel_name(p: Problem) -> str:

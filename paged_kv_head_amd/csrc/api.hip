@@ -390,7 +390,7 @@ mla_status check_index_problem(const mla_index_problem* p, size_t* ws_bytes) {
   if (p->batch < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "batch: must be >= 0 (got %d)", p->batch);
   if (p->s_q < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "s_q: must be >= 1 (got %d)", p->s_q);
   if (p->h < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "h: must be >= 1 (got %d)", p->h);
-  if (p->h > 256) return fail(MLA_ERR_UNSUPPORTED, "h: at most 256 index heads (got %d)", p->h);
+  if (p->h > 4096) return fail(MLA_ERR_UNSUPPORTED, "h: at most 4096 index heads (got %d)", p->h);
   if (p->d != 512) return fail(MLA_ERR_UNSUPPORTED, "d: must be 512 (got %d)", p->d);
   if (p->page_size != mla::kPage) return fail(MLA_ERR_UNSUPPORTED, "page_size: must be 64 (got %d)", p->page_size);
   if (p->num_pages < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "num_pages: must be >= 1 (got %d)", p->num_pages);
@@ -410,7 +410,7 @@ mla_status check_index_problem(const mla_index_problem* p, size_t* ws_bytes) {
     return fail(MLA_ERR_UNSUPPORTED, "batch: batch * s_q = %lld query tokens exceed 2^31 - 1", tokens);
   if ((long long)p->batch * p->max_pages_per_seq > (1LL << 31) - 1)
     return fail(MLA_ERR_UNSUPPORTED, "block_table: more than 2^31 entries");
-  *ws_bytes = mla::align256((size_t)tokens * (size_t)n_max * sizeof(float));
+  *ws_bytes = mla::index_workspace_bytes(p->batch, p->s_q, p->max_pages_per_seq);
   return MLA_OK;
 }
 
@@ -426,40 +426,82 @@ mla_status mla_fp8_index_workspace_bytes(const mla_index_problem* p, size_t* byt
   return ok();
 }
 
+}  // extern "C"
+
+namespace {
+
+// The indexer's shared argument checks; fills the launch description.
+mla_status index_launch(const mla_index_problem* p, const void* q_fp8, const float* q_scale,
+                        const void* kv_pool, const int32_t* block_table, const int32_t* cache_seqlens,
+                        void* workspace, size_t workspace_bytes, int32_t* indices, float* scores,
+                        bool need_scores_in, bool need_select_out, mla::IndexLaunch* l) {
+  size_t need = 0;
+  MLA_CHECK(check_index_problem(p, &need));
+  if (need_scores_in) {
+    MLA_CHECK(check_ptr(q_fp8, "q_fp8", 16));
+    MLA_CHECK(check_ptr(q_scale, "q_scale", 16));
+    MLA_CHECK(check_ptr(kv_pool, "kv_pool", 16));
+    MLA_CHECK(check_ptr(block_table, "block_table", 4));
+  }
+  MLA_CHECK(check_ptr(cache_seqlens, "cache_seqlens", 4));
+  MLA_CHECK(check_ptr(workspace, "workspace", 16));
+  if (need_select_out) {
+    MLA_CHECK(check_ptr(indices, "indices", 4));
+    if (scores) MLA_CHECK(check_ptr(scores, "scores", 4));
+  }
+  if (workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes: %zu given, %zu needed", workspace_bytes, need);
+  l->batch = p->batch;
+  l->s_q = p->s_q;
+  l->h = p->h;
+  l->kpool = p->kpool;
+  l->is_causal = p->is_causal;
+  l->max_pages = p->max_pages_per_seq;
+  l->topk = p->topk;
+  l->q = (const uint8_t*)q_fp8;
+  l->qs = q_scale;
+  l->kv = (const uint8_t*)kv_pool;
+  l->block_table = block_table;
+  l->seqlens = cache_seqlens;
+  l->ws = (float*)workspace;
+  l->indices = indices;
+  l->scores = scores;
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 mla_status mla_fp8_index_top_k(const mla_index_problem* p, const void* q_fp8, const float* q_scale,
                                const void* kv_pool, const int32_t* block_table,
                                const int32_t* cache_seqlens, void* workspace,
                                size_t workspace_bytes, int32_t* indices, float* scores,
                                void* stream) {
-  size_t need = 0;
-  MLA_CHECK(check_index_problem(p, &need));
-  MLA_CHECK(check_ptr(q_fp8, "q_fp8", 16));
-  MLA_CHECK(check_ptr(q_scale, "q_scale", 16));
-  MLA_CHECK(check_ptr(kv_pool, "kv_pool", 16));
-  MLA_CHECK(check_ptr(block_table, "block_table", 4));
-  MLA_CHECK(check_ptr(cache_seqlens, "cache_seqlens", 4));
-  MLA_CHECK(check_ptr(workspace, "workspace", 16));
-  MLA_CHECK(check_ptr(indices, "indices", 4));
-  if (scores) MLA_CHECK(check_ptr(scores, "scores", 4));
-  if (workspace_bytes < need)
-    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes: %zu given, %zu needed", workspace_bytes, need);
   mla::IndexLaunch l;
-  l.batch = p->batch;
-  l.s_q = p->s_q;
-  l.h = p->h;
-  l.kpool = p->kpool;
-  l.is_causal = p->is_causal;
-  l.max_pages = p->max_pages_per_seq;
-  l.topk = p->topk;
-  l.q = (const uint8_t*)q_fp8;
-  l.qs = q_scale;
-  l.kv = (const uint8_t*)kv_pool;
-  l.block_table = block_table;
-  l.seqlens = cache_seqlens;
-  l.ws = (float*)workspace;
-  l.indices = indices;
-  l.scores = scores;
-  return hip_status(mla::launch_index(l, (hipStream_t)stream), "indexer kernel launch");
+  MLA_CHECK(index_launch(p, q_fp8, q_scale, kv_pool, block_table, cache_seqlens, workspace,
+                         workspace_bytes, indices, scores, true, true, &l));
+  MLA_CHECK(hip_status(mla::launch_index_scores(l, (hipStream_t)stream), "indexer score kernel launch"));
+  return hip_status(mla::launch_index_select(l, (hipStream_t)stream), "indexer selection kernel launch");
+}
+
+mla_status mla_fp8_index_scores(const mla_index_problem* p, const void* q_fp8, const float* q_scale,
+                                const void* kv_pool, const int32_t* block_table,
+                                const int32_t* cache_seqlens, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  mla::IndexLaunch l;
+  MLA_CHECK(index_launch(p, q_fp8, q_scale, kv_pool, block_table, cache_seqlens, workspace,
+                         workspace_bytes, nullptr, nullptr, true, false, &l));
+  return hip_status(mla::launch_index_scores(l, (hipStream_t)stream), "indexer score kernel launch");
+}
+
+mla_status mla_fp8_index_select(const mla_index_problem* p, const int32_t* cache_seqlens,
+                                const void* workspace, size_t workspace_bytes, int32_t* indices,
+                                float* scores, void* stream) {
+  mla::IndexLaunch l;
+  MLA_CHECK(index_launch(p, nullptr, nullptr, nullptr, nullptr, cache_seqlens, (void*)workspace,
+                         workspace_bytes, indices, scores, false, true, &l));
+  return hip_status(mla::launch_index_select(l, (hipStream_t)stream), "indexer selection kernel launch");
 }
 
 mla_status mla_decode_check_inputs(const mla_problem* p, const int32_t* block_table,

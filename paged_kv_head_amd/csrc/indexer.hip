@@ -3,30 +3,30 @@
 // 稀疏注意力（MSA）与 MLA 索引内核, mla_fp8_index_top_k).  The definition and
 // its readings are in include/mla_index.h.
 //
-// Two kernels on the caller's stream:
+// The sum over heads is linear, so it can be taken before the dot products:
+//   S_j = sum_t s_j[t] * sum_{d in tile t} e4m3(c_j[d]) * Qsum[d],
+//   Qsum[d] = sum_h qs[h][t(d)] * e4m3(q[h][d]),
+// which is the definition's value with the sums regrouped.  Scoring a row
+// then costs 512 multiply-adds per query token instead of 512 per head, and
+// the kernels are bound by the stream of cache rows.  Three kernels on the
+// caller's stream:
+//   index_query_kernel  Qsum of every query token (fp32, into the workspace);
 //   index_score_kernel  S[b][i][j] for every row j of the pages that hold
 //                       visible rows (fp32, into the workspace);
 //   index_topk_kernel   per (b, i): the top-k visible rows by S, ascending j,
 //                       -1 fill.
 //
-// Scores.  A workgroup (4 waves) owns one sequence b, a group of query
-// tokens (their heads padded to a multiple of 16 rows, at most 256 rows) and
-// a chunk of kChunkPages pages.  Q rows are the A operand of
-// v_mfma_f32_32x32x64_f8f6f4 (32 query rows x 64 dims of e4m3 codes, eight
-// VGPRs per lane; all 512 dims of the wave's row blocks stay in registers);
-// the cache rows are the B operand (64 dims x 32 keys), read from LDS.  The
-// fp32 result of a 128-dim tile (two MFMAs) is scaled per row by the query's
-// tile scale and summed over the lane's 16 rows, then scaled by the key's
-// tile scale: S_j += s_j[t] * sum_rows qs[row][t] * P_t[row][j].  A lane of
-// a 32x32 result holds 16 rows of one key: rows 0..15 of the block in
-// elements 0..7 (both lane halves), rows 16..31 in 8..15, so with heads
-// padded to 16 every half block belongs to one query token.
+// Scores.  A workgroup (8 waves) owns one sequence b, up to kMaxTokens of its
+// query tokens and a chunk of kChunkPages pages.  Sixteen lanes share a row:
+// lane c holds Qsum of dims [16c, 16c + 16) and [256 + 16c, 256 + 16c + 16)
+// of each token in registers, converts the row's codes of those dims to fp32
+// (exactly), takes its two partial dot products, scales each by its tile's
+// scale and sums with the other fifteen lanes in four DPP rotations.
 //
 // Cache rows are staged whole-page, 528 bytes per row (the 512 codes and
-// the four scales; the bf16 RoPE part is not read) at a 528-byte pitch:
-// 16 consecutive rows start on 16 distinct 16-byte bank groups, so the B
-// operand reads (16 rows at one offset) are conflict-free.  A page is 33
-// direct global->LDS copies of 1 KiB, spread over the four waves, into a
+// the four scales; the bf16 RoPE part is not read) at a 528-byte pitch, so
+// the 16 lanes of a row read 16 distinct 16-byte bank groups.  A page is 33
+// direct global->LDS copies of 1 KiB, spread over the eight waves, into a
 // ring of kRing pages kept kRing - 1 pages ahead.
 #include "../../include/mla_index.h"
 #include "internal.h"
@@ -34,20 +34,21 @@
 namespace mla {
 namespace {
 
-typedef int i32x8 __attribute__((ext_vector_type(8)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kIdxThreads = 256;
+constexpr int kIdxThreads = 512;         // 8 waves
+constexpr int kIdxWaves = kIdxThreads / 64;
 constexpr int kRowBytes = 656;           // cache row (MLA_KV_FP8_656)
 constexpr int kStageRow = 528;           // staged part: codes + scales
 constexpr int kStagePage = kPage * kStageRow;  // 33792
 constexpr int kPageCopies = kStagePage / 1024;  // 33
 constexpr int kRing = 4;
-constexpr int kMaxRows = 256;            // query rows of a workgroup
-constexpr int kCopiesPerWave = 8;        // waves 1..3; wave 0 issues 9
-static_assert(kPageCopies == 4 * kCopiesPerWave + 1, "copy split");
+constexpr int kCopiesPerWave = 4;        // waves 1..7; wave 0 issues 5
+static_assert(kPageCopies == kIdxWaves * kCopiesPerWave + 1, "copy split");
+constexpr int kMaxTokens = 4;            // query tokens of a workgroup
+constexpr int kChunkPages = 32;
 
 // Waits and barriers that leave the direct copies alone (the compiler does
 // not see them; see the decode kernel for the same rules).
@@ -69,30 +70,70 @@ __device__ inline uint32_t lds_u32(const void* p) {
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p);
 }
 
+// x rotated right by N lanes within each row of 16 lanes (DPP).
+template <int N>
+__device__ inline float row_ror(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + N, 0xF, 0xF, false));
+}
+// Sum over the 16 lanes of a DPP row, in every lane of it.
+__device__ inline float row_sum16(float x) {
+  x += row_ror<8>(x);
+  x += row_ror<4>(x);
+  x += row_ror<2>(x);
+  x += row_ror<1>(x);
+  return x;
+}
+
 struct IndexArgs {
-  int32_t batch, s_q, h, h16, tokens_per_group, groups, rows, row_blocks;
+  int32_t batch, s_q, h, tokens_per_group, groups;
   int32_t kpool, is_causal, max_pages, chunks, n_max;
   const uint8_t* q;
   const float* qs;
   const uint8_t* kv;
   const int32_t* block_table;
   const int32_t* seqlens;
-  float* ws;  // [B, s_q, n_max]
+  float* ws;    // scores [B, s_q, n_max]
+  float* qsum;  // [B, s_q, 512]
   int32_t topk;
   int32_t* indices;
   float* scores;
 };
 
-constexpr int kChunkPages = 32;
+// Qsum of query token blockIdx.x: thread t sums dims 2t and 2t + 1 over the
+// heads in head order, each head's code times its tile scale (fp32 fma).
+__global__ void __launch_bounds__(256) index_query_kernel(IndexArgs a) {
+  const int64_t tok = blockIdx.x;
+  const int d0 = 2 * (int)threadIdx.x;
+  const uint8_t* q = a.q + tok * a.h * 512 + d0;
+  const float* qs = a.qs + tok * a.h * 4 + (d0 >> 7);
+  float s0 = 0.f, s1 = 0.f;
+  for (int h = 0; h < a.h; ++h) {
+    const uint32_t two = *reinterpret_cast<const uint16_t*>(q + (int64_t)h * 512);
+    const auto f = __builtin_amdgcn_cvt_pk_f32_fp8(two, false);
+    const float sc = qs[(int64_t)h * 4];
+    s0 = __builtin_fmaf(sc, f[0], s0);
+    s1 = __builtin_fmaf(sc, f[1], s1);
+  }
+  *reinterpret_cast<f32x2*>(a.qsum + tok * 512 + d0) = f32x2{s0, s1};
+}
 
+// Four e4m3 codes (one 32-bit word) to fp32, exactly.
+__device__ inline void codes4(uint32_t w, float* out) {
+  const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+  const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+  out[0] = lo[0];
+  out[1] = lo[1];
+  out[2] = hi[0];
+  out[3] = hi[1];
+}
+
+template <int TG>
 __global__ void __launch_bounds__(kIdxThreads, 1) index_score_kernel(IndexArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kRing * kStagePage];
-  __shared__ __attribute__((aligned(16))) float qs_lds[4 * kMaxRows];  // [tile][row]
-  __shared__ __attribute__((aligned(16))) float part[16 * kPage];       // [16-row group][key]
 
   // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs; XCD x
   // takes a contiguous run of (sequence, group, chunk) items, so the chunks
-  // of one sequence share that XCD's L2 for their query.
+  // of one sequence share that XCD's L2.
   const int total = a.batch * a.groups * a.chunks;
   const int per_xcd = (total + 7) / 8;
   const int item = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
@@ -113,12 +154,15 @@ __global__ void __launch_bounds__(kIdxThreads, 1) index_score_kernel(IndexArgs a
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hh = lane >> 5;  // lane half
+  const int c = lane & 15;  // dim chunk of the lane
   cint32* bt = (cint32*)(a.block_table + (int64_t)b * a.max_pages);
 
-  // Direct copies of page p into ring slot p % kRing.  Copy c (of 33) fills
-  // LDS bytes [1024c, 1024c + 1024) of the slot: lane L's 16 bytes are byte
-  // o = 1024c + 16L of the staged page, row o / 528, offset o % 528.
+  // Direct copies of page p into ring slot p % kRing.  Copy k (of 33) fills
+  // LDS bytes [1024k, 1024k + 1024) of the slot: lane L's 16 bytes are byte
+  // o = 1024k + 16L of the staged page, row o / 528, offset o % 528.  Wave w
+  // issues copies w, w + 8, ..; wave 0 also the 33rd, which the waits below
+  // count as if it belonged to the next page (a slightly longer wait on
+  // wave 0, exact on the others).
   const uint32_t ring_base = lds_u32(ring);
   auto issue_page = [&](int p) {
     const int pg = bt[p];
@@ -126,48 +170,33 @@ __global__ void __launch_bounds__(kIdxThreads, 1) index_score_kernel(IndexArgs a
     const uint32_t slot = ring_base + (uint32_t)(p % kRing) * kStagePage;
     const int ncopy = wave == 0 ? kCopiesPerWave + 1 : kCopiesPerWave;
     for (int k = 0; k < ncopy; ++k) {
-      const int c = wave + 4 * k;
-      const uint32_t o = 1024u * c + 16u * lane;
+      const int cp = wave + kIdxWaves * k;
+      const uint32_t o = 1024u * cp + 16u * lane;
       const uint32_t r = (o * 7944u) >> 22;  // o / 528 for o < 33792
       const uint32_t voff = r * kRowBytes + (o - r * kStageRow);
-      const uint32_t m0 = __builtin_amdgcn_readfirstlane(slot + 1024u * c);
+      const uint32_t m0 = __builtin_amdgcn_readfirstlane(slot + 1024u * cp);
       asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                    :: "v"(voff), "s"(src), "s"(m0) : "memory", "m0");
     }
-    // wave 0's ninth copy is accounted for as if it were one of the next
-    // page's: waiting for all but 2 * kCopiesPerWave copies then waits for a
-    // little more than the page on wave 0, exactly the page on the others
   };
 
-  // Query: scales into LDS ([tile][row], 0 for padding rows), codes of the
-  // wave's row blocks (w and w + 4) into registers.
-  for (int rr = tid; rr < kMaxRows; rr += kIdxThreads) {
-    const int tl = rr / a.h16, head = rr % a.h16;
-    f32x4 v = {0.f, 0.f, 0.f, 0.f};
-    if (rr < a.rows && tl < ntok && head < a.h)
-      v = *reinterpret_cast<const f32x4*>(a.qs + (((int64_t)b * a.s_q + i0 + tl) * a.h + head) * 4);
+  // Qsum of the lane's 32 dims for each token of the group (0 past ntok).
+  float qlo[TG][16], qhi[TG][16];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) qs_lds[t * kMaxRows + rr] = v[t];
-  }
-  i32x8 qf[2][8];
+  for (int tk = 0; tk < TG; ++tk) {
+    const float* qv = a.qsum + ((int64_t)b * a.s_q + i0 + min(tk, ntok - 1)) * 512;
 #pragma unroll
-  for (int lb = 0; lb < 2; ++lb) {
-    const int rb = wave + 4 * lb;
-    const int rr = 32 * rb + (lane & 31);
-    const int tl = rr / a.h16, head = rr % a.h16;
-    const bool ok = rb < a.row_blocks && rr < a.rows && tl < ntok && head < a.h;
-    const uint8_t* qrow = a.q + (((int64_t)b * a.s_q + i0 + (ok ? tl : 0)) * a.h + (ok ? head : 0)) * 512 + 32 * hh;
+    for (int e4 = 0; e4 < 4; ++e4) {
+      f32x4 lo = *reinterpret_cast<const f32x4*>(qv + 16 * c + 4 * e4);
+      f32x4 hi = *reinterpret_cast<const f32x4*>(qv + 256 + 16 * c + 4 * e4);
+      if (tk >= ntok) lo = hi = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      i32x4 lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
-      if (ok) {
-        lo = *reinterpret_cast<const i32x4*>(qrow + 64 * s);
-        hi = *reinterpret_cast<const i32x4*>(qrow + 64 * s + 16);
+      for (int e = 0; e < 4; ++e) {
+        qlo[tk][4 * e4 + e] = lo[e];
+        qhi[tk][4 * e4 + e] = hi[e];
       }
-      qf[lb][s] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
   }
-  const bool has0 = wave < a.row_blocks, has1 = wave + 4 < a.row_blocks;  // wave-uniform
   // the query loads must land before the first copy is counted
   __builtin_amdgcn_s_waitcnt(0);
   asm volatile("" ::: "memory");
@@ -187,69 +216,35 @@ __global__ void __launch_bounds__(kIdxThreads, 1) index_score_kernel(IndexArgs a
     if (k + kRing - 1 < npages) issue_page(p + kRing - 1);
 
     const uint8_t* st = ring + (p % kRing) * kStagePage;
-    float acc[2][2][2] = {};  // [local row block][key block][row half]
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      f32x4 qv[2][4];
+    for (int m = 0; m < 2; ++m) {
+      const int row = 8 * wave + 4 * m + (lane >> 4);
+      const uint8_t* kr = st + row * kStageRow;
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(kr + 16 * c);
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(kr + 256 + 16 * c);
+      const f32x4 sc = *reinterpret_cast<const f32x4*>(kr + 512);
+      const float s_lo = c < 8 ? sc[0] : sc[1];  // tile of dims 16c..
+      const float s_hi = c < 8 ? sc[2] : sc[3];  // tile of dims 256 + 16c..
+      float klo[16], khi[16];
 #pragma unroll
-      for (int lb = 0; lb < 2; ++lb)
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq)
-          qv[lb][gq] = *reinterpret_cast<const f32x4*>(
-              &qs_lds[t * kMaxRows + 32 * (wave + 4 * lb) + 8 * gq + 4 * hh]);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const uint8_t* krow = st + (32 * kb + (lane & 31)) * kStageRow;
-        const float ks = *reinterpret_cast<const float*>(krow + 512 + 4 * t);
-        i32x8 kf[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const i32x4 lo = *reinterpret_cast<const i32x4*>(krow + 128 * t + 64 * u + 32 * hh);
-          const i32x4 hi = *reinterpret_cast<const i32x4*>(krow + 128 * t + 64 * u + 32 * hh + 16);
-          kf[u] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        }
-#pragma unroll
-        for (int lb = 0; lb < 2; ++lb) {
-          if ((lb == 0 && !has0) || (lb == 1 && !has1)) continue;
-          f32x16 pr = {};
-          pr = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qf[lb][2 * t], kf[0], pr, 0, 0, 0, 0, 0, 0);
-          pr = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qf[lb][2 * t + 1], kf[1], pr, 0, 0, 0, 0, 0, 0);
-          float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-          for (int v = 0; v < 8; ++v) s0 = __builtin_fmaf(qv[lb][v >> 2][v & 3], pr[v], s0);
-#pragma unroll
-          for (int v = 8; v < 16; ++v) s1 = __builtin_fmaf(qv[lb][v >> 2][v & 3], pr[v], s1);
-          acc[lb][kb][0] = __builtin_fmaf(ks, s0, acc[lb][kb][0]);
-          acc[lb][kb][1] = __builtin_fmaf(ks, s1, acc[lb][kb][1]);
-        }
+      for (int w = 0; w < 4; ++w) {
+        codes4(lo[w], klo + 4 * w);
+        codes4(hi[w], khi + 4 * w);
       }
-    }
-    // Both lane halves hold 8 of the 16 rows of a half block: add them, then
-    // lanes 0..31 publish row half 0 and lanes 32..63 row half 1.
+      float v[TG];
 #pragma unroll
-    for (int lb = 0; lb < 2; ++lb) {
-      if ((lb == 0 && !has0) || (lb == 1 && !has1)) continue;
+      for (int tk = 0; tk < TG; ++tk) {
+        float p1 = 0.f, p2 = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        float v[2];
-#pragma unroll
-        for (int rh = 0; rh < 2; ++rh) {
-          const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[lb][kb][rh]),
-                                                          __float_as_uint(acc[lb][kb][rh]), false, false);
-          v[rh] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+        for (int e = 0; e < 16; ++e) {
+          p1 = __builtin_fmaf(qlo[tk][e], klo[e], p1);
+          p2 = __builtin_fmaf(qhi[tk][e], khi[e], p2);
         }
-        const int grp = 2 * (wave + 4 * lb) + hh;
-        part[grp * kPage + 32 * kb + (lane & 31)] = hh ? v[1] : v[0];
+        v[tk] = row_sum16(__builtin_fmaf(s_lo, p1, s_hi * p2));
       }
-    }
-    IDX_BARRIER();
-    // Sum the 16-row groups of each token and store the page's scores.
-    const int gpt = a.h16 / 16;  // 16-row groups per token
-    for (int e = tid; e < ntok * kPage; e += kIdxThreads) {
-      const int tl = e / kPage, key = e % kPage;
-      float sum = 0.f;
-      for (int q = 0; q < gpt; ++q) sum += part[(tl * gpt + q) * kPage + key];
-      ws_b[(int64_t)tl * a.n_max + p * kPage + key] = sum;
+#pragma unroll
+      for (int tk = 0; tk < TG; ++tk)
+        if (c == tk && tk < ntok) ws_b[(int64_t)tk * a.n_max + p * kPage + row] = v[tk];
     }
   }
 }
@@ -384,22 +379,19 @@ __global__ void __launch_bounds__(kTopkThreads, 1) index_topk_kernel(IndexArgs a
 
 }  // namespace
 
-bool index_shape(int32_t h, int32_t s_q, int32_t* h16, int32_t* tokens_per_group, int32_t* groups) {
-  if (h < 1 || h > kMaxRows) return false;
-  *h16 = (h + 15) / 16 * 16;
-  *tokens_per_group = max(1, min(s_q, kMaxRows / *h16));
-  *groups = (s_q + *tokens_per_group - 1) / *tokens_per_group;
-  return true;
+void index_groups(int32_t s_q, int32_t* tokens_per_group, int32_t* groups) {
+  *groups = (s_q + kMaxTokens - 1) / kMaxTokens;
+  *tokens_per_group = (s_q + *groups - 1) / *groups;
 }
 
-hipError_t launch_index(const IndexLaunch& l, hipStream_t stream) {
+namespace {
+
+IndexArgs index_args(const IndexLaunch& l) {
   IndexArgs a;
   a.batch = l.batch;
   a.s_q = l.s_q;
   a.h = l.h;
-  index_shape(l.h, l.s_q, &a.h16, &a.tokens_per_group, &a.groups);
-  a.rows = a.tokens_per_group * a.h16;
-  a.row_blocks = (a.rows + 31) / 32;
+  index_groups(l.s_q, &a.tokens_per_group, &a.groups);
   a.kpool = l.kpool;
   a.is_causal = l.is_causal;
   a.max_pages = l.max_pages;
@@ -411,15 +403,40 @@ hipError_t launch_index(const IndexLaunch& l, hipStream_t stream) {
   a.block_table = l.block_table;
   a.seqlens = l.seqlens;
   a.ws = l.ws;
+  a.qsum = l.ws + (int64_t)l.batch * l.s_q * a.n_max;
   a.topk = l.topk;
   a.indices = l.indices;
   a.scores = l.scores;
+  return a;
+}
+
+}  // namespace
+
+size_t index_workspace_bytes(int32_t batch, int32_t s_q, int32_t max_pages) {
+  const size_t tokens = (size_t)batch * (size_t)s_q;
+  return align256(tokens * (size_t)max_pages * kPage * sizeof(float)) + align256(tokens * 512 * sizeof(float));
+}
+
+hipError_t launch_index_scores(const IndexLaunch& l, hipStream_t stream) {
   if (l.batch == 0) return hipSuccess;
-  const int total = a.batch * a.groups * a.chunks;
-  const int grid = (total + 7) / 8 * 8;
-  hipLaunchKernelGGL(index_score_kernel, dim3(grid), dim3(kIdxThreads), 0, stream, a);
+  const IndexArgs a = index_args(l);
+  hipLaunchKernelGGL(index_query_kernel, dim3(a.batch * a.s_q), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  const int total = a.batch * a.groups * a.chunks;
+  const int grid = (total + 7) / 8 * 8;
+  switch (a.tokens_per_group) {
+    case 1: hipLaunchKernelGGL(index_score_kernel<1>, dim3(grid), dim3(kIdxThreads), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(index_score_kernel<2>, dim3(grid), dim3(kIdxThreads), 0, stream, a); break;
+    case 3: hipLaunchKernelGGL(index_score_kernel<3>, dim3(grid), dim3(kIdxThreads), 0, stream, a); break;
+    default: hipLaunchKernelGGL(index_score_kernel<4>, dim3(grid), dim3(kIdxThreads), 0, stream, a); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_index_select(const IndexLaunch& l, hipStream_t stream) {
+  if (l.batch == 0) return hipSuccess;
+  const IndexArgs a = index_args(l);
   hipLaunchKernelGGL(index_topk_kernel, dim3(a.batch * a.s_q), dim3(kTopkThreads), 0, stream, a);
   return hipGetLastError();
 }

@@ -89,14 +89,19 @@ struct IndexLaunch {
   const uint8_t* kv;
   const int32_t* block_table;
   const int32_t* seqlens;
-  float* ws;  // fp32 scores [batch, s_q, 64 * max_pages]
+  float* ws;  // index_workspace_bytes: scores, then head-summed queries
   int32_t* indices;
   float* scores;  // may be null
 };
-// Heads padded to a multiple of 16 rows, query tokens per workgroup and
-// workgroups per sequence for h heads; false when h is out of range.
-bool index_shape(int32_t h, int32_t s_q, int32_t* h16, int32_t* tokens_per_group, int32_t* groups);
-hipError_t launch_index(const IndexLaunch& l, hipStream_t stream);
+// Query tokens per score workgroup and workgroups per sequence.
+void index_groups(int32_t s_q, int32_t* tokens_per_group, int32_t* groups);
+// Workspace of the indexer: fp32 scores [batch, s_q, 64 * max_pages], then
+// the head-summed queries [batch, s_q, 512] (fp32), each 256-byte aligned.
+size_t index_workspace_bytes(int32_t batch, int32_t s_q, int32_t max_pages);
+// Scores of every row of the pages holding visible rows into l.ws, then the
+// selection from l.ws (the two kernels of the indexer).
+hipError_t launch_index_scores(const IndexLaunch& l, hipStream_t stream);
+hipError_t launch_index_select(const IndexLaunch& l, hipStream_t stream);
 
 // Sparse prefill runs the decode path over chunks of at most this many query
 // tokens (each a decode unit), which bounds the split workspace.

@@ -309,7 +309,7 @@ def call_index(p, ws_bytes=1 << 40, **ptrs):
 
 
 @pytest.mark.parametrize("field,value,status", [
-    ("h", 0, mla.MLA_ERR_INVALID_ARGUMENT), ("h", 257, mla.MLA_ERR_UNSUPPORTED),
+    ("h", 0, mla.MLA_ERR_INVALID_ARGUMENT), ("h", 4097, mla.MLA_ERR_UNSUPPORTED),
     ("d", 576, mla.MLA_ERR_UNSUPPORTED), ("page_size", 32, mla.MLA_ERR_UNSUPPORTED),
     ("max_pages_per_seq", 1025, mla.MLA_ERR_UNSUPPORTED), ("topk", 0, mla.MLA_ERR_INVALID_ARGUMENT),
     ("topk", 257, mla.MLA_ERR_INVALID_ARGUMENT), ("kpool", 0, mla.MLA_ERR_INVALID_ARGUMENT),
@@ -331,5 +331,5 @@ def test_index_pointers_and_workspace_checked():
         assert name in mla.mla_last_error()
     assert call_index(p, q=FAKE + 4) == mla.MLA_ERR_INVALID_ARGUMENT  # alignment
     need = mla.mla_fp8_index_workspace_bytes(p)
-    assert need == 2 * 2 * 4 * 64 * 4  # fp32 scores [B, s_q, 64 * max_pages]
+    assert need == 2 * 2 * 4 * 64 * 4 + 2 * 2 * 512 * 4  # fp32 scores [B, s_q, 64 * max_pages], Qsum [B, s_q, 512]
     assert call_index(p, ws_bytes=need - 1) == mla.MLA_ERR_WORKSPACE_TOO_SMALL

@@ -27,7 +27,8 @@ from paged_kv_head_amd import build as build_mod
 HIPCC = build_mod.HIPCC
 DECODE = os.path.join(build_mod.CSRC, "decode.hip")
 INDEXER = os.path.join(build_mod.CSRC, "indexer.hip")
-SCORE_KERNEL = "_ZN3mla12_GLOBAL__N_118index_score_kernelENS0_9IndexArgsE"
+SCORE_KERNEL = "_ZN3mla12_GLOBAL__N_118index_score_kernelILi{}EEEvNS0_9IndexArgsE"
+QUERY_KERNEL = "_ZN3mla12_GLOBAL__N_118index_query_kernelENS0_9IndexArgsE"
 TOPK_KERNEL = "_ZN3mla12_GLOBAL__N_117index_topk_kernelENS0_9IndexArgsE"
 KERNELS = {  # (cache format, sparse) -> mangled name
     (0, False): "_ZN3mla12_GLOBAL__N_113decode_kernelILi0ELb0EEEvNS_10DecodeArgsE",
@@ -166,18 +167,19 @@ def test_lds_fits_one_workgroup_per_cu(asm):
 
 
 def test_indexer_page_loop_waits_only_for_its_copies(asm_indexer):
-    """The score kernel's page loop (outermost loop) waits on vector memory
+    """Each score kernel's page loop (outermost loop) waits on vector memory
     only through its three explicit waits (two pages ahead, one, none), and
-    neither indexer kernel spills or touches memory through flat pointers
-    in a loop."""
-    body = function_body(asm_indexer, SCORE_KERNEL)
-    depth = loop_blocks(body)
-    page_loop = instructions([l for l, d in zip(body, depth) if d == 1])
-    counts = sorted(int(re.search(r"vmcnt\((\d+)\)", t).group(1)) for t in page_loop
-                    if t.startswith("s_waitcnt") and "vmcnt" in t)
-    assert counts == [0, 8, 16], counts
-    assert sum("mfma" in t for t in page_loop) == 32  # 4 tiles x 2 key blocks x 2 row blocks x 2
-    for name in (SCORE_KERNEL, TOPK_KERNEL):
+    no indexer kernel spills or touches memory through flat pointers in a
+    loop."""
+    for tg in (1, 2, 3, 4):
+        body = function_body(asm_indexer, SCORE_KERNEL.format(tg))
+        depth = loop_blocks(body)
+        page_loop = instructions([l for l, d in zip(body, depth) if d == 1])
+        counts = sorted(int(re.search(r"vmcnt\((\d+)\)", t).group(1)) for t in page_loop
+                        if t.startswith("s_waitcnt") and "vmcnt" in t)
+        assert counts == [0, 4, 8], (tg, counts)
+        assert sum("row_ror" in t for t in page_loop) == 8 * tg  # 2 rows x 4 rotations per token
+    for name in [SCORE_KERNEL.format(t) for t in (1, 2, 3, 4)] + [TOPK_KERNEL, QUERY_KERNEL]:
         b = function_body(asm_indexer, name)
         d = loop_blocks(b)
         in_loops = instructions([l for l, x in zip(b, d) if x >= 1])
