@@ -413,7 +413,7 @@ INDEX_WORKLOAD = dict(name="index_b128_sq2_h128_l65536_topk2048", batch=128, s_q
                       topk=2048, seed=88)
 
 
-def index_cpu_baseline(w, n_tokens=8, min_seconds=10.0, max_reps=6):
+def index_cpu_baseline(w, n_tokens=16, min_seconds=10.0, max_reps=8):
     """The indexer oracle (numpy fp64) on a bounded sample of query tokens;
     value in GB/s of the sample's algorithmic bytes (its share of the cache
     rows, query and indices)."""

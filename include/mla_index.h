@@ -35,7 +35,7 @@
  *     then -1 up to topk.  scores (optional) holds S of each selected row,
  *     -inf beside each -1.
  * The sum over heads is linear, so the kernels take it first: per query
- * token Qsum[d] = sum_h qs[h][t(d)] * e4m3(q[h][d]) (fp32, heads in order),
+ * token Qsum[d] = sum_h qs[h][t(d)] * e4m3(q[h][d]) (fp32, in a fixed order),
  * then S_j = sum_t s_j[t] * sum_{d in tile t} e4m3(c_j[d]) * Qsum[d] (fp32;
  * every code converts to fp32 exactly).  Selection is made on those fp32
  * scores.  For a given problem the results are the same bits on every run.

@@ -99,24 +99,6 @@ struct IndexArgs {
   float* scores;
 };
 
-// Qsum of query token blockIdx.x: thread t sums dims 2t and 2t + 1 over the
-// heads in head order, each head's code times its tile scale (fp32 fma).
-__global__ void __launch_bounds__(256) index_query_kernel(IndexArgs a) {
-  const int64_t tok = blockIdx.x;
-  const int d0 = 2 * (int)threadIdx.x;
-  const uint8_t* q = a.q + tok * a.h * 512 + d0;
-  const float* qs = a.qs + tok * a.h * 4 + (d0 >> 7);
-  float s0 = 0.f, s1 = 0.f;
-  for (int h = 0; h < a.h; ++h) {
-    const uint32_t two = *reinterpret_cast<const uint16_t*>(q + (int64_t)h * 512);
-    const auto f = __builtin_amdgcn_cvt_pk_f32_fp8(two, false);
-    const float sc = qs[(int64_t)h * 4];
-    s0 = __builtin_fmaf(sc, f[0], s0);
-    s1 = __builtin_fmaf(sc, f[1], s1);
-  }
-  *reinterpret_cast<f32x2*>(a.qsum + tok * 512 + d0) = f32x2{s0, s1};
-}
-
 // Four e4m3 codes (one 32-bit word) to fp32, exactly.
 __device__ inline void codes4(uint32_t w, float* out) {
   const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
@@ -125,6 +107,55 @@ __device__ inline void codes4(uint32_t w, float* out) {
   out[1] = lo[1];
   out[2] = hi[0];
   out[3] = hi[1];
+}
+
+// Qsum of query token blockIdx.x.  Lane l of wave w holds dims 8l .. 8l + 7
+// (one 8-byte load per head row) and sums heads w, w + 4, .. in head order;
+// the four wave partials are added in wave order through LDS.
+__global__ void __launch_bounds__(256) index_query_kernel(IndexArgs a) {
+  __shared__ __attribute__((aligned(16))) float part[4][512];
+  const int64_t tok = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int d0 = 8 * lane;
+  const uint8_t* q = a.q + tok * a.h * 512 + d0;
+  const float* qs = a.qs + tok * a.h * 4 + (d0 >> 7);
+  float acc[8] = {};
+  int h = wave;
+  // four heads in flight per step: independent loads, then the fmas in order
+  for (; h + 12 < a.h; h += 16) {
+    uint64_t codes[4];
+    float sc[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      codes[u] = *reinterpret_cast<const uint64_t*>(q + (int64_t)(h + 4 * u) * 512);
+      sc[u] = qs[(int64_t)(h + 4 * u) * 4];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      float f[8];
+      codes4((uint32_t)codes[u], f);
+      codes4((uint32_t)(codes[u] >> 32), f + 4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(sc[u], f[e], acc[e]);
+    }
+  }
+  for (; h < a.h; h += 4) {
+    const uint64_t c8 = *reinterpret_cast<const uint64_t*>(q + (int64_t)h * 512);
+    const float sc = qs[(int64_t)h * 4];
+    float f[8];
+    codes4((uint32_t)c8, f);
+    codes4((uint32_t)(c8 >> 32), f + 4);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(sc, f[e], acc[e]);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) part[wave][d0 + e] = acc[e];
+  __syncthreads();
+  const int d = 2 * (int)threadIdx.x;
+  f32x2 r;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) r[e] = ((part[0][d + e] + part[1][d + e]) + part[2][d + e]) + part[3][d + e];
+  *reinterpret_cast<f32x2*>(a.qsum + tok * 512 + d) = r;
 }
 
 template <int TG>
@@ -260,9 +291,12 @@ __device__ inline uint32_t score_key(float f) {
 constexpr int kTopkThreads = 1024;
 constexpr int kPerThread = 64;  // rows per thread: 65536 per sequence at most
 
-// Workgroup sum of one int per wave (16 waves), through LDS.
-__device__ inline int block_sum16(int wave_value, int* red, int wave, int lane) {
-  if (lane == 0) red[wave] = wave_value;
+// Workgroup sum of one int per thread: a butterfly within each wave, then
+// the 16 wave sums through LDS (in wave order).
+__device__ inline int block_sum(int v, int* red, int wave, int lane) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  if (lane == 0) red[wave] = v;
   __syncthreads();
   int s = 0;
 #pragma unroll
@@ -302,13 +336,13 @@ __global__ void __launch_bounds__(kTopkThreads, 1) index_topk_kernel(IndexArgs a
       const uint32_t cand = T | (1u << bit);
       int c = 0;
 #pragma unroll
-      for (int e = 0; e < kPerThread; ++e) c += __builtin_popcountll(__builtin_amdgcn_ballot_w64(key[e] >= cand));
-      if (block_sum16(c, red, wave, lane) >= k) T = cand;
+      for (int e = 0; e < kPerThread; ++e) c += key[e] >= cand ? 1 : 0;
+      if (block_sum(c, red, wave, lane) >= k) T = cand;
     }
     int cg = 0;
 #pragma unroll
-    for (int e = 0; e < kPerThread; ++e) cg += __builtin_popcountll(__builtin_amdgcn_ballot_w64(key[e] > T));
-    need_eq = k - block_sum16(cg, red, wave, lane);
+    for (int e = 0; e < kPerThread; ++e) cg += key[e] > T ? 1 : 0;
+    need_eq = k - block_sum(cg, red, wave, lane);
   }
 
   // Ties at T go to the smallest rows: rank them in row order (a thread's
