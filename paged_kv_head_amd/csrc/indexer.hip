@@ -291,118 +291,197 @@ __device__ inline uint32_t score_key(float f) {
 constexpr int kTopkThreads = 1024;
 constexpr int kPerThread = 64;  // rows per thread: 65536 per sequence at most
 
-// Workgroup sum of one int per thread: a butterfly within each wave, then
-// the 16 wave sums through LDS (in wave order).
-__device__ inline int block_sum(int v, int* red, int wave, int lane) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  if (lane == 0) red[wave] = v;
+// Inclusive prefix sum over the 64 lanes of a wave in six DPP adds: within
+// each row of 16 lanes by shifts of 1, 2, 4 and 8, then the last lane of
+// rows 0 and 2 into rows 1 and 3 (row_bcast:15) and lane 31 into rows 2 and
+// 3 (row_bcast:31).
+__device__ inline int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return x;
+}
+__device__ inline int wave_total(int x) { return __builtin_amdgcn_readlane(wave_incl_scan(x), 63); }
+
+// Workgroup sum of one int per thread: the wave sums, then the 16 of them
+// through LDS (in wave order).  The two halves of red[] alternate between
+// calls, so one barrier per call suffices: a wave can write the other half
+// while slower waves still read this one, and a half is written again only
+// after a later barrier that every reader of it has passed.
+__device__ inline int block_sum(int v, int* red, int& parity, int wave, int lane) {
+  const int t = wave_total(v);
+  int* r = red + parity * (kTopkThreads / 64);
+  parity ^= 1;
+  if (lane == 0) r[wave] = t;
   __syncthreads();
   int s = 0;
 #pragma unroll
-  for (int w = 0; w < kTopkThreads / 64; ++w) s += red[w];
-  __syncthreads();
+  for (int w = 0; w < kTopkThreads / 64; ++w) s += r[w];
   return s;
 }
 
+// Bits of the threshold found over all rows before the candidates that
+// share them are compacted into LDS, and the most candidates compacted.
+constexpr int kTopBits = 12;
+constexpr int kLowBits = 32 - kTopBits;
+constexpr int kMaxCand = 8192;
+constexpr int kWaveRows = 64 * kPerThread;  // rows of one wave: 4096
+constexpr int kQuads = kPerThread / 4;       // 16-byte loads per lane
+
+// Selection of the top-k rows of one query token.  Wave w owns rows
+// [4096w, 4096w + 4096); its load e4 covers rows 4096w + 256e4 + [0, 256),
+// four per lane (rows 4l .. 4l + 3 of the 256), so every load reads 1 KiB
+// contiguous and row order is (wave, e4, lane, element).  Ranks in row order
+// come from lane prefix sums per load plus the totals of the waves before.
 __global__ void __launch_bounds__(kTopkThreads, 1) index_topk_kernel(IndexArgs a) {
-  __shared__ int red[kTopkThreads / 64];
-  __shared__ int wave_base[kTopkThreads / 64];
+  __shared__ int red[2 * (kTopkThreads / 64)];
+  __shared__ int wred[kTopkThreads / 64];
+  __shared__ uint32_t cand[kMaxCand];  // low bits of the keys that share the threshold's top bits
+  __shared__ uint32_t t_low;           // low bits of the threshold, found by wave 0
+  int parity = 0;
   const int row = blockIdx.x;  // (b, i)
   const int b = row / a.s_q, i = row % a.s_q;
   const int L = a.seqlens[b];
   const int n = min(visible_rows(L, a.s_q, i, a.kpool, a.is_causal), a.n_max);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* src = a.ws + (int64_t)row * a.n_max;
-  const int j0 = tid * kPerThread;
+  const int jw = kWaveRows * wave + 4 * lane;  // row of element (e4, q): jw + 256 e4 + q
 
   uint32_t key[kPerThread];
 #pragma unroll
-  for (int e4 = 0; e4 < kPerThread / 4; ++e4) {
-    const int j = j0 + 4 * e4;
+  for (int e4 = 0; e4 < kQuads; ++e4) {
+    const int j = jw + 256 * e4;
     f32x4 v = {0.f, 0.f, 0.f, 0.f};
-    if (j < n) v = *reinterpret_cast<const f32x4*>(src + j);  // rows past n are never read
+    if (j < n) v = *reinterpret_cast<const f32x4*>(src + j);  // j + 3 < n_max: inside the row
 #pragma unroll
     for (int q = 0; q < 4; ++q) key[4 * e4 + q] = (j + q < n) ? score_key(v[q]) : 0u;
   }
 
+  // Sum over the waves before this one of one wave-uniform value per wave.
+  auto waves_before = [&](int wave_value) {
+    if (lane == 0) wred[wave] = wave_value;
+    __syncthreads();
+    int s0 = 0;
+    for (int w = 0; w < wave; ++w) s0 += wred[w];
+    __syncthreads();
+    return s0;
+  };
+
   // Threshold: the largest T with #{key >= T} >= k (n > k), else take all.
+  // Bisection, one bit at a time from the top.  After the top kTopBits bits
+  // the keys that still share them are usually few: they are compacted into
+  // LDS and the low bits are found on them alone (the keys above their band
+  // counted once); a band too wide for LDS keeps bisecting over all rows.
   const int k = a.topk;
   uint32_t T = 1u;
   int need_eq = 0;
   if (n > k) {
     T = 0u;
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = T | (1u << bit);
+    for (int bit = 31; bit >= kLowBits; --bit) {
+      const uint32_t c1 = T | (1u << bit);
       int c = 0;
 #pragma unroll
-      for (int e = 0; e < kPerThread; ++e) c += key[e] >= cand ? 1 : 0;
-      if (block_sum(c, red, wave, lane) >= k) T = cand;
+      for (int e = 0; e < kPerThread; ++e) c += key[e] >= c1 ? 1 : 0;
+      if (block_sum(c, red, parity, wave, lane) >= k) T = c1;
+    }
+    constexpr uint32_t kBand = 1u << kLowBits;
+    int in_band = 0, above = 0;
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+      in_band += (key[e] - T) < kBand ? 1 : 0;  // T <= key < T + kBand (T <= 2^32 - kBand: no wrap)
+      above += key[e] > (T | (kBand - 1)) ? 1 : 0;
+    }
+    const int m = block_sum(in_band, red, parity, wave, lane);
+    const int above_all = block_sum(above, red, parity, wave, lane);
+    if (m <= kMaxCand) {
+      // compaction, in any order: the lane's slots after the lanes and waves before it
+      const int incl = wave_incl_scan(in_band);
+      int at = waves_before(__builtin_amdgcn_readlane(incl, 63)) + incl - in_band;
+#pragma unroll
+      for (int e = 0; e < kPerThread; ++e)
+        if ((key[e] - T) < kBand) cand[at++] = key[e] - T;
+      __syncthreads();
+      // the low bits on the m candidates, by wave 0 alone (no barriers)
+      if (wave == 0) {
+        uint32_t U = 0u;
+        for (int bit = kLowBits - 1; bit >= 0; --bit) {
+          const uint32_t c1 = U | (1u << bit);
+          int c = 0;
+          for (int ci = lane; ci < m; ci += 64) c += cand[ci] >= c1 ? 1 : 0;
+          if (wave_total(c) + above_all >= k) U = c1;
+        }
+        if (lane == 0) t_low = U;
+      }
+      __syncthreads();
+      T += t_low;
+    } else {
+      for (int bit = kLowBits - 1; bit >= 0; --bit) {
+        const uint32_t c1 = T | (1u << bit);
+        int c = 0;
+#pragma unroll
+        for (int e = 0; e < kPerThread; ++e) c += key[e] >= c1 ? 1 : 0;
+        if (block_sum(c, red, parity, wave, lane) >= k) T = c1;
+      }
     }
     int cg = 0;
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e) cg += key[e] > T ? 1 : 0;
-    need_eq = k - block_sum(cg, red, wave, lane);
+    need_eq = k - block_sum(cg, red, parity, wave, lane);
   }
 
-  // Ties at T go to the smallest rows: rank them in row order (a thread's
-  // rows are contiguous, threads in order).
-  int eq = 0;
+  // Selection in row order: keys above T, and the first need_eq keys equal
+  // to T (ties go to the smallest rows).
+  uint32_t selw[kPerThread / 32] = {};  // bit e % 32 of word e / 32: element e selected
   if (n > k) {
+    int eq_lane = 0;
 #pragma unroll
-    for (int e = 0; e < kPerThread; ++e) eq += key[e] == T ? 1 : 0;
-  }
-  auto exclusive_scan = [&](int v) {
-    int incl = v;
+    for (int e = 0; e < kPerThread; ++e) eq_lane += key[e] == T ? 1 : 0;
+    int run = waves_before(wave_total(eq_lane));  // ties in earlier waves
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int o = __shfl_up(incl, d);
-      if (lane >= d) incl += o;
-    }
-    if (lane == 63) red[wave] = incl;
-    __syncthreads();
-    if (tid == 0) {
-      int s = 0;
-      for (int w = 0; w < kTopkThreads / 64; ++w) {
-        wave_base[w] = s;
-        s += red[w];
+    for (int e4 = 0; e4 < kQuads; ++e4) {
+      int c = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) c += key[4 * e4 + q] == T ? 1 : 0;
+      const int incl = wave_incl_scan(c);
+      int r = run + incl - c;  // ties before this lane's four rows
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t kk = key[4 * e4 + q];
+        const bool sel = kk > T || (kk == T && r < need_eq);
+        r += kk == T ? 1 : 0;
+        selw[(4 * e4 + q) >> 5] |= (uint32_t)sel << ((4 * e4 + q) & 31);
       }
+      run += __builtin_amdgcn_readlane(incl, 63);
     }
-    __syncthreads();
-    const int r = wave_base[wave] + incl - v;
-    __syncthreads();
-    return r;
-  };
-  int eq_before = exclusive_scan(eq);
+  } else {
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) selw[e >> 5] |= (uint32_t)(key[e] != 0u) << (e & 31);
+  }
   int nsel = 0;
-  uint64_t selmask = 0;  // bit e: row j0 + e selected
 #pragma unroll
-  for (int e = 0; e < kPerThread; ++e) {
-    bool sel;
-    if (n > k) {
-      sel = key[e] > T;
-      if (key[e] == T) {
-        sel = eq_before < need_eq;
-        ++eq_before;
-      }
-    } else {
-      sel = key[e] != 0u;
-    }
-    if (sel) {
-      selmask |= 1ull << e;
-      ++nsel;
-    }
-  }
-  int pos = exclusive_scan(nsel);
+  for (int w = 0; w < kPerThread / 32; ++w) nsel += __builtin_popcount(selw[w]);
+  int pos = waves_before(wave_total(nsel));
   int32_t* out_i = a.indices + (int64_t)row * k;
   float* out_s = a.scores ? a.scores + (int64_t)row * k : nullptr;
 #pragma unroll
-  for (int e = 0; e < kPerThread; ++e) {
-    if ((selmask >> e) & 1ull) {
-      out_i[pos] = j0 + e;
-      if (out_s) out_s[pos] = src[j0 + e];
-      ++pos;
+  for (int e4 = 0; e4 < kQuads; ++e4) {
+    const uint32_t quad = (selw[(4 * e4) >> 5] >> ((4 * e4) & 31)) & 15u;
+    const int c = __builtin_popcount(quad);
+    const int incl = wave_incl_scan(c);
+    int at = pos + incl - c;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if ((quad >> q) & 1u) {
+        const int j = jw + 256 * e4 + q;
+        out_i[at] = j;
+        if (out_s) out_s[at] = src[j];
+        ++at;
+      }
     }
+    pos += __builtin_amdgcn_readlane(incl, 63);
   }
   const int filled = min(k, n);
   for (int q = filled + tid; q < k; q += kTopkThreads) {

@@ -185,3 +185,18 @@ def test_two_phases_equal_the_one_call():
             S, A = ix.scores(w, b, i), ix.abs_scores(w, b, i)
             n = S.shape[0]
             assert np.all(np.abs(S_all[b, i, :n] - S) <= rel_bound(w.h) * A)
+
+
+@pytest.mark.parametrize("L", [5000, 20000])
+def test_index_all_scores_equal(L):
+    """Every row identical, so every score ties: the k smallest rows are
+    selected.  5000 rows take the selection's compacted path, 20000 rows its
+    fallback for a band too wide to compact."""
+    w = synth.make_index_workload("idx_ties", batch=1, s_q=1, h=8, seqlens=[L], seed=306, topk=300)
+    first = w.kv[w.block_table[0, 0], 0].copy()
+    for j in range(L):
+        w.kv[w.block_table[0, j // 64], j % 64] = first
+    idx, sc = run_index(w)
+    assert idx[0, 0].tolist() == list(range(300))
+    assert np.all(sc[0, 0] == sc[0, 0, 0])
+    check_token(w, 0, 0, idx, sc, what=f"ties L={L}")
