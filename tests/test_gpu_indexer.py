@@ -200,3 +200,46 @@ def test_index_all_scores_equal(L):
     assert idx[0, 0].tolist() == list(range(300))
     assert np.all(sc[0, 0] == sc[0, 0, 0])
     check_token(w, 0, 0, idx, sc, what=f"ties L={L}")
+
+
+def test_index_benchmark_workload_sampled():
+    """The benchmark's workload in its launch configuration (128 sequences of
+    65536 FP8 rows, two query tokens of 128 heads, topk 2048): sampled
+    tokens against the oracle."""
+    import bench
+
+    c = bench.INDEX_WORKLOAD
+    w = synth.make_index_workload(c["name"], batch=c["batch"], s_q=c["s_q"], h=c["h"],
+                                  seqlens=[c["seqlen"]] * c["batch"], seed=c["seed"], topk=c["topk"])
+    print(f"{w.name}: {w.batch} x {c['seqlen']} rows", flush=True)
+    idx, sc = run_index(w)
+    rng = np.random.default_rng(1)
+    for u in rng.choice(w.batch * w.s_q, size=4, replace=False):
+        b, i = int(u) // w.s_q, int(u) % w.s_q
+        a, e = check_token(w, b, i, idx, sc, what=f"b={b} i={i}")
+        print(f"token ({b}, {i}): agreement {a:.4f}, max |S_gpu - S| / A {e:.3g}", flush=True)
+    # every token: a full, ascending, in-range list (no -1: 65536 rows > 2048)
+    assert np.all(idx >= 0) and np.all(idx < c["seqlen"])
+    assert np.all(np.diff(idx, axis=-1) > 0)
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_index_random_shapes(seed):
+    """Seeded random shapes: heads 1-160, query tokens 1-6, lengths 0-3000
+    (some 0), pooling 1-3, causal or not, topk 1-400."""
+    rng = np.random.default_rng(1000 + seed)
+    B = int(rng.integers(1, 5))
+    h = int(rng.integers(1, 161))
+    s_q = int(rng.integers(1, 7))
+    kpool = int(rng.integers(1, 4))
+    causal = int(rng.integers(0, 2))
+    lens = [int(x) if rng.random() > 0.15 else 0 for x in rng.integers(1, 3001, size=B)]
+    topk = int(rng.integers(1, 401))
+    print(f"seed {seed}: B {B} h {h} s_q {s_q} kpool {kpool} causal {causal} lens {lens} topk {topk}", flush=True)
+    w = synth.make_index_workload("idx_rand", batch=B, s_q=s_q, h=h, seqlens=lens, seed=2000 + seed,
+                                  topk=topk, kpool=kpool, is_causal=causal)
+    w.topk = min(topk, 64 * w.max_pages_per_seq)  # the call's limit: rows the table can hold
+    idx, sc = run_index(w)
+    for b in range(B):
+        for i in range(s_q):
+            check_token(w, b, i, idx, sc, what=f"seed {seed} b={b} i={i}")
