@@ -410,6 +410,11 @@ mla_status check_index_problem(const mla_index_problem* p, size_t* ws_bytes) {
     return fail(MLA_ERR_UNSUPPORTED, "batch: batch * s_q = %lld query tokens exceed 2^31 - 1", tokens);
   if ((long long)p->batch * p->max_pages_per_seq > (1LL << 31) - 1)
     return fail(MLA_ERR_UNSUPPORTED, "block_table: more than 2^31 entries");
+  int32_t per_group = 0, groups = 0;
+  mla::index_groups(p->s_q, &per_group, &groups);
+  const long long workgroups = (long long)p->batch * groups * ((p->max_pages_per_seq + mla::kIndexChunkPages - 1) / mla::kIndexChunkPages);
+  if (workgroups > (1LL << 31) - 8)
+    return fail(MLA_ERR_UNSUPPORTED, "batch: %lld score workgroups exceed the grid limit", workgroups);
   *ws_bytes = mla::index_workspace_bytes(p->batch, p->s_q, p->max_pages_per_seq);
   return MLA_OK;
 }

@@ -48,7 +48,7 @@ constexpr int kRing = 4;
 constexpr int kCopiesPerWave = 4;        // waves 1..7; wave 0 issues 5
 static_assert(kPageCopies == kIdxWaves * kCopiesPerWave + 1, "copy split");
 constexpr int kMaxTokens = 4;            // query tokens of a workgroup
-constexpr int kChunkPages = 32;
+constexpr int kChunkPages = kIndexChunkPages;
 
 // Waits and barriers that leave the direct copies alone (the compiler does
 // not see them; see the decode kernel for the same rules).

@@ -93,6 +93,8 @@ struct IndexLaunch {
   int32_t* indices;
   float* scores;  // may be null
 };
+// Pages of one sequence a score workgroup of the indexer covers.
+constexpr int kIndexChunkPages = 32;
 // Query tokens per score workgroup and workgroups per sequence.
 void index_groups(int32_t s_q, int32_t* tokens_per_group, int32_t* groups);
 // Workspace of the indexer: fp32 scores [batch, s_q, 64 * max_pages], then
