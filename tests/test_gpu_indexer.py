@@ -243,3 +243,27 @@ def test_index_random_shapes(seed):
     for b in range(B):
         for i in range(s_q):
             check_token(w, b, i, idx, sc, what=f"seed {seed} b={b} i={i}")
+
+
+@pytest.mark.parametrize("k,want_nan", [(290, []), (299, [5, 17]), (300, [5, 17, 200])])
+def test_index_nan_scores_rank_last(k, want_nan):
+    """Rows whose tile scale is NaN score NaN and rank below every other row:
+    they are selected only when k exceeds the rows with a number, the
+    smallest first."""
+    w = synth.make_index_workload("idx_nan", batch=1, s_q=1, h=32, seqlens=[300], seed=307, topk=k)
+    for j in (5, 17, 200):
+        w.kv[w.block_table[0, j // 64], j % 64, 512:516] = 0xFF  # scale of tile 0: NaN
+    idx, sc = run_index(w)
+    S = ix.scores(w, 0, 0)
+    assert np.isnan(S[[5, 17, 200]]).all() and np.isfinite(np.delete(S, [5, 17, 200])).all()
+    got = idx[0, 0]
+    nan_rows = [j for j in got.tolist() if j in (5, 17, 200)]
+    assert nan_rows == want_nan
+    numbered = np.array([j for j in got.tolist() if j >= 0 and j not in (5, 17, 200)])
+    assert len(numbered) == min(k, 297)
+    if len(numbered) < 297:  # the numbered part is a valid top-k of the rows with a number
+        A = ix.abs_scores(w, 0, 0)
+        tol = rel_bound(w.h) * A
+        rest = np.setdiff1d(np.setdiff1d(np.arange(300), numbered), [5, 17, 200])
+        assert np.min(S[numbered] + tol[numbered]) >= np.max(S[rest] - tol[rest])
+    assert np.isnan(sc[0, 0][np.isin(got, [5, 17, 200])]).all()
