@@ -77,7 +77,8 @@ mla_status mla_fp8_index_workspace_bytes(const mla_index_problem* p, size_t* byt
  *                 hold visible rows must lie in [0, num_pages)
  *   cache_seqlens int32 [B], tokens per sequence, in [0, 64 * kpool *
  *                 max_pages_per_seq] (mla_decode_check_inputs checks the
- *                 kpool = 1 case on the device)
+ *                 kpool = 1 case on the device); the kernels read at most
+ *                 the 64 * max_pages_per_seq rows a table row holds
  *   workspace     >= mla_fp8_index_workspace_bytes (16-byte aligned)
  *   indices       int32 [B, s_q, topk]                 (output)
  *   scores        float [B, s_q, topk] or NULL         (output)

@@ -177,7 +177,9 @@ __global__ void __launch_bounds__(kIdxThreads, 1) index_score_kernel(IndexArgs a
   const int L = ((cint32*)a.seqlens)[b];
   const int i0 = g * a.tokens_per_group;
   const int ntok = min(a.tokens_per_group, a.s_q - i0);
-  const int nvis = visible_rows(L, a.s_q, i0 + ntok - 1, a.kpool, a.is_causal);  // the group's most
+  // the group's most visible rows, at most the rows the table holds (as in
+  // the selection), so a length beyond the table reads nothing past its row
+  const int nvis = min(visible_rows(L, a.s_q, i0 + ntok - 1, a.kpool, a.is_causal), a.n_max);
   const int p_begin = chunk * kChunkPages;
   const int p_end = min(p_begin + kChunkPages, ceil_div(nvis, kPage));
   if (p_begin >= p_end) return;
