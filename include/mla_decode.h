@@ -170,7 +170,14 @@ mla_status mla_decode_get_metadata(const mla_problem* p, const int32_t* cache_se
  * run on a streaming kernel that keeps a whole unit in one workgroup;
  * larger units and sparse calls run on the 128-row tile kernel.  For a given
  * num_parts the results are deterministic: the same bits on every run and
- * under any permutation of the physical pages. */
+ * under any permutation of the physical pages.
+ * With the environment variable MLA_DEBUG_CHECKS set to anything but "" or
+ * "0" (read at every call), this call and those built on it first run
+ * mla_decode_check_inputs on `stream`, wait for it, and return
+ * MLA_ERR_INVALID_ARGUMENT naming the first bad sequence instead of
+ * launching the decode.  That mode synchronises the stream (not for graph
+ * capture), and its result words live in a static per-GPU array, so such
+ * calls that overlap on one GPU race. */
 mla_status mla_decode_paged(const mla_problem* p, const void* q, const void* kv_pool,
                             const int32_t* block_table, const int32_t* cache_seqlens,
                             const int32_t* indices, const int32_t* sched, int32_t num_parts,

@@ -7,6 +7,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <mutex>
@@ -22,6 +23,9 @@
 // process ends.  In host code this name is a host-side stand-in: only the
 // device address taken by scratch_address() below may reach a kernel.
 static __device__ __align__(256) uint8_t scratch[MLA_NOALLOC_SCRATCH_BYTES];
+// Result words of the input check that MLA_DEBUG_CHECKS runs before a decode
+// launch (one pair per GPU; reached only through symbol_address() below).
+static __device__ __align__(256) int32_t check_words[2];
 
 namespace {
 
@@ -142,13 +146,16 @@ mla_status check_ptr(const void* ptr, const char* name, size_t align) {
   return MLA_OK;
 }
 
-// Device address of `scratch` on each GPU, taken once per device, with that
-// device current, on the first no-allocation call that runs there.
+// Device address of a static device array (`scratch`, `check_words`) on
+// each GPU, taken once per device, with that device current, on the first
+// call that needs it there.
 constexpr int kScratchDevices = 64;
+enum DeviceSymbol { kScratch = 0, kCheckWords = 1 };
 std::mutex g_scratch_mutex;
-void* g_scratch_addr[kScratchDevices] = {};
+void* g_symbol_addr[2][kScratchDevices] = {};
 
-mla_status scratch_address(hipStream_t stream, void** addr) {
+mla_status symbol_address(hipStream_t stream, DeviceSymbol which, void** addr) {
+  const char* name = which == kScratch ? "scratch" : "check_words";
   int cur = -1;
   hipError_t e = hipGetDevice(&cur);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
@@ -158,25 +165,56 @@ mla_status scratch_address(hipStream_t stream, void** addr) {
     if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipStreamGetDevice: %s", hipGetErrorString(e));
   }
   if (dev < 0 || dev >= kScratchDevices)
-    return fail(MLA_ERR_UNSUPPORTED, "stream: device %d is beyond the %d devices the static scratch serves",
-                dev, kScratchDevices);
+    return fail(MLA_ERR_UNSUPPORTED, "stream: device %d is beyond the %d devices the static %s serves",
+                dev, kScratchDevices, name);
   std::lock_guard<std::mutex> lock(g_scratch_mutex);
-  if (!g_scratch_addr[dev]) {
+  void*& slot = g_symbol_addr[which][dev];
+  if (!slot) {
     if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess)
       return fail(MLA_ERR_HIP, "hipSetDevice(%d): %s", dev, hipGetErrorString(e));
     void* a = nullptr;
-    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    e = which == kScratch ? hipGetSymbolAddress(&a, HIP_SYMBOL(scratch))
+                          : hipGetSymbolAddress(&a, HIP_SYMBOL(check_words));
     if (dev != cur) {
       const hipError_t back = hipSetDevice(cur);
       if (e == hipSuccess) e = back;
     }
     if (e != hipSuccess)
-      return fail(MLA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+      return fail(MLA_ERR_HIP, "hipGetSymbolAddress(%s) on device %d: %s", name, dev, hipGetErrorString(e));
     if (!a || !aligned(a, 256))
-      return fail(MLA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: unusable address %p", dev, a);
-    g_scratch_addr[dev] = a;
+      return fail(MLA_ERR_HIP, "hipGetSymbolAddress(%s) on device %d: unusable address %p", name, dev, a);
+    slot = a;
   }
-  *addr = g_scratch_addr[dev];
+  *addr = slot;
+  return MLA_OK;
+}
+
+mla_status scratch_address(hipStream_t stream, void** addr) { return symbol_address(stream, kScratch, addr); }
+
+// MLA_DEBUG_CHECKS set to anything but "" or "0" (read at every call): the
+// decode calls first run the device-side input check on their stream, wait
+// for it, and fail naming the first bad sequence instead of launching.
+bool debug_checks() {
+  const char* v = getenv("MLA_DEBUG_CHECKS");
+  return v && v[0] && strcmp(v, "0") != 0;
+}
+
+mla_status debug_check(const mla::Shape& s, const int32_t* block_table, const int32_t* seqlens,
+                       hipStream_t stream) {
+  void* words = nullptr;
+  MLA_CHECK(symbol_address(stream, kCheckWords, &words));
+  MLA_CHECK(hip_status(mla::launch_check_inputs(s, block_table, seqlens, (int32_t*)words, stream),
+                       "MLA_DEBUG_CHECKS: input check kernel launch"));
+  int32_t host[2] = {0, -1};
+  hipError_t e = hipMemcpyAsync(host, words, sizeof(host), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess)
+    return fail(MLA_ERR_HIP, "MLA_DEBUG_CHECKS: reading the input check: %s", hipGetErrorString(e));
+  if (host[0] != 0)
+    return fail(MLA_ERR_INVALID_ARGUMENT,
+                "cache_seqlens/block_table: %d sequence(s) have a length outside [0, 64 * max_pages_per_seq] "
+                "or a reachable block-table entry outside [0, num_pages); first: sequence %d (MLA_DEBUG_CHECKS)",
+                host[0], host[1]);
   return MLA_OK;
 }
 
@@ -278,6 +316,7 @@ mla_status mla_decode_paged(const mla_problem* p, const void* q, const void* kv_
   if (workspace_bytes < need)
     return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes: %zu given, %zu needed", workspace_bytes, need);
   if (s.units == 0) return ok();
+  if (debug_checks()) MLA_CHECK(debug_check(s, block_table, cache_seqlens, (hipStream_t)stream));
   mla::DecodeArgs a;
   a.s = s;
   a.q = (const uint16_t*)q;

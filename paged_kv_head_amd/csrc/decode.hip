@@ -91,7 +91,6 @@ constexpr int kThreads = 256;
 constexpr int kQSteps = kDqk / 16;   // 36 MFMA k-steps over the 576 dims
 constexpr int kTileBytes = kPage * kDqk * 2;  // 73728: 72 chunk groups of 1 KiB
 constexpr int kTileLoads = kTileBytes / 1024;  // 72 direct copies, 18 per wave
-constexpr int kRopeOffset = 8 * 512 * 16;      // chunk group 8: dims 512..575
 constexpr int kStageGroups = 6;                // raw FP8 row: 41 chunks in 6 groups of 8
 constexpr int kStageBytes = kStageGroups * 8 * 16 * kPage;  // 49152
 constexpr int kStageLoads = kStageBytes / 1024;             // 48, 12 per wave
@@ -898,15 +897,6 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
       };
       auto load_p = [&](lds_u8* pl, int rb) {
         return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(pl + 2048 * rb);
-      };
-      // Every first operand of a half: V^T as pv_prefetch, and the P^T blocks
-      // of the first key step (once the half's P^T is visible).
-      auto pv_begin = [&](const uint8_t* vt, int kb2, const uint8_t* pb, bf16x8* vf, bf16x8* pfr)
-          __attribute__((always_inline)) {
-        pv_prefetch(vt, kb2, vf);
-        lds_u8* pl = p_lane(pb, 0);
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) pfr[rb] = load_p(pl, rb);
       };
       auto pv_run = [&](int kb2, const uint8_t* vt, const uint8_t* pb, bf16x8* vf, bf16x8* pfr,
                         auto&& hook) __attribute__((always_inline)) {
