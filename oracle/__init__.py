@@ -38,27 +38,32 @@ def _load():
     if _lib is None:
         if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
             build(force=True)
-        lib = ctypes.CDLL(_LIB)
-        P = ctypes.c_void_p
-        I = ctypes.c_int
-        lib.oracle_mla_decode.argtypes = [I, I, I, I, I, I, I, I, I, I, ctypes.c_float,
-                                          P, P, P, P, P, I, P, P, P]
-        lib.oracle_mla_decode.restype = I
-        lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
-        lib.oracle_e4m3_value.restype = ctypes.c_double
-        lib.oracle_bf16_round.argtypes = [ctypes.c_float]
-        lib.oracle_bf16_round.restype = ctypes.c_uint16
-        lib.oracle_decode_row.argtypes = [P, I, P]
-        lib.oracle_decode_row.restype = None
-        lib.oracle_num_threads.restype = I
-        lib.oracle_e4m3_encode.argtypes = [ctypes.c_float]
-        lib.oracle_e4m3_encode.restype = ctypes.c_uint8
-        lib.oracle_quantize_row_fp8.argtypes = [P, P]
-        lib.oracle_quantize_row_fp8.restype = None
-        lib.oracle_kv_append_fp8.argtypes = [I, I, I, I, I, P, P, P, P]
-        lib.oracle_kv_append_fp8.restype = None
-        _lib = lib
+        _lib = _declare(ctypes.CDLL(_LIB))
     return _lib
+
+
+def _declare(lib):
+    """Argument and result types of the oracle's C functions on a loaded
+    library (the built oracle, or a test's compiled copy of it)."""
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    lib.oracle_mla_decode.argtypes = [I, I, I, I, I, I, I, I, I, I, ctypes.c_float,
+                                      P, P, P, P, P, I, P, P, P]
+    lib.oracle_mla_decode.restype = I
+    lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3_value.restype = ctypes.c_double
+    lib.oracle_bf16_round.argtypes = [ctypes.c_float]
+    lib.oracle_bf16_round.restype = ctypes.c_uint16
+    lib.oracle_decode_row.argtypes = [P, I, P]
+    lib.oracle_decode_row.restype = None
+    lib.oracle_num_threads.restype = I
+    lib.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+    lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+    lib.oracle_quantize_row_fp8.argtypes = [P, P]
+    lib.oracle_quantize_row_fp8.restype = None
+    lib.oracle_kv_append_fp8.argtypes = [I, I, I, I, I, P, P, P, P]
+    lib.oracle_kv_append_fp8.restype = None
+    return lib
 
 
 def _ptr(a: Optional[np.ndarray]):
