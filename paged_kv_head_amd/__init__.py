@@ -510,7 +510,8 @@ class DecodePlan:
     """Device buffers for one problem shape: metadata and workspace.
 
     Allocated once (torch caching allocator) and reused across layers and
-    steps; ``run`` enqueues metadata, decode and combine on the stream.
+    steps: ``metadata`` enqueues the scheduler once per decode step,
+    ``decode`` enqueues decode and combine (per layer) on the stream.
     """
 
     def __init__(self, p: Problem, device="cuda", num_parts: Optional[int] = None):
