@@ -616,20 +616,24 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
     const int kfirst = (u == ub) ? kb0 : 0;
     // Q operand fragments of this lane's score row: dims 16*st + 8*h .. +8.
     // Dense: issued first, in flight while the scalar loads below resolve
-    // the segment.  Sparse: issued after the first tile's copies, so that
-    // the waits of the row resolution do not wait for them.  (The row is
-    // recomputed from the thread index: a value kept through the previous
-    // segment would come back as a spill reload, whose wait would also
-    // wait for these loads.)
+    // the segment.  Sparse: issued in two halves behind the two rounds of
+    // row lookups of the first tiles (below), so that each round waits only
+    // for the loads issued before it.  (The row is recomputed from the
+    // thread index: a value kept through the previous segment would come
+    // back as a spill reload, whose wait would also wait for these loads.)
     bf16x8 qf[kQSteps];
-    auto load_q = [&]() __attribute__((always_inline)) {
+    auto load_q_steps = [&](auto lo_c, auto hi_c) __attribute__((always_inline)) {
       int tid = threadIdx.x;
       asm volatile("" : "+v"(tid));
       const int qr = grp * kRowsPerGroup + (tid >> 6) * 32 + (tid & 31);
       const uint16_t* qrow =
           a.q + ((int64_t)u * s.rows + (qr < s.rows ? qr : 0)) * kDqk + 8 * ((tid >> 5) & 1);
 #pragma unroll
-      for (int st = 0; st < kQSteps; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(qrow + 16 * st);
+      for (int st = decltype(lo_c)::value; st < decltype(hi_c)::value; ++st)
+        qf[st] = *reinterpret_cast<const bf16x8*>(qrow + 16 * st);
+    };
+    auto load_q = [&]() __attribute__((always_inline)) {
+      load_q_steps(std::integral_constant<int, 0>{}, std::integral_constant<int, kQSteps>{});
     };
     if constexpr (!SPARSE) load_q();
     // One round of scalar loads: the sequence length, the split counts and
@@ -725,11 +729,32 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
       {
         TileCopy<FMT> first;
         if constexpr (SPARSE) {
-          const int t0 = position(kfirst);
-          const int t1 = position(kfirst + 1);
-          res_t = position(kfirst + 2);
-          const int64_t off0 = offset_of(t0, page_of(t0));
-          res_off = offset_of(t1, page_of(t1));
+          // The first three tiles' indices, then the first two tiles'
+          // table entries, each round issued together (every load at an
+          // in-range address, its result selected afterwards) and each
+          // followed by half of Q.  The empty asm statements keep the
+          // compiler from turning the loads into branches with a wait each
+          // and keep the rounds in this order.
+          int ix[3];
+#pragma unroll
+          for (int j = 0; j < 3; ++j) {
+            const int k = (kfirst + j) * kPage + lane;
+            ix[j] = idx_row[k < s.topk ? k : s.topk - 1];
+          }
+          load_q_steps(std::integral_constant<int, 0>{}, std::integral_constant<int, kQSteps / 2>{});
+          asm volatile("" : "+v"(ix[0]), "+v"(ix[1]), "+v"(ix[2])::"memory");
+          auto pos = [&](int j) {
+            const int k = (kfirst + j) * kPage + lane;
+            return (kfirst + j < kend && k < s.topk) ? ix[j] : -1;
+          };
+          const int t0 = pos(0), t1 = pos(1);
+          res_t = pos(2);
+          int pg0 = bt_row[visible(t0) ? (t0 >> 6) : 0];
+          int pg1 = bt_row[visible(t1) ? (t1 >> 6) : 0];
+          load_q_steps(std::integral_constant<int, kQSteps / 2>{}, std::integral_constant<int, kQSteps>{});
+          asm volatile("" : "+v"(pg0), "+v"(pg1)::"memory");
+          const int64_t off0 = offset_of(t0, pg0);
+          res_off = offset_of(t1, pg1);
           vm_cur = __ballot(off0 >= 0);
           first.prepare(a.kv, off0, lds_addr(FMT == 0 ? lds0 : lds1), wave, lane);
         } else if constexpr (kPipelined) {
@@ -744,7 +769,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs a) {
           pg_next = pg_second;
         }
         if constexpr (!kPipelined) first.issue_all(lane);
-        if (SPARSE || pass > 0) load_q();
+        if (!SPARSE && pass > 0) load_q();
         if constexpr (FMT == 1) {
           MLA_WAIT_VMCNT(0);
           __syncthreads();
