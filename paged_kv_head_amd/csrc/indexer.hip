@@ -342,7 +342,6 @@ __global__ void __launch_bounds__(kTopkThreads, 1) index_topk_kernel(IndexArgs a
   __shared__ int red[2 * (kTopkThreads / 64)];
   __shared__ int wred[kTopkThreads / 64];
   __shared__ uint32_t cand[kMaxCand];  // low bits of the keys that share the threshold's top bits
-  __shared__ uint32_t t_low;           // low bits of the threshold, found by wave 0
   int parity = 0;
   const int row = blockIdx.x;  // (b, i)
   const int b = row / a.s_q, i = row % a.s_q;
@@ -406,19 +405,15 @@ __global__ void __launch_bounds__(kTopkThreads, 1) index_topk_kernel(IndexArgs a
       for (int e = 0; e < kPerThread; ++e)
         if ((key[e] - T) < kBand) cand[at++] = key[e] - T;
       __syncthreads();
-      // the low bits on the m candidates, by wave 0 alone (no barriers)
-      if (wave == 0) {
-        uint32_t U = 0u;
-        for (int bit = kLowBits - 1; bit >= 0; --bit) {
-          const uint32_t c1 = U | (1u << bit);
-          int c = 0;
-          for (int ci = lane; ci < m; ci += 64) c += cand[ci] >= c1 ? 1 : 0;
-          if (wave_total(c) + above_all >= k) U = c1;
-        }
-        if (lane == 0) t_low = U;
+      // the low bits on the m candidates, by all waves (at most 8 a thread)
+      uint32_t U = 0u;
+      for (int bit = kLowBits - 1; bit >= 0; --bit) {
+        const uint32_t c1 = U | (1u << bit);
+        int c = 0;
+        for (int ci = tid; ci < m; ci += kTopkThreads) c += cand[ci] >= c1 ? 1 : 0;
+        if (block_sum(c, red, parity, wave, lane) + above_all >= k) U = c1;
       }
-      __syncthreads();
-      T += t_low;
+      T += U;
     } else {
       for (int bit = kLowBits - 1; bit >= 0; --bit) {
         const uint32_t c1 = T | (1u << bit);
@@ -468,24 +463,47 @@ __global__ void __launch_bounds__(kTopkThreads, 1) index_topk_kernel(IndexArgs a
   int pos = waves_before(wave_total(nsel));
   int32_t* out_i = a.indices + (int64_t)row * k;
   float* out_s = a.scores ? a.scores + (int64_t)row * k : nullptr;
-#pragma unroll
-  for (int e4 = 0; e4 < kQuads; ++e4) {
-    const uint32_t quad = (selw[(4 * e4) >> 5] >> ((4 * e4) & 31)) & 15u;
-    const int c = __builtin_popcount(quad);
-    const int incl = wave_incl_scan(c);
-    int at = pos + incl - c;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if ((quad >> q) & 1u) {
-        const int j = jw + 256 * e4 + q;
-        out_i[at] = j;
-        if (out_s) out_s[at] = src[j];
-        ++at;
-      }
-    }
-    pos += __builtin_amdgcn_readlane(incl, 63);
-  }
+  // With k <= kMaxCand the selected rows are ranked into LDS (cand is free
+  // once the threshold is known) and then written out by all threads in
+  // order, coalesced; beyond that each lane stores its own rows.
   const int filled = min(k, n);
+  if (k <= kMaxCand) {
+#pragma unroll
+    for (int e4 = 0; e4 < kQuads; ++e4) {
+      const uint32_t quad = (selw[(4 * e4) >> 5] >> ((4 * e4) & 31)) & 15u;
+      const int c = __builtin_popcount(quad);
+      const int incl = wave_incl_scan(c);
+      int at = pos + incl - c;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if ((quad >> q) & 1u) cand[at++] = (uint32_t)(jw + 256 * e4 + q);
+      pos += __builtin_amdgcn_readlane(incl, 63);
+    }
+    __syncthreads();
+    for (int q = tid; q < filled; q += kTopkThreads) {
+      const int j = (int)cand[q];
+      out_i[q] = j;
+      if (out_s) out_s[q] = src[j];
+    }
+  } else {
+#pragma unroll
+    for (int e4 = 0; e4 < kQuads; ++e4) {
+      const uint32_t quad = (selw[(4 * e4) >> 5] >> ((4 * e4) & 31)) & 15u;
+      const int c = __builtin_popcount(quad);
+      const int incl = wave_incl_scan(c);
+      int at = pos + incl - c;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if ((quad >> q) & 1u) {
+          const int j = jw + 256 * e4 + q;
+          out_i[at] = j;
+          if (out_s) out_s[at] = src[j];
+          ++at;
+        }
+      }
+      pos += __builtin_amdgcn_readlane(incl, 63);
+    }
+  }
   for (int q = filled + tid; q < k; q += kTopkThreads) {
     out_i[q] = -1;
     if (out_s) out_s[q] = -INFINITY;
