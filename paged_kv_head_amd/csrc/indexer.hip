@@ -467,6 +467,11 @@ __global__ void __launch_bounds__(kTopkThreads, 1) index_topk_kernel(IndexArgs a
   // once the threshold is known) and then written out by all threads in
   // order, coalesced; beyond that each lane stores its own rows.
   const int filled = min(k, n);
+  // the lane's first row, recomputed from the thread index: values kept from
+  // the loads would be held (spilled) through the whole selection
+  int tid_o = threadIdx.x;
+  asm volatile("" : "+v"(tid_o));
+  const int jo = kWaveRows * (tid_o >> 6) + 4 * (tid_o & 63);
   if (k <= kMaxCand) {
 #pragma unroll
     for (int e4 = 0; e4 < kQuads; ++e4) {
@@ -476,7 +481,7 @@ __global__ void __launch_bounds__(kTopkThreads, 1) index_topk_kernel(IndexArgs a
       int at = pos + incl - c;
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        if ((quad >> q) & 1u) cand[at++] = (uint32_t)(jw + 256 * e4 + q);
+        if ((quad >> q) & 1u) cand[at++] = (uint32_t)(jo + 256 * e4 + q);
       pos += __builtin_amdgcn_readlane(incl, 63);
     }
     __syncthreads();
@@ -495,7 +500,7 @@ __global__ void __launch_bounds__(kTopkThreads, 1) index_topk_kernel(IndexArgs a
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         if ((quad >> q) & 1u) {
-          const int j = jw + 256 * e4 + q;
+          const int j = jo + 256 * e4 + q;
           out_i[at] = j;
           if (out_s) out_s[at] = src[j];
           ++at;

@@ -184,3 +184,7 @@ def test_indexer_page_loop_waits_only_for_its_copies(asm_indexer):
         d = loop_blocks(b)
         in_loops = instructions([l for l, x in zip(b, d) if x >= 1])
         assert not [t for t in in_loops if t.startswith("scratch_") or t.startswith("flat_")], name
+    # the selection kernel keeps no spill at all (its 64 keys per thread fill
+    # the 128 registers a 1024-thread workgroup leaves each lane)
+    topk = instructions(function_body(asm_indexer, TOPK_KERNEL))
+    assert not [t for t in topk if t.startswith("scratch_")]
