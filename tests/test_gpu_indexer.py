@@ -83,6 +83,7 @@ CASES = [
     (1, 1, 0, 1, [500, 2], 8),
     (32, 1, 0, 1, [10, 0, 64], 16),
     (128, 1, 0, 1, [5000], 4096),
+    (64, 1, 0, 1, [20000, 9000], 10000),  # k above 8192: rows stored lane by lane (also all of a shorter row set)
     (4096, 1, 0, 1, [700, 64], 100),   # the most index heads the call takes
     (1000, 2, 1, 3, [2000, 333], 77),  # many heads, not a multiple of 16
 ]
