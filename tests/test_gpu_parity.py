@@ -70,6 +70,18 @@ def test_head_shapes(h_q, s_q, causal):
 
 
 @pytest.mark.parametrize("kv_format", [synth.KV_BF16, synth.KV_FP8_656])
+@pytest.mark.parametrize("h_q,s_q", [(128, 8), (96, 7)])
+def test_many_query_tokens(h_q, s_q, kv_format):
+    """Up to 1024 query rows per sequence: eight 128-row groups of one unit
+    spread over the XCD mapping, causal rows of eight positions."""
+    w = synth.make_workload("t", batch=3, h_q=h_q, s_q=s_q, seqlens=[5, 300, 1000], seed=36,
+                            is_causal=1, kv_format=kv_format)
+    out, lse = run(w)
+    ref_out, ref_lse = oracle.mla_decode(w)
+    assert_close(out, lse, ref_out, ref_lse, what=f"h_q={h_q} s_q={s_q} fmt={kv_format}")
+
+
+@pytest.mark.parametrize("kv_format", [synth.KV_BF16, synth.KV_FP8_656])
 def test_edge_lengths(kv_format):
     """Empty sequences, one token, page boundaries, causal with L < s_q."""
     w = synth.make_workload("t", batch=7, h_q=32, s_q=2, seqlens=[0, 1, 63, 64, 65, 128, 2],
