@@ -69,6 +69,18 @@ def test_head_shapes(h_q, s_q, causal):
     assert_close(out, lse, ref_out, ref_lse, what=f"h_q={h_q} s_q={s_q}")
 
 
+@pytest.mark.parametrize("h_q,kv_format,L", [(128, synth.KV_BF16, 120_000), (16, synth.KV_BF16, 200_000),
+                                             (64, synth.KV_FP8_656, 120_000)])
+def test_long_sequence(h_q, kv_format, L):
+    """One long sequence beside a short one: the scheduler cuts the long unit
+    over most parts and the combine merges all of its splits."""
+    w = synth.make_workload("t", batch=2, h_q=h_q, s_q=1, seqlens=[L, 77], seed=37, kv_format=kv_format)
+    out, lse, _, splits, parts = run(w, return_meta=True)
+    assert splits[1] - splits[0] > parts // 2  # the long unit really is split many ways
+    ref_out, ref_lse = oracle.mla_decode(w)
+    assert_close(out, lse, ref_out, ref_lse, what=f"long sequence h_q={h_q} fmt={kv_format}")
+
+
 @pytest.mark.parametrize("kv_format", [synth.KV_BF16, synth.KV_FP8_656])
 @pytest.mark.parametrize("h_q,s_q", [(128, 8), (96, 7)])
 def test_many_query_tokens(h_q, s_q, kv_format):
