@@ -398,6 +398,7 @@ def bench_prefill(args):
     flops = w.flops()
     alg_bytes = w.algorithmic_bytes()
     achieved = flops / (call_ms * 1e-3) / 1e12
+    traffic = traffic_record(w.name, "prefill")
     peaks = None if args.no_measured_peaks else measured_peaks()
     cpu = None if args.no_cpu_baseline else prefill_cpu_baseline(w)
     line = {
@@ -411,7 +412,9 @@ def bench_prefill(args):
                    "kv_format": "bf16", "num_parts": parts, "flops_per_step": flops,
                    "algorithmic_bytes_per_step": alg_bytes},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     # HBM bytes of the whole call (every kernel it launches)
+                     "traffic": None if traffic is None else traffic["hbm_bytes_per_launch"],
                      "kernel": "mla_sparse_prefill call (identity table; per 2048-token chunk: "
                                "metadata, decode_kernel, combine_kernel)",
                      "kernel_ms": call_ms},
