@@ -72,6 +72,8 @@ constexpr float kSLag = 64.0f;
 // block, and the two phases do not overlap)
 constexpr int kSKAhead = 4;
 constexpr int kSVAhead = 3;
+// FP8 rows: pairs of V^T operands (one transposing read each) in flight.
+constexpr int kSVPairAhead = 2;
 
 // Stands in for the cache bytes of keys that are not visible.
 __device__ __attribute__((aligned(16))) const uint8_t g_zero16[16] = {};
@@ -89,6 +91,7 @@ __device__ inline uint16_t to_bf16_bits(float x) {
 }
 
 typedef __bf16 bf16x4s __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2s __attribute__((ext_vector_type(2)));
 typedef float f32x2s __attribute__((ext_vector_type(2)));
 
@@ -352,42 +355,68 @@ __global__ void __launch_bounds__(64 * kSWaves, 1) decode_small_kernel(DecodeArg
 #pragma unroll
         for (int e = 0; e < 4; ++e) vsc[e] = *reinterpret_cast<const f32x4s*>(vrow + e * kPitch + 512);
       }
-      // The 4 raw values, one per word (bf16 bits or FP8 codes), are packed
-      // or dequantised only where the MFMA takes them, so their LDS reads
-      // have kSVAhead column blocks to land.
-      using VRaw = uint4;
-      auto v_raw = [&](int cb) -> VRaw {
-        if constexpr (FMT == 0) {
+      if constexpr (FMT == 0) {
+        // The 4 raw bf16 values, one per word, are packed only where the
+        // MFMA takes them, so their LDS reads have kSVAhead column blocks to
+        // land.
+        auto v_raw = [&](int cb) -> uint4 {
           const uint16_t* vc = reinterpret_cast<const uint16_t*>(vrow) + 16 * cb + j16;
           return make_uint4(vc[0], vc[kPitch / 2], vc[kPitch], vc[3 * (kPitch / 2)]);
-        } else {
-          const uint8_t* vc = vrow + 16 * cb + j16;
-          return make_uint4(vc[0], vc[kPitch], vc[2 * kPitch], vc[3 * kPitch]);
+        };
+        uint4 vop[kSVAhead];  // V^T operands read kSVAhead column blocks ahead
+#pragma unroll
+        for (int i = 0; i < kSVAhead; ++i) vop[i] = v_raw(i);
+#pragma unroll
+        for (int cb = 0; cb < 32; ++cb) {
+          const uint4 r = vop[cb % kSVAhead];
+          const bf16x4s vcur = __builtin_bit_cast(bf16x4s, make_uint2(r.x | (r.y << 16), r.z | (r.w << 16)));
+          if (cb + kSVAhead < 32) vop[cb % kSVAhead] = v_raw(cb + kSVAhead);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb)
+            o[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vcur, pf[rb], o[rb][cb], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
         }
-      };
-      auto v_operand = [&](VRaw r, int cb) -> bf16x4s {
-        if constexpr (FMT == 0) {
-          return __builtin_bit_cast(bf16x4s, make_uint2(r.x | (r.y << 16), r.z | (r.w << 16)));
-        } else {
-          const int t = cb >> 3;
-          const uint32_t v01 = pk_bf16(__builtin_amdgcn_cvt_pk_f32_fp8(r.x, false)[0] * vsc[0][t],
-                                       __builtin_amdgcn_cvt_pk_f32_fp8(r.y, false)[0] * vsc[1][t]);
-          const uint32_t v23 = pk_bf16(__builtin_amdgcn_cvt_pk_f32_fp8(r.z, false)[0] * vsc[2][t],
-                                       __builtin_amdgcn_cvt_pk_f32_fp8(r.w, false)[0] * vsc[3][t]);
-          return __builtin_bit_cast(bf16x4s, make_uint2(v01, v23));
+      } else {
+        // FP8 codes of two column blocks per transposing byte read.  In each
+        // 16-lane group, lane j loads 8 codes of key 4g + (j % 8) / 2 at
+        // columns 16*cb + 8*(j % 2) + 16*(j / 8) ..; the read hands lane r
+        // byte r % 8 of the loads of the group's even lanes (r < 8) or odd
+        // lanes (r >= 8), so lane j16 receives keys 4g .. 4g+3 of column
+        // 16*cb + j16 (bytes 0..3) and of column 16*(cb + 1) + j16 (bytes
+        // 4..7).  Two paired conversions and four multiplies with the keys'
+        // scales of the columns' tile per column block.
+        const uint8_t* vlane = vrow + ((j16 & 7) >> 1) * kPitch + 8 * (j16 & 1) + 16 * (j16 >> 3);
+        auto v_pair = [&](int cp) -> uint2 {  // column blocks 2cp, 2cp + 1
+          const i32x2 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              reinterpret_cast<__attribute__((address_space(3))) i32x2*>(
+                  (__attribute__((address_space(3))) uint8_t*)(vlane + 32 * cp)));
+          return make_uint2((uint32_t)r[0], (uint32_t)r[1]);
+        };
+        auto v_deq = [&](uint32_t w, int t) -> bf16x4s {
+          const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+          const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+          return __builtin_bit_cast(bf16x4s, make_uint2(pk_bf16(lo[0] * vsc[0][t], lo[1] * vsc[1][t]),
+                                                         pk_bf16(hi[0] * vsc[2][t], hi[1] * vsc[3][t])));
+        };
+        uint2 vop[kSVPairAhead];  // pairs of V^T operands read kSVPairAhead pairs ahead
+#pragma unroll
+        for (int i = 0; i < kSVPairAhead; ++i) vop[i] = v_pair(i);
+#pragma unroll
+        for (int cp = 0; cp < 16; ++cp) {
+          const uint2 r = vop[cp % kSVPairAhead];
+          if (cp + kSVPairAhead < 16) vop[cp % kSVPairAhead] = v_pair(cp + kSVPairAhead);
+          const int t = cp >> 2;  // the 128-column tile of columns 32cp .. 32cp + 31
+          const bf16x4s v0 = v_deq(r.x, t);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb)
+            o[rb][2 * cp] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v0, pf[rb], o[rb][2 * cp], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          const bf16x4s v1 = v_deq(r.y, t);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb)
+            o[rb][2 * cp + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v1, pf[rb], o[rb][2 * cp + 1], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
         }
-      };
-      VRaw vop[kSVAhead];  // V^T operands read kSVAhead column blocks ahead
-#pragma unroll
-      for (int i = 0; i < kSVAhead; ++i) vop[i] = v_raw(i);
-#pragma unroll
-      for (int cb = 0; cb < 32; ++cb) {
-        const bf16x4s vcur = v_operand(vop[cb % kSVAhead], cb);
-        if (cb + kSVAhead < 32) vop[cb % kSVAhead] = v_raw(cb + kSVAhead);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-          o[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vcur, pf[rb], o[rb][cb], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
       }
     }
     if (!__builtin_amdgcn_ballot_w64(restart)) break;  // wave-uniform
