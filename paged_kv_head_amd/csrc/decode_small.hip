@@ -92,6 +92,7 @@ __device__ inline uint16_t to_bf16_bits(float x) {
 
 typedef __bf16 bf16x4s __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4s __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2s __attribute__((ext_vector_type(2)));
 typedef float f32x2s __attribute__((ext_vector_type(2)));
 
@@ -356,20 +357,21 @@ __global__ void __launch_bounds__(64 * kSWaves, 1) decode_small_kernel(DecodeArg
         for (int e = 0; e < 4; ++e) vsc[e] = *reinterpret_cast<const f32x4s*>(vrow + e * kPitch + 512);
       }
       if constexpr (FMT == 0) {
-        // The 4 raw bf16 values, one per word, are packed only where the
-        // MFMA takes them, so their LDS reads have kSVAhead column blocks to
-        // land.
-        auto v_raw = [&](int cb) -> uint4 {
-          const uint16_t* vc = reinterpret_cast<const uint16_t*>(vrow) + 16 * cb + j16;
-          return make_uint4(vc[0], vc[kPitch / 2], vc[kPitch], vc[3 * (kPitch / 2)]);
+        // One transposing read per column block: in each 16-lane group, lane
+        // j loads columns 16*cb + 4*(j % 4) .. +3 of key 4g + j / 4, and lane
+        // j16 receives column 16*cb + j16 of keys 4g .. 4g+3, the operand as
+        // the MFMA takes it.  Read kSVAhead column blocks ahead.
+        const uint8_t* vlane = vrow + (j16 >> 2) * kPitch + 8 * (j16 & 3);
+        auto v_raw = [&](int cb) -> i16x4s {
+          return __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<__attribute__((address_space(3))) i16x4s*>(
+              (__attribute__((address_space(3))) uint8_t*)(vlane + 32 * cb)));
         };
-        uint4 vop[kSVAhead];  // V^T operands read kSVAhead column blocks ahead
+        i16x4s vop[kSVAhead];  // V^T operands read kSVAhead column blocks ahead
 #pragma unroll
         for (int i = 0; i < kSVAhead; ++i) vop[i] = v_raw(i);
 #pragma unroll
         for (int cb = 0; cb < 32; ++cb) {
-          const uint4 r = vop[cb % kSVAhead];
-          const bf16x4s vcur = __builtin_bit_cast(bf16x4s, make_uint2(r.x | (r.y << 16), r.z | (r.w << 16)));
+          const bf16x4s vcur = __builtin_bit_cast(bf16x4s, vop[cb % kSVAhead]);
           if (cb + kSVAhead < 32) vop[cb % kSVAhead] = v_raw(cb + kSVAhead);
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb)
