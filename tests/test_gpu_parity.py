@@ -286,3 +286,35 @@ def test_check_inputs_finds_bad_lengths_and_pages():
     n, first = mla.mla_decode_check_inputs(p, torch.from_numpy(bt_bad).cuda(),
                                            torch.from_numpy(sl_bad).cuda())
     assert (n, first) == (3, 1)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_metadata_random_shapes(seed):
+    """The scheduler alone, bit for bit against the CPU mirror, over random
+    shapes: dense and sparse units, empty sequences, more parts than blocks,
+    and unit counts above the 1024 threads of the metadata workgroup."""
+    rng = np.random.default_rng(700 + seed)
+    sparse = seed % 3 == 2
+    s_q = int(rng.integers(1, 4))
+    if seed < 6:
+        batch, parts = int(rng.integers(1, 300)), int(rng.integers(1, 3000))
+    else:
+        units, parts = int(rng.integers(1025, 5000)), int(rng.integers(1, 400))
+        batch = units // s_q if sparse else units
+    mp = int(rng.integers(1, 40))
+    topk = int(rng.integers(1, 64 * mp + 1)) if sparse else 0
+    seqlens = rng.integers(0, 64 * mp + 1, size=batch).astype(np.int32)
+    seqlens[rng.random(batch) < 0.2] = 0
+    p = mla.Problem.make(batch=batch, s_q=s_q, h_q=64, num_pages=batch * mp, max_pages_per_seq=mp,
+                         softmax_scale=0.05, topk=topk,
+                         kv_format=synth.KV_FP8_656 if sparse else synth.KV_BF16)
+    n_sched, n_splits = mla.mla_decode_metadata_size(p, parts)
+    sched = torch.full((n_sched,), -7, dtype=torch.int32, device="cuda")
+    splits = torch.full((n_splits,), -7, dtype=torch.int32, device="cuda")
+    print(f"seed {seed}: units {mla.mla_decode_num_units(p)} parts {parts} topk {topk}", flush=True)
+    mla.mla_decode_get_metadata(p, torch.from_numpy(seqlens).cuda(), parts, sched, splits)
+    got_sched, got_splits = sched.cpu().numpy(), splits.cpu().numpy()
+    nb = blocks_per_unit(seqlens, s_q, topk)
+    ref_sched, ref_splits = schedule(nb, parts, int(got_sched[6]))
+    assert np.array_equal(got_sched.reshape(parts, 8), np.array(ref_sched, dtype=np.int32))
+    assert np.array_equal(got_splits, np.array(ref_splits, dtype=np.int32))
