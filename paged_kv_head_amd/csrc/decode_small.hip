@@ -68,7 +68,7 @@ constexpr int kSOPitch = 516;  // floats per merge-buffer row
 // inside the fp32 range.  A larger climb restarts the wave's segment.
 constexpr float kSLag = 64.0f;
 // LDS operand reads in flight ahead of their MFMA (the LDS counter holds at
-// most 15 outstanding reads: one K read per step, four V reads per column
+// most 15 outstanding reads: one K read per step, one V read per column
 // block, and the two phases do not overlap)
 constexpr int kSKAhead = 4;
 constexpr int kSVAhead = 3;
