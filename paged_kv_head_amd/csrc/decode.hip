@@ -443,8 +443,10 @@ struct HalfDequant {
 // kernel uses them, and the 256 AGPRs are all taken by the output: score
 // accumulators there force the output blocks to be shuffled every tile.
 // Back-to-back MFMAs chained through srcC need no wait states; the drain
-// below pads the chain before any VALU reads the result (an MFMA result read
-// by the VALU needs wait states the compiler cannot see through asm).
+// below pads the chain before any VALU reads or writes the result (an MFMA
+// result read by the VALU needs wait states the compiler cannot see through
+// asm: for this 8-pass MFMA on gfx950 the compiler's own padding is 12, a
+// build check confirms it; the drain gives 16).
 // Their operands come from LDS reads (K) or are set once per segment (Q),
 // so no VALU instruction writes one within the two wait states before an
 // MFMA that the hardware would need; a build check verifies this on the
@@ -456,7 +458,7 @@ __device__ inline void mfma_s_acc(f32x16& acc, const bf16x8& a, const bf16x8& b)
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
 __device__ inline void mfma_s_drain(f32x16& acc) {
-  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15" : "+v"(acc));
+  asm volatile("s_nop 15" : "+v"(acc));
 }
 
 // S^T for 32 keys (rows of the tile at kb) against this lane's Q row, with

@@ -188,3 +188,38 @@ def test_indexer_page_loop_waits_only_for_its_copies(asm_indexer):
     # the 128 registers a 1024-thread workgroup leaves each lane)
     topk = instructions(function_body(asm_indexer, TOPK_KERNEL))
     assert not [t for t in topk if t.startswith("scratch_")]
+
+
+MFMA_THEN_VALU = r'''
+#include <hip/hip_runtime.h>
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+__global__ void probe(const bf16x8* a, const bf16x8* b, float* out) {
+  f32x16 acc = {};
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[threadIdx.x], b[threadIdx.x], acc, 0, 0, 0);
+  out[threadIdx.x] = acc[0] * 3.0f + acc[5];
+}
+'''
+
+
+def test_score_chain_drain_covers_the_mfma_to_valu_hazard(tmp_path_factory):
+    """The hand-written score chains end with a drain of s_nop wait states
+    before any VALU instruction touches the accumulator.  The compiler pads
+    the same dependency (v_mfma_f32_32x32x16_bf16 result read by a VALU
+    instruction) in code it can see; the drain must give at least as many
+    wait states as that padding."""
+    d = tmp_path_factory.mktemp("probe")
+    src = str(d / "probe.hip")
+    with open(src, "w") as f:
+        f.write(MFMA_THEN_VALU)
+    lines = [t for t in instructions(compile_asm(tmp_path_factory, src)) if t]
+    i = next(k for k, t in enumerate(lines) if t.startswith("v_mfma_f32_32x32x16_bf16"))
+    j = next(k for k in range(i + 1, len(lines)) if lines[k].startswith("v_") and "mfma" not in lines[k])
+    needed = sum(int(re.match(r"s_nop\s+(\d+)", t).group(1)) + 1 for t in lines[i + 1:j]
+                 if t.startswith("s_nop"))
+    assert needed > 0
+    with open(DECODE) as f:
+        text = f.read()
+    body = re.search(r"void mfma_s_drain\(f32x16& acc\) \{\s*asm volatile\(\"([^\"]*)\"", text).group(1)
+    drain = sum(int(n) + 1 for n in re.findall(r"s_nop (\d+)", body))
+    assert drain >= needed, (drain, needed)
