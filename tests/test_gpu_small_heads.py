@@ -100,13 +100,15 @@ def test_small_heads_bit_identity(h_q, s_q, kv_format):
 @pytest.mark.parametrize("name,h_q,s_q,lo,hi,kv_format,seed,max_pages", [
     ("b128_h16_sq1", 16, 1, 1024, 8192, synth.KV_BF16, 1006, 128),
     ("b128_h16_sq1_fp8", 16, 1, 1024, 8192, synth.KV_FP8_656, 1007, 128),
+    ("b128_h16_sq1_fp8_l8k_32k", 16, 1, 8192, 32768, synth.KV_FP8_656, 1008, 512),
     ("b128_h16_sq2_fp8_l8k_32k", 16, 2, 8192, 32768, synth.KV_FP8_656, 1009, 512),
 ])
 def test_small_heads_full_size(name, h_q, s_q, lo, hi, kv_format, seed, max_pages):
     """The small-head benchmark shapes at batch 128 in the default launch
     configuration, every query row against the oracle: 16 heads over the bf16
-    and FP8 caches, and 16 heads x 2 causal query tokens over the FP8 cache at
-    lengths U[8192, 32768] (the two-row-block variant)."""
+    and FP8 caches (the FP8 one also at the benchmark's lengths U[8192,
+    32768], same seed), and 16 heads x 2 causal query tokens over the FP8
+    cache at lengths U[8192, 32768] (the two-row-block variant)."""
     w = synth.make_workload(name, batch=128, h_q=h_q, s_q=s_q, seqlens=synth.Uniform(lo, hi),
                             seed=seed, max_pages_per_seq=max_pages, kv_format=kv_format,
                             is_causal=int(s_q > 1))
