@@ -240,7 +240,7 @@ def make_workload(name: str, *, batch: int, h_q: int, s_q: int, seqlens,
 
 # The five decode configurations, by number.  ``batch`` may be overridden to
 # build a smaller batch of the same shape for parity runs.
-CONFIGS = {
+BENCH_WORKLOADS = {
     1: dict(name="c1_tiny_bf16", batch=2, h_q=16, s_q=1, seqlens=[100, 257],
             kv_format=KV_BF16, slack=0.0),
     2: dict(name="c2_dense_bf16_b64_sq1", batch=64, h_q=128, s_q=1, seqlens=Uniform(1024, 8192),
@@ -256,7 +256,7 @@ CONFIGS = {
 
 def config_workload(n: int, batch: Optional[int] = None, seed: Optional[int] = None) -> Workload:
     """Workload of configuration ``n`` (seed 1000 + n unless given)."""
-    c = dict(CONFIGS[n])
+    c = dict(BENCH_WORKLOADS[n])
     b = batch if batch is not None else c["batch"]
     c["batch"] = b
     if isinstance(c["seqlens"], int):
