@@ -561,7 +561,7 @@ def main():
         copy_calibration()
         return
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); "
+        print(f"bench.py: this benchmark measures one GPU only (got --gpus {args.gpus}); "
               "the path shards by batch or by query head with no exchange, so N GPUs "
               "would run N independent copies of the one-GPU step.", file=sys.stderr)
         sys.exit(2)
